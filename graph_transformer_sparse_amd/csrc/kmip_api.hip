@@ -1,0 +1,146 @@
+// libkmip C ABI: argument checks, workspace layout and kernel launches.
+// The contract of every entry point is documented in include/kmip.h.
+#include "kmip_internal.h"
+
+using namespace kmip;
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool single_graph(const int32_t* offsets, int num_graphs) {
+  return offsets == nullptr || num_graphs <= 1;
+}
+
+kmip_status_t check_shape(int64_t N, int H, int d, int topk, int num_graphs) {
+  if (N < 1 || H < 1 || num_graphs < 0) return KMIP_ERR_INVALID_VALUE;
+  if (d != 32 && d != 64) return KMIP_ERR_UNSUPPORTED;
+  if (topk < 1 || topk > 64) return KMIP_ERR_UNSUPPORTED;
+  const int64_t NH = N * (int64_t)H;
+  if (N > (int64_t)INT32_MAX || NH * topk >= (int64_t)INT32_MAX - 1 ||
+      NH >= (int64_t)INT32_MAX - 2)
+    return KMIP_ERR_UNSUPPORTED;
+  if (scan_max_tiles(N, num_graphs) * H >= (int64_t)INT32_MAX) return KMIP_ERR_UNSUPPORTED;
+  return KMIP_OK;
+}
+
+size_t forward_ws(int64_t N, int num_graphs) {
+  if (num_graphs <= 1) return 0;
+  const int64_t tiles = scan_max_tiles(N, num_graphs);
+  return align256((size_t)(num_graphs + 1) * 4) + align256((size_t)tiles * sizeof(int2));
+}
+
+size_t backward_ws(int64_t N, int H, int d, int topk) {
+  const int64_t P = N * H * topk;
+  const int64_t HN = N * H;
+  return align256((size_t)P * sizeof(float2)) + sort_scratch_bytes(P, HN) +
+         segreduce_scratch_bytes(P, d);
+}
+
+kmip_status_t launch_status(hipError_t e) { return e == hipSuccess ? KMIP_OK : KMIP_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kmip_status_string(kmip_status_t status) {
+  switch (status) {
+    case KMIP_OK: return "KMIP_OK: success";
+    case KMIP_ERR_INVALID_VALUE: return "KMIP_ERR_INVALID_VALUE: invalid argument";
+    case KMIP_ERR_UNSUPPORTED: return "KMIP_ERR_UNSUPPORTED: unsupported shape (d, topk or size)";
+    case KMIP_ERR_WORKSPACE: return "KMIP_ERR_WORKSPACE: workspace too small";
+    case KMIP_ERR_LAUNCH: return "KMIP_ERR_LAUNCH: kernel launch failed";
+  }
+  return "KMIP: unknown status";
+}
+
+int kmip_version(void) { return kVersion; }
+
+size_t kmip_forward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
+  if (check_shape(N, H, d, topk, num_graphs) != KMIP_OK) return 0;
+  return forward_ws(N, num_graphs);
+}
+
+size_t kmip_backward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
+  if (check_shape(N, H, d, topk, num_graphs) != KMIP_OK) return 0;
+  return backward_ws(N, H, d, topk);
+}
+
+kmip_status_t kmip_forward(const void* q, const void* k, const void* v, int64_t N, int H,
+                           int d, int topk, const int32_t* graph_offsets, int num_graphs,
+                           float* out, int32_t* topk_idx, float* topk_score, void* workspace,
+                           size_t workspace_bytes, kmip_stream_t stream) {
+  if (!q || !k || !v || !out || !topk_idx || !topk_score) return KMIP_ERR_INVALID_VALUE;
+  kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
+  if (st != KMIP_OK) return st;
+  if (num_graphs > 1 && graph_offsets == nullptr) return KMIP_ERR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(topk_idx, 4) || !aligned(topk_score, 4))
+    return KMIP_ERR_INVALID_VALUE;
+  const bool single = single_graph(graph_offsets, num_graphs);
+  const size_t need = single ? 0 : forward_ws(N, num_graphs);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return KMIP_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t max_tiles = scan_max_tiles(N, num_graphs);
+  int2* tiles = nullptr;
+  if (!single) {
+    char* w = static_cast<char*>(workspace);
+    int32_t* tile_start = reinterpret_cast<int32_t*>(w);
+    tiles = reinterpret_cast<int2*>(w + align256((size_t)(num_graphs + 1) * 4));
+    st = launch_status(launch_tile_plan(graph_offsets, num_graphs, max_tiles, tile_start,
+                                        tiles, s));
+    if (st != KMIP_OK) return st;
+  }
+  st = launch_status(launch_score_topk(static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(k), N, H, d, topk,
+                                       single ? nullptr : graph_offsets, num_graphs, tiles,
+                                       max_tiles, topk_idx, topk_score, s));
+  if (st != KMIP_OK) return st;
+  return launch_status(launch_gather_av(static_cast<const uint16_t*>(v), N, H, d, topk,
+                                        topk_idx, topk_score, out, s));
+}
+
+kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t N, int H,
+                            int d, int topk, const int32_t* graph_offsets, int num_graphs,
+                            const int32_t* topk_idx, const float* topk_score,
+                            const float* dout, float* dq, float* dk, float* dv,
+                            void* workspace, size_t workspace_bytes, kmip_stream_t stream) {
+  if (!q || !k || !v || !topk_idx || !topk_score || !dout || !dq || !dk || !dv)
+    return KMIP_ERR_INVALID_VALUE;
+  kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
+  if (st != KMIP_OK) return st;
+  if (num_graphs > 1 && graph_offsets == nullptr) return KMIP_ERR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(topk_idx, 4) ||
+      !aligned(topk_score, 4))
+    return KMIP_ERR_INVALID_VALUE;
+  const size_t need = backward_ws(N, H, d, topk);
+  if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return KMIP_ERR_INVALID_VALUE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t P = N * H * topk;
+  const int64_t HN = N * H;
+  char* w = static_cast<char*>(workspace);
+  float2* pairs = reinterpret_cast<float2*>(w);
+  w += align256((size_t)P * sizeof(float2));
+  SortScratch sc;
+  sort_scratch_carve(w, P, HN, &sc);
+  w += sort_scratch_bytes(P, HN);
+  double* partials = reinterpret_cast<double*>(w);
+
+  st = launch_status(launch_bwd_query(static_cast<const uint16_t*>(k),
+                                      static_cast<const uint16_t*>(v), N, H, d, topk,
+                                      topk_idx, topk_score, dout, dq, pairs, s));
+  if (st != KMIP_OK) return st;
+  st = launch_status(launch_selection_transpose(topk_idx, N, H, topk, &sc, s));
+  if (st != KMIP_OK) return st;
+  return launch_status(launch_bwd_keys(static_cast<const uint16_t*>(q), dout, N, H, d, topk,
+                                       pairs, &sc, partials, dk, dv, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,474 @@
+// Key side of the k-MIP backward: dk_j = sum_i ds_ij q_i and
+// dv_j = sum_i p_ij dO_i over every query i that selected key j.
+//
+// Page "k-Maximum Inner Product Attention for Graph Transformers and the
+// Expressive Power of GraphGPS", Abstract: the attention pattern is the
+// sparse set of selected (query, key) pairs; its gradient reaches a key only
+// through the pairs that selected it.
+//
+// The forward leaves the selection as rows of k keys per query.  The key
+// side needs the transpose, so:
+//  1. every pair (row*k + slot) gets the sort key h*N + j (padding slots get
+//     the sentinel H*N) and key counts are histogrammed;
+//  2. a stable LSD radix sort (8-bit digits) orders the pairs by key; within
+//     a key the pairs stay in ascending pair id, i.e. ascending query;
+//  3. an exclusive scan of the counts gives the key segment pointers;
+//  4. fixed-length slices of the sorted pairs are reduced by 16-lane groups
+//     (no atomics).  Runs that cover a whole key segment are written
+//     directly; runs cut by a slice boundary go to per-slice partials, which
+//     a fix-up pass adds in slice order.  Keys selected by no query get exact
+//     zeros.  Every sum has a fixed order, so results are bitwise repeatable.
+#include "kmip_internal.h"
+
+namespace kmip {
+namespace {
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// keys[pid] = h*N + j (or H*N for padding), vals[pid] = pid, counts[key]++.
+__global__ void make_keys_kernel(const int32_t* __restrict__ idx, int64_t P, int64_t N, int H,
+                                 int topk, uint32_t* __restrict__ keys,
+                                 uint32_t* __restrict__ vals, int32_t* __restrict__ counts) {
+  const int64_t pid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (pid >= P) return;
+  const int64_t row = pid / topk;
+  const int h = (int)(row % H);
+  const int32_t j = idx[pid];
+  const uint32_t key = j < 0 ? (uint32_t)(N * H) : (uint32_t)(h * N + j);
+  keys[pid] = key;
+  vals[pid] = (uint32_t)pid;
+  atomicAdd(&counts[key], 1);   // integer counts: order-independent result
+}
+
+// ------------------------------------------------------------ device scan
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan of the values of one block (256 threads); returns the
+// thread's exclusive prefix and the block total through *total.
+__device__ __forceinline__ int32_t block_excl_scan(int32_t x, int32_t* sh, int32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t incl = wave_incl_scan(x, lane);
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  int32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < SCAN_THREADS / 64; ++w) {
+    const int32_t v = sh[w];
+    base += w < wave ? v : 0;
+    tot += v;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - x;
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void scan_reduce_kernel(
+    const int32_t* __restrict__ in, int64_t n, int32_t* __restrict__ aux) {
+  __shared__ int32_t sh[SCAN_THREADS / 64];
+  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE_ELEMS + (int64_t)threadIdx.x * SCAN_ITEMS;
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_ITEMS; ++i) s += (base + i < n) ? in[base + i] : 0;
+  int32_t tot;
+  block_excl_scan(s, sh, &tot);
+  if (threadIdx.x == 0) aux[blockIdx.x] = tot;
+}
+
+// One block: exclusive scan of aux[0..m) in place.
+__global__ __launch_bounds__(SCAN_THREADS) void scan_aux_kernel(int32_t* __restrict__ aux,
+                                                                int64_t m) {
+  __shared__ int32_t sh[SCAN_THREADS / 64];
+  int32_t carry = 0;
+  for (int64_t b = 0; b < m; b += SCAN_THREADS) {
+    const int64_t i = b + threadIdx.x;
+    const int32_t x = i < m ? aux[i] : 0;
+    int32_t tot;
+    const int32_t ex = block_excl_scan(x, sh, &tot);
+    if (i < m) aux[i] = carry + ex;
+    carry += tot;
+  }
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void scan_down_kernel(
+    const int32_t* __restrict__ in, int32_t* __restrict__ out, int64_t n,
+    const int32_t* __restrict__ aux) {
+  __shared__ int32_t sh[SCAN_THREADS / 64];
+  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE_ELEMS + (int64_t)threadIdx.x * SCAN_ITEMS;
+  int32_t v[SCAN_ITEMS];
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_ITEMS; ++i) {
+    v[i] = (base + i < n) ? in[base + i] : 0;
+    s += v[i];
+  }
+  int32_t tot;
+  int32_t run = block_excl_scan(s, sh, &tot) + aux[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < SCAN_ITEMS; ++i) {
+    if (base + i < n) out[base + i] = run;
+    run += v[i];
+  }
+}
+
+// ------------------------------------------------------------ radix sort
+__global__ __launch_bounds__(SORT_THREADS) void radix_hist_kernel(
+    const uint32_t* __restrict__ keys, int64_t P, int shift, int32_t* __restrict__ hist,
+    int64_t nblk) {
+  __shared__ int32_t cnt[SORT_BINS];
+  cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * SORT_TILE;
+#pragma unroll
+  for (int i = 0; i < SORT_ITEMS; ++i) {
+    const int64_t e = base + i * SORT_THREADS + threadIdx.x;
+    if (e < P) atomicAdd(&cnt[(keys[e] >> shift) & (SORT_BINS - 1)], 1);
+  }
+  __syncthreads();
+  hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = cnt[threadIdx.x];
+}
+
+// Stable scatter.  Wave w of the block ranks the elements
+// [tile + w*1024, +1024) in order, 64 at a time: equal digits inside a
+// 64-element chunk are found with 8 ballots, and a per-wave running count
+// per digit carries the rank across chunks.  Waves are then offset by the
+// counts of the earlier waves, blocks by the scanned histogram.
+__global__ __launch_bounds__(SORT_THREADS) void radix_scatter_kernel(
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t P,
+    int shift, const int32_t* __restrict__ hist_scan, int64_t nblk,
+    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out) {
+  constexpr int NW = SORT_THREADS / 64;
+  constexpr int PER_WAVE = SORT_TILE / NW;
+  constexpr int CHUNKS = PER_WAVE / 64;
+  __shared__ int32_t wcnt[NW][SORT_BINS];
+  __shared__ int32_t gbase[SORT_BINS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) wcnt[w][threadIdx.x] = 0;
+  gbase[threadIdx.x] = hist_scan[(int64_t)threadIdx.x * nblk + blockIdx.x];
+  __syncthreads();
+
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int64_t wbase = (int64_t)blockIdx.x * SORT_TILE + (int64_t)wave * PER_WAVE;
+  uint32_t k[CHUNKS], v[CHUNKS];
+  int32_t rank[CHUNKS];
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) {
+    const int64_t e = wbase + c * 64 + lane;
+    const bool valid = e < P;
+    k[c] = valid ? keys_in[e] : 0u;
+    v[c] = valid ? vals_in[e] : 0u;
+    const int dg = (int)((k[c] >> shift) & (SORT_BINS - 1));
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < SORT_BITS; ++b) {
+      const int bit = (dg >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int32_t before = wcnt[wave][dg];
+    rank[c] = before + __popcll(peers & lt);
+    const bool leader = valid && (lane == 63 || (peers >> (lane + 1)) == 0ull);
+    if (leader) wcnt[wave][dg] = before + __popcll(peers);
+  }
+  __syncthreads();
+  {   // exclusive prefix over waves, one digit per thread
+    const int d = threadIdx.x;
+    int32_t run = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int32_t c = wcnt[w][d];
+      wcnt[w][d] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) {
+    const int64_t e = wbase + c * 64 + lane;
+    if (e < P) {
+      const int dg = (int)((k[c] >> shift) & (SORT_BINS - 1));
+      const int64_t pos = (int64_t)gbase[dg] + wcnt[wave][dg] + rank[c];
+      keys_out[pos] = k[c];
+      vals_out[pos] = v[c];
+    }
+  }
+}
+
+// ------------------------------------------------------------ segmented reduce
+template <int EPL>
+__device__ __forceinline__ void load_bf16_cols(const uint16_t* p, float* x) {
+  if constexpr (EPL == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    x[0] = __uint_as_float(w << 16);
+    x[1] = __uint_as_float(w & 0xffff0000u);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void load_f32_cols(const float* p, float* x) {
+  if constexpr (EPL == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    x[0] = t.x;
+    x[1] = t.y;
+  } else {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    x[0] = t.x;
+    x[1] = t.y;
+    x[2] = t.z;
+    x[3] = t.w;
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void store_f32_cols(float* p, const float* x) {
+  if constexpr (EPL == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+}
+
+constexpr int SEG_GROUPS = 16;     // 16-lane groups per 256-thread block
+
+// partials layout: [slice][slot 0|1][dk | dv][D], fp64.  Sums are carried in
+// fp64 (hub keys add thousands of terms of mixed sign) and rounded to fp32
+// once, when the key's total is written.
+template <int D>
+__global__ __launch_bounds__(256) void segreduce_kernel(
+    const uint16_t* __restrict__ Q, const float* __restrict__ dout,
+    const float2* __restrict__ pairs, const uint32_t* __restrict__ skeys,
+    const uint32_t* __restrict__ svals, const int32_t* __restrict__ key_ptr, int64_t N, int H,
+    int topk, int64_t nslices, double* __restrict__ partials, float* __restrict__ dk,
+    float* __restrict__ dv) {
+  constexpr int EPL = D / 16;
+  const int l16 = threadIdx.x & 15;
+  const int64_t slice = (int64_t)blockIdx.x * SEG_GROUPS + (threadIdx.x >> 4);
+  if (slice >= nslices) return;
+  const int64_t HN = N * H;
+  const int64_t valid_end = key_ptr[HN];
+  const int64_t s0 = slice * SEG_SLICE;
+  if (s0 >= valid_end) return;
+  const int64_t s1 = s0 + SEG_SLICE < valid_end ? s0 + SEG_SLICE : valid_end;
+
+  double ak[EPL], av[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ak[e] = av[e] = 0.0;
+  uint32_t cur = skeys[s0];
+  int64_t run0 = s0;
+
+  auto flush = [&](uint32_t key, int64_t ra, int64_t rb) __attribute__((always_inline)) {
+    const int64_t sa = key_ptr[key], sb = key_ptr[key + 1];
+    if (ra == sa && rb == sb) {
+      const int64_t j = key % N, h = key / N;
+      const int64_t orow = j * H + h;
+      float fk[EPL], fv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        fk[e] = (float)ak[e];
+        fv[e] = (float)av[e];
+      }
+      store_f32_cols<EPL>(dk + orow * D + l16 * EPL, fk);
+      store_f32_cols<EPL>(dv + orow * D + l16 * EPL, fv);
+      return;
+    }
+    const int slot = (ra == s0) ? 0 : 1;
+    double* dst = partials + ((slice * 2 + slot) * 2) * D + l16 * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      dst[e] = ak[e];
+      dst[D + e] = av[e];
+    }
+  };
+
+  for (int64_t t = s0; t < s1; ++t) {
+    const uint32_t key = skeys[t];
+    if (key != cur) {
+      flush(cur, run0, t);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ak[e] = av[e] = 0.0;
+      cur = key;
+      run0 = t;
+    }
+    const uint32_t pid = svals[t];
+    const int64_t row = pid / (uint32_t)topk;
+    const float2 pr = pairs[pid];
+    float qx[EPL], gx[EPL];
+    load_bf16_cols<EPL>(Q + row * D + l16 * EPL, qx);
+    load_f32_cols<EPL>(dout + row * D + l16 * EPL, gx);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      ak[e] = fma((double)pr.y, (double)qx[e], ak[e]);
+      av[e] = fma((double)pr.x, (double)gx[e], av[e]);
+    }
+  }
+  flush(cur, run0, s1);
+}
+
+// One 16-lane group per key: zeros for unselected keys, and the in-order sum
+// of slice partials for keys whose segment crosses a slice boundary.
+template <int D>
+__global__ __launch_bounds__(256) void segfix_kernel(const int32_t* __restrict__ key_ptr,
+                                                     int64_t N, int H,
+                                                     const double* __restrict__ partials,
+                                                     float* __restrict__ dk,
+                                                     float* __restrict__ dv) {
+  constexpr int EPL = D / 16;
+  const int l16 = threadIdx.x & 15;
+  const int64_t key = (int64_t)blockIdx.x * SEG_GROUPS + (threadIdx.x >> 4);
+  const int64_t HN = N * H;
+  if (key >= HN) return;
+  const int64_t a = key_ptr[key], b = key_ptr[key + 1];
+  const int64_t orow = (key % N) * H + key / N;
+  double ak[EPL], av[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ak[e] = av[e] = 0.0;
+  if (a < b) {
+    const int64_t sa = a / SEG_SLICE, sb = (b - 1) / SEG_SLICE;
+    if (sa == sb) return;                       // written by segreduce_kernel
+    for (int64_t s = sa; s <= sb; ++s) {
+      const int slot = (s == sa && a != sa * SEG_SLICE) ? 1 : 0;
+      const double* src = partials + ((s * 2 + slot) * 2) * D + l16 * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        ak[e] += src[e];
+        av[e] += src[D + e];
+      }
+    }
+  }
+  float fk[EPL], fv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    fk[e] = (float)ak[e];
+    fv[e] = (float)av[e];
+  }
+  store_f32_cols<EPL>(dk + orow * D + l16 * EPL, fk);
+  store_f32_cols<EPL>(dv + orow * D + l16 * EPL, fv);
+}
+
+int sort_passes(int64_t max_key) {
+  int bits = 0;
+  while ((max_key >> bits) != 0) ++bits;
+  return bits == 0 ? 1 : (bits + SORT_BITS - 1) / SORT_BITS;
+}
+
+}  // namespace
+
+int64_t scan_aux_elems(int64_t n) { return ceil_div(n, SCAN_TILE_ELEMS) + 1; }
+
+hipError_t launch_exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* aux,
+                                 hipStream_t s) {
+  const int64_t nb = ceil_div(n, SCAN_TILE_ELEMS);
+  hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(SCAN_THREADS), 0, s, in, n,
+                     aux);
+  hipLaunchKernelGGL(scan_aux_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, aux, nb);
+  hipLaunchKernelGGL(scan_down_kernel, dim3((unsigned)nb), dim3(SCAN_THREADS), 0, s, in, out,
+                     n, aux);
+  return hipGetLastError();
+}
+
+size_t sort_scratch_bytes(int64_t P, int64_t HN) {
+  const int64_t nblk = ceil_div(P, SORT_TILE);
+  const int64_t hist_n = (int64_t)SORT_BINS * nblk;
+  const int64_t aux_n = scan_aux_elems(hist_n > HN + 2 ? hist_n : HN + 2);
+  size_t b = 0;
+  b += 4 * align256((size_t)P * 4);            // keys[2], vals[2]
+  b += align256((size_t)hist_n * 4);
+  b += align256((size_t)aux_n * 4);
+  b += 2 * align256((size_t)(HN + 2) * 4);     // counts, key_ptr
+  return b;
+}
+
+void sort_scratch_carve(void* base, int64_t P, int64_t HN, SortScratch* sc) {
+  const int64_t nblk = ceil_div(P, SORT_TILE);
+  const int64_t hist_n = (int64_t)SORT_BINS * nblk;
+  const int64_t aux_n = scan_aux_elems(hist_n > HN + 2 ? hist_n : HN + 2);
+  char* p = static_cast<char*>(base);
+  sc->keys[0] = reinterpret_cast<uint32_t*>(p); p += align256((size_t)P * 4);
+  sc->keys[1] = reinterpret_cast<uint32_t*>(p); p += align256((size_t)P * 4);
+  sc->vals[0] = reinterpret_cast<uint32_t*>(p); p += align256((size_t)P * 4);
+  sc->vals[1] = reinterpret_cast<uint32_t*>(p); p += align256((size_t)P * 4);
+  sc->hist = reinterpret_cast<int32_t*>(p); p += align256((size_t)hist_n * 4);
+  sc->scan_aux = reinterpret_cast<int32_t*>(p); p += align256((size_t)aux_n * 4);
+  sc->counts = reinterpret_cast<int32_t*>(p); p += align256((size_t)(HN + 2) * 4);
+  sc->key_ptr = reinterpret_cast<int32_t*>(p);
+  sc->final_buf = 0;
+}
+
+hipError_t launch_selection_transpose(const int32_t* topk_idx, int64_t N, int H, int topk,
+                                      SortScratch* sc, hipStream_t s) {
+  const int64_t P = N * H * topk;
+  const int64_t HN = N * H;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)ceil_div(HN + 2, 256)), dim3(256), 0, s,
+                     sc->counts, HN + 2, 0);
+  hipLaunchKernelGGL(make_keys_kernel, dim3((unsigned)ceil_div(P, 256)), dim3(256), 0, s,
+                     topk_idx, P, N, H, topk, sc->keys[0], sc->vals[0], sc->counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nblk = ceil_div(P, SORT_TILE);
+  const int passes = sort_passes(HN);
+  int cur = 0;
+  for (int ps = 0; ps < passes; ++ps) {
+    const int shift = ps * SORT_BITS;
+    hipLaunchKernelGGL(radix_hist_kernel, dim3((unsigned)nblk), dim3(SORT_THREADS), 0, s,
+                       sc->keys[cur], P, shift, sc->hist, nblk);
+    e = launch_exclusive_scan(sc->hist, sc->hist, (int64_t)SORT_BINS * nblk, sc->scan_aux, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(radix_scatter_kernel, dim3((unsigned)nblk), dim3(SORT_THREADS), 0, s,
+                       sc->keys[cur], sc->vals[cur], P, shift, sc->hist, nblk,
+                       sc->keys[cur ^ 1], sc->vals[cur ^ 1]);
+    cur ^= 1;
+  }
+  sc->final_buf = cur;
+  e = launch_exclusive_scan(sc->counts, sc->key_ptr, HN + 2, sc->scan_aux, s);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+size_t segreduce_scratch_bytes(int64_t P, int d) {
+  const int64_t nslices = ceil_div(P, SEG_SLICE);
+  return align256((size_t)nslices * 2 * 2 * d * sizeof(double));
+}
+
+hipError_t launch_bwd_keys(const uint16_t* q, const float* dout, int64_t N, int H, int d,
+                           int topk, const float2* pairs, const SortScratch* sc,
+                           double* partials, float* dk, float* dv, hipStream_t s) {
+  const int64_t P = N * H * topk;
+  const int64_t HN = N * H;
+  const int64_t nslices = ceil_div(P, SEG_SLICE);
+  const unsigned b1 = (unsigned)ceil_div(nslices, SEG_GROUPS);
+  const unsigned b2 = (unsigned)ceil_div(HN, SEG_GROUPS);
+  const uint32_t* sk = sc->keys[sc->final_buf];
+  const uint32_t* sv = sc->vals[sc->final_buf];
+  if (d == 32) {
+    hipLaunchKernelGGL(segreduce_kernel<32>, dim3(b1), dim3(256), 0, s, q, dout, pairs, sk, sv,
+                       sc->key_ptr, N, H, topk, nslices, partials, dk, dv);
+    hipLaunchKernelGGL(segfix_kernel<32>, dim3(b2), dim3(256), 0, s, sc->key_ptr, N, H,
+                       partials, dk, dv);
+  } else if (d == 64) {
+    hipLaunchKernelGGL(segreduce_kernel<64>, dim3(b1), dim3(256), 0, s, q, dout, pairs, sk, sv,
+                       sc->key_ptr, N, H, topk, nslices, partials, dk, dv);
+    hipLaunchKernelGGL(segfix_kernel<64>, dim3(b2), dim3(256), 0, s, sc->key_ptr, N, H,
+                       partials, dk, dv);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kmip

@@ -1,0 +1,98 @@
+// Internal declarations shared by the libkmip HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kmip.h"
+
+namespace kmip {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- tiling
+// Score scan: a workgroup of SCAN_WAVES wavefronts, each owning 32 query rows
+// of one head (one 32x32 MFMA output block: keys x queries).
+constexpr int SCAN_WAVES = 4;
+constexpr int SCAN_QPW = 32;
+constexpr int SCAN_QT = SCAN_WAVES * SCAN_QPW;   // queries per workgroup tile
+constexpr int SCAN_CAP = 16;                      // per-lane candidate buffer entries
+
+// Key-side backward: consecutive sorted (key, pair) positions per slice.
+constexpr int SEG_SLICE = 64;
+// Radix sort: elements per block tile, digit width.
+constexpr int SORT_THREADS = 256;
+constexpr int SORT_ITEMS = 16;
+constexpr int SORT_TILE = SORT_THREADS * SORT_ITEMS;
+constexpr int SORT_BITS = 8;
+constexpr int SORT_BINS = 1 << SORT_BITS;
+// Device-wide exclusive scan tile.
+constexpr int SCAN_THREADS = 256;
+constexpr int SCAN_ITEMS = 16;
+constexpr int SCAN_TILE_ELEMS = SCAN_THREADS * SCAN_ITEMS;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Smallest list length the scan kernel is instantiated for that holds k.
+int scan_list_len(int topk);
+
+// Maximum number of query tiles for N nodes in num_graphs graphs.
+inline int64_t scan_max_tiles(int64_t N, int num_graphs) {
+  return ceil_div(N, SCAN_QT) + (num_graphs > 1 ? num_graphs : 0);
+}
+
+// ---------------------------------------------------------------- launchers
+// All return hipSuccess or the first launch error.  No allocation, no sync.
+
+// Ragged tile plan: tiles[t] = (graph, first query) for t < total, (-1, 0)
+// beyond; tile_start is [B+1] scratch.
+hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_tiles,
+                            int32_t* tile_start, int2* tiles, hipStream_t s);
+
+// Fused score scan + running top-k.  Writes topk_idx / topk_score.
+hipError_t launch_score_topk(const uint16_t* q, const uint16_t* k, int64_t N, int H, int d,
+                             int topk, const int32_t* offsets, int num_graphs,
+                             const int2* tiles, int64_t max_tiles, int32_t* topk_idx,
+                             float* topk_score, hipStream_t s);
+
+// Gather the selected V rows, softmax over saved scores, weighted sum.
+hipError_t launch_gather_av(const uint16_t* v, int64_t N, int H, int d, int topk,
+                            const int32_t* topk_idx, const float* topk_score, float* out,
+                            hipStream_t s);
+
+// Backward, query side: dq and the per-pair (p, ds).
+hipError_t launch_bwd_query(const uint16_t* k, const uint16_t* v, int64_t N, int H, int d,
+                            int topk, const int32_t* topk_idx, const float* topk_score,
+                            const float* dout, float* dq, float2* pairs, hipStream_t s);
+
+// Backward, selection transpose: stable sort of pairs by key h*N + j, key
+// segment pointers key_ptr[H*N + 2].
+struct SortScratch {
+  uint32_t* keys[2];
+  uint32_t* vals[2];
+  int32_t* hist;          // SORT_BINS * nblocks
+  int32_t* scan_aux;      // block sums of the device-wide scan
+  int32_t* counts;        // H*N + 2
+  int32_t* key_ptr;       // H*N + 2
+  int final_buf;          // which of keys/vals holds the sorted result
+};
+size_t sort_scratch_bytes(int64_t P, int64_t HN);
+void sort_scratch_carve(void* base, int64_t P, int64_t HN, SortScratch* sc);
+hipError_t launch_selection_transpose(const int32_t* topk_idx, int64_t N, int H, int topk,
+                                      SortScratch* sc, hipStream_t s);
+
+// Backward, key side: dk, dv by segmented reduction over the sorted pairs.
+size_t segreduce_scratch_bytes(int64_t P, int d);
+hipError_t launch_bwd_keys(const uint16_t* q, const float* dout, int64_t N, int H, int d,
+                           int topk, const float2* pairs, const SortScratch* sc,
+                           double* partials, float* dk, float* dv, hipStream_t s);
+
+// Device-wide exclusive scan of int32 (aux: scan_aux_elems(n) ints).
+int64_t scan_aux_elems(int64_t n);
+hipError_t launch_exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* aux,
+                                 hipStream_t s);
+
+}  // namespace kmip

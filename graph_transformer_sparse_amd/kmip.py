@@ -1,0 +1,149 @@
+"""Thin Python binding over libkmip's C ABI (include/kmip.h).
+
+Argument marshalling only: PyTorch provides device memory and the current
+HIP stream; every step of the computation runs in the library's kernels.
+The binding refuses to run when libkmip.so is missing -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkmip.so")
+
+KMIP_OK = 0
+_lib = None
+
+
+class KmipError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkmip.so (after torch, so that both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m graph_transformer_sparse_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.kmip_status_string.argtypes = [i32]
+    L.kmip_status_string.restype = ctypes.c_char_p
+    L.kmip_version.argtypes = []
+    L.kmip_version.restype = i32
+    L.kmip_forward_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    L.kmip_forward_workspace_bytes.restype = sz
+    L.kmip_backward_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    L.kmip_backward_workspace_bytes.restype = sz
+    L.kmip_forward.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.kmip_forward.restype = i32
+    L.kmip_backward.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
+                                vp, vp, sz, vp]
+    L.kmip_backward.restype = i32
+    _lib = L
+    return L
+
+
+EXPORTED = ["kmip_status_string", "kmip_version", "kmip_forward_workspace_bytes",
+            "kmip_backward_workspace_bytes", "kmip_forward", "kmip_backward"]
+
+
+def status_string(status: int) -> str:
+    return lib().kmip_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().kmip_version())
+
+
+def forward_workspace_bytes(N: int, H: int, d: int, topk: int, num_graphs: int = 0) -> int:
+    return int(lib().kmip_forward_workspace_bytes(N, H, d, topk, num_graphs))
+
+
+def backward_workspace_bytes(N: int, H: int, d: int, topk: int, num_graphs: int = 0) -> int:
+    return int(lib().kmip_backward_workspace_bytes(N, H, d, topk, num_graphs))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor [N, H, d]")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have the same shape")
+
+
+def _graphs(graph_offsets):
+    if graph_offsets is None:
+        return None, 0
+    if graph_offsets.dtype != torch.int32 or not graph_offsets.is_cuda:
+        raise ValueError("graph_offsets must be an int32 CUDA tensor [B+1]")
+    return graph_offsets, int(graph_offsets.numel()) - 1
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
+            graph_offsets: Optional[torch.Tensor] = None, *, out=None, topk_idx=None,
+            topk_score=None, workspace=None, stream=None):
+    """k-MIP attention forward.  Returns (out fp32, topk_idx int32, topk_score fp32)."""
+    _check_qkv(q, k, v)
+    N, H, d = q.shape
+    go, B = _graphs(graph_offsets)
+    dev = q.device
+    if out is None:
+        out = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((N, H, topk), dtype=torch.int32, device=dev)
+    if topk_score is None:
+        topk_score = torch.empty((N, H, topk), dtype=torch.float32, device=dev)
+    need = forward_workspace_bytes(N, H, d, topk, B)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().kmip_forward(_ptr(q), _ptr(k), _ptr(v), N, H, d, topk, _ptr(go), B, _ptr(out),
+                            _ptr(topk_idx), _ptr(topk_score), _ptr(workspace), ws_bytes,
+                            _stream(stream))
+    if st != KMIP_OK:
+        raise KmipError(st, "kmip_forward")
+    return out, topk_idx, topk_score
+
+
+def backward(q, k, v, topk: int, topk_idx, topk_score, dout,
+             graph_offsets: Optional[torch.Tensor] = None, *, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """k-MIP attention backward with the selection fixed.  Returns (dq, dk, dv) fp32."""
+    _check_qkv(q, k, v)
+    N, H, d = q.shape
+    go, B = _graphs(graph_offsets)
+    dev = q.device
+    if dout.dtype != torch.float32 or not dout.is_contiguous() or tuple(dout.shape) != (N, H, d):
+        raise ValueError("dout must be a contiguous float32 tensor [N, H, d]")
+    dq = torch.empty((N, H, d), dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty((N, H, d), dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty((N, H, d), dtype=torch.float32, device=dev) if dv is None else dv
+    need = backward_workspace_bytes(N, H, d, topk, B)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().kmip_backward(_ptr(q), _ptr(k), _ptr(v), N, H, d, topk, _ptr(go), B,
+                             _ptr(topk_idx), _ptr(topk_score), _ptr(dout), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != KMIP_OK:
+        raise KmipError(st, "kmip_backward")
+    return dq, dk, dv

@@ -1,0 +1,126 @@
+/*
+ * libkmip -- k-Maximum-Inner-Product (k-MIP) attention on AMD Instinct MI355X
+ * (gfx950).  C ABI.
+ *
+ * The operation (page "k-Maximum Inner Product Attention for Graph
+ * Transformers and the Expressive Power of GraphGPS", Abstract): for every
+ * query node i and head h, score every key node j of the same graph by the
+ * inner product s_ij = <q_ih, k_jh>, keep the top-k keys, take a softmax over
+ * those k scores and return the softmax-weighted sum of their value rows.
+ * The N x N score matrix is never stored: memory is O(N * H * k) beyond the
+ * inputs and outputs.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Layout: q, k, v, out, dout, dq, dk, dv are row-major [N][H][d] (the
+ *    natural x.view(N, H, d) of an [N, H*d] matrix).  q, k, v are bfloat16
+ *    bit patterns (uint16); every other floating-point array is fp32.
+ *    topk_idx / topk_score are [N][H][topk].
+ *  - Ownership: every pointer is device memory owned by the caller.  The
+ *    library allocates nothing, keeps no state between calls and is
+ *    reentrant; scratch space comes in through `workspace`.
+ *  - Streams: all work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream).  A return of KMIP_OK means the work was enqueued; the
+ *    library never synchronises.
+ *  - Graphs: graph_offsets is a device int32 array [num_graphs + 1], monotone,
+ *    starting at 0 and ending at N; a query attends only to keys of its own
+ *    graph (block-diagonal batching).  graph_offsets == NULL or
+ *    num_graphs == 0 means one graph of N nodes.  These device-side
+ *    preconditions, and finite inputs, are not checked.
+ *  - Semantics: scores are the unscaled inner product (fold a temperature
+ *    such as 1/sqrt(d) into q).  Heads are independent.  A query's
+ *    candidates include itself.  Ties are broken by ascending node id.  A
+ *    graph of n_b < topk nodes uses k_eff = n_b keys; unused slots hold index
+ *    -1 and score -inf.  Results are bitwise deterministic.
+ *  - Errors: arguments are validated on the host before any HIP call;
+ *    nothing is enqueued when a check fails.
+ *      null required pointer, N < 1, H < 1, num_graphs < 0,
+ *      num_graphs >= 2 with graph_offsets == NULL, q/k/v/out/dout/dq/dk/dv
+ *      not 16-byte aligned, workspace not aligned (16 bytes forward,
+ *      256 bytes backward)                     -> KMIP_ERR_INVALID_VALUE
+ *      d not in {32, 64}, topk not in [1, 64],
+ *      N * H * topk >= 2^31                      -> KMIP_ERR_UNSUPPORTED
+ *      workspace smaller than the *_workspace_bytes figure
+ *                                               -> KMIP_ERR_WORKSPACE
+ *      a launch error reported by hipGetLastError -> KMIP_ERR_LAUNCH
+ */
+#ifndef KMIP_H_
+#define KMIP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KMIP_OK = 0,
+  KMIP_ERR_INVALID_VALUE = 1,
+  KMIP_ERR_UNSUPPORTED = 2,
+  KMIP_ERR_WORKSPACE = 3,
+  KMIP_ERR_LAUNCH = 4
+} kmip_status_t;
+
+/* A hipStream_t, passed as an opaque pointer so that this header needs no
+ * HIP include. */
+typedef void* kmip_stream_t;
+
+/* Static, NUL-terminated description of a status code. */
+const char* kmip_status_string(kmip_status_t status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int kmip_version(void);
+
+/* Bytes of device workspace kmip_forward needs for these sizes (0 is a valid
+ * answer).  Depends only on the arguments. */
+size_t kmip_forward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs);
+
+/* Bytes of device workspace kmip_backward needs for these sizes. */
+size_t kmip_backward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs);
+
+/*
+ * k-MIP attention forward (page "k-Maximum Inner Product Attention for Graph
+ * Transformers ...", Abstract: top-k selection by inner product, softmax
+ * over the selected scores, weighted sum of the selected value rows).
+ *
+ *  q, k, v      in   bf16 [N][H][d]
+ *  out          out  fp32 [N][H][d]
+ *  topk_idx     out  int32 [N][H][topk], global node ids, best first
+ *  topk_score   out  fp32 [N][H][topk], the selected inner products (kept for
+ *                    kmip_backward)
+ *  workspace    scratch of at least kmip_forward_workspace_bytes(...) bytes
+ *                    (may be NULL when that figure is 0)
+ */
+kmip_status_t kmip_forward(const void* q, const void* k, const void* v, int64_t N, int H,
+                           int d, int topk, const int32_t* graph_offsets, int num_graphs,
+                           float* out, int32_t* topk_idx, float* topk_score,
+                           void* workspace, size_t workspace_bytes, kmip_stream_t stream);
+
+/*
+ * k-MIP attention backward with the forward selection held fixed: gradients
+ * of L = sum(dout * out) flow through the selected entries only.  With
+ * p = softmax of the saved scores, dp_ij = dout_i . v_j,
+ * D_i = sum_j p_ij dp_ij and ds_ij = p_ij (dp_ij - D_i):
+ *   dq_i = sum_j ds_ij k_j,  dk_j = sum_i ds_ij q_i,  dv_j = sum_i p_ij dout_i.
+ * Every row of dq, dk and dv is written; keys no query selected get exact
+ * zeros.  The key-side sums run in a fixed order (no atomics), so the result
+ * is bitwise repeatable.
+ *
+ *  q, k, v                 in   bf16 [N][H][d] (as given to kmip_forward)
+ *  topk_idx, topk_score    in   as written by kmip_forward
+ *  dout                    in   fp32 [N][H][d]
+ *  dq, dk, dv              out  fp32 [N][H][d]
+ *  workspace               scratch of at least kmip_backward_workspace_bytes(...)
+ */
+kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t N, int H,
+                            int d, int topk, const int32_t* graph_offsets, int num_graphs,
+                            const int32_t* topk_idx, const float* topk_score,
+                            const float* dout, float* dq, float* dk, float* dv,
+                            void* workspace, size_t workspace_bytes, kmip_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KMIP_H_ */

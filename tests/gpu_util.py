@@ -1,0 +1,38 @@
+"""Helpers for the GPU tests: move a workload to the device, call libkmip
+through its binding, bring results back."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from graph_transformer_sparse_amd import kmip
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def to_device(w, device="cuda"):
+    t = dict(q=bf16_tensor(w.q, device), k=bf16_tensor(w.k, device), v=bf16_tensor(w.v, device))
+    t["offsets"] = (torch.from_numpy(w.offsets).to(device) if w.num_graphs > 1 else None)
+    if w.dout is not None:
+        t["dout"] = torch.from_numpy(w.dout).to(device)
+    return t
+
+
+def run_forward(w, t=None):
+    t = to_device(w) if t is None else t
+    out, idx, score = kmip.forward(t["q"], t["k"], t["v"], w.topk, t["offsets"])
+    torch.cuda.synchronize()
+    return t, out, idx, score
+
+
+def run_backward(w, t, idx, score):
+    dq, dk, dv = kmip.backward(t["q"], t["k"], t["v"], w.topk, idx, score, t["dout"],
+                               t["offsets"])
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def np_(x):
+    return x.detach().cpu().numpy()

@@ -1,0 +1,81 @@
+"""libkmip loads, exports every symbol its header declares, and rejects bad
+arguments on the host (before any HIP call).  CPU only: no kernel runs."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kmip.h")
+
+torch = pytest.importorskip("torch")
+from graph_transformer_sparse_amd import kmip  # noqa: E402
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(1 << 20)       # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kmip_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    L = kmip.lib()
+    names = declared_functions()
+    assert set(names) == set(kmip.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    assert kmip.status_string(OK).startswith("KMIP_OK")
+    assert "workspace" in kmip.status_string(WORKSPACE)
+    assert kmip.version() >= 10000
+
+
+def _fwd(q=FAKE, k=FAKE, v=FAKE, N=128, H=2, d=32, topk=15, offs=None, B=0, out=FAKE,
+         idx=FAKE, score=FAKE, ws=None, ws_bytes=0):
+    return kmip.lib().kmip_forward(q, k, v, N, H, d, topk, offs, B, out, idx, score, ws,
+                                   ws_bytes, None)
+
+
+def _bwd(N=128, H=2, d=32, topk=15, ws=FAKE, ws_bytes=1 << 40, dq=FAKE, offs=None, B=0):
+    return kmip.lib().kmip_backward(FAKE, FAKE, FAKE, N, H, d, topk, offs, B, FAKE, FAKE, FAKE,
+                                    dq, FAKE, FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(idx=None), INVALID),
+    (dict(N=0), INVALID), (dict(H=0), INVALID), (dict(B=-1), INVALID),
+    (dict(B=3, offs=None), INVALID),
+    (dict(q=ctypes.c_void_p((1 << 20) + 8)), INVALID),
+    (dict(d=48), UNSUPPORTED), (dict(d=128), UNSUPPORTED), (dict(topk=0), UNSUPPORTED),
+    (dict(topk=65), UNSUPPORTED), (dict(N=1 << 30, H=4), UNSUPPORTED),
+    (dict(B=4, offs=FAKE, ws=None, ws_bytes=0), WORKSPACE),
+    (dict(B=4, offs=FAKE, ws=FAKE, ws_bytes=16), WORKSPACE),
+])
+def test_forward_rejects(kw, status):
+    assert _fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=None), INVALID), (dict(N=-5), INVALID), (dict(d=16), UNSUPPORTED),
+    (dict(topk=100), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16)), INVALID),
+])
+def test_backward_rejects(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_workspace_sizes_are_linear_in_n():
+    f = kmip.forward_workspace_bytes
+    b = kmip.backward_workspace_bytes
+    assert f(100000, 4, 32, 15, 0) == 0                     # one graph: no scratch
+    assert f(100000, 4, 32, 15, 64) > 0
+    b1, b2 = b(100000, 4, 32, 15), b(200000, 4, 32, 15)
+    assert 1.9 < b2 / b1 < 2.1                              # O(N * H * k)
+    assert b(500000, 4, 32, 15) < 1.5e9
+    assert f(0, 4, 32, 15, 0) == 0 and b(10, 4, 48, 15) == 0   # invalid shapes -> 0

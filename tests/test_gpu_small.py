@@ -1,0 +1,138 @@
+"""GPU parity on small seeded cases: every row against the fp64 oracle.
+
+Sizes span several 128-query tiles and 32-key MFMA blocks with ragged tails,
+every instantiated list length, d in {32, 64}, tiny and empty graphs,
+graphs smaller than k, exact score ties, and the backward pass.
+"""
+import numpy as np
+import pytest
+
+import oracle.kmip_oracle as orc
+from tests.parity import assert_rows_close, check_selection, decode
+from workloads import small_case, with_offsets
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _forward_check(w, rows=None):
+    from tests.gpu_util import np_, run_forward
+    print(f"[case] {w.name} n={w.n} H={w.heads} d={w.d} k={w.topk} B={w.num_graphs}", flush=True)
+    t, out, idx, score = run_forward(w)
+    q, k, v = decode(w)
+    idx_n, score_n, out_n = np_(idx), np_(score), np_(out)
+    rows = range(w.n) if rows is None else rows
+    st = check_selection(idx_n, score_n, q, k, w.offsets, w.topk, rows)
+    rows = np.asarray(list(rows))
+    ref = orc.attend_on_sets(q, k, v, idx_n[rows].astype(np.int64), rows=rows)
+    assert_rows_close(out_n[rows], ref["out"], "out")
+    return t, out, idx, score, st
+
+
+def _backward_check(w, t, idx, score):
+    from tests.gpu_util import np_, run_backward
+    dq, dk, dv = run_backward(w, t, idx, score)
+    q, k, v = decode(w)
+    rq, rk, rv = orc.kmip_backward_on_sets(q, k, v, np_(idx).astype(np.int64),
+                                           w.dout.astype(np.float64))
+    assert_rows_close(np_(dq), rq, "dq")
+    assert_rows_close(np_(dk), rk, "dk")
+    assert_rows_close(np_(dv), rv, "dv")
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("n,heads,d,topk", [
+    (300, 2, 32, 15), (97, 1, 32, 15), (1000, 1, 64, 15), (517, 3, 64, 5),
+    (33, 2, 32, 32), (260, 1, 32, 1), (130, 2, 32, 64),
+])
+def test_single_graph_forward_backward(n, heads, d, topk):
+    w = small_case(n, heads, d, topk, seed=1000 + n)
+    t, out, idx, score, st = _forward_check(w)
+    _backward_check(w, t, idx, score)
+
+
+@pytest.mark.parametrize("topk", [1, 2, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 45, 48, 63, 64])
+def test_every_list_length(topk):
+    w = small_case(400, 2, 32, topk, seed=2000 + topk)
+    _forward_check(w)
+
+
+def test_clustered_structure():
+    w = small_case(3000, 4, 32, 15, law="clustered", clusters=16, seed=77)
+    t, out, idx, score, st = _forward_check(w)
+    _backward_check(w, t, idx, score)
+
+
+@pytest.mark.parametrize("sizes,topk", [
+    ([1, 3, 10, 17, 130, 257], 15),
+    ([5, 0, 200, 1, 64, 0, 129], 8),
+    ([2, 40, 3], 64),
+    ([128, 128, 1], 15),
+    ([700], 15),
+])
+def test_ragged_graphs(sizes, topk):
+    w = with_offsets(f"ragged_{len(sizes)}_{topk}", sizes, heads=2, d=32, topk=topk,
+                     law="iid", seed=sum(sizes) + topk)
+    t, out, idx, score, st = _forward_check(w)
+    _backward_check(w, t, idx, score)
+
+
+def test_single_node_graph_is_identity():
+    from tests.gpu_util import np_, run_backward, run_forward
+    w = with_offsets("singletons", [1, 1, 1, 1, 1], heads=2, d=64, topk=4, seed=9)
+    t, out, idx, score = run_forward(w)
+    q, k, v = decode(w)
+    assert np.array_equal(np_(out), v.astype(np.float32))
+    dq, dk, dv = run_backward(w, t, idx, score)
+    assert not np_(dq).any() and not np_(dk).any()
+    assert np.array_equal(np_(dv), w.dout)
+
+
+def test_exact_ties_follow_ascending_id():
+    """Duplicated key rows give bitwise-equal scores; the smaller node id wins."""
+    from tests.gpu_util import np_, run_forward
+    w = small_case(256, 2, 32, 6, seed=31)
+    w.k = w.k[np.arange(256) % 8]                        # 8 distinct keys, 32 copies each
+    t, out, idx, score = run_forward(w)
+    q, k, v = decode(w)
+    fw = orc.kmip_forward(q, k, v, None, w.topk)
+    assert np.array_equal(np_(idx), fw["idx"].astype(np.int32))
+
+
+def test_full_attention_limit():
+    """k >= n_b: every key of the graph is kept, so the output is full softmax
+    attention (oracle pinned to torch SDPA in fp64)."""
+    w = with_offsets("full", [20, 33, 64], heads=2, d=32, topk=64, seed=4)
+    _forward_check(w)
+
+
+def test_deterministic_repeat():
+    from tests.gpu_util import np_, run_backward, run_forward, to_device
+    w = small_case(2000, 4, 32, 15, law="clustered", clusters=8, seed=5)
+    t = to_device(w)
+    a = run_forward(w, t)
+    b = run_forward(w, t)
+    for x, y in zip(a[1:], b[1:]):
+        assert np.array_equal(np_(x), np_(y))
+    ga = run_backward(w, t, a[2], a[3])
+    gb = run_backward(w, t, a[2], a[3])
+    for x, y in zip(ga, gb):
+        assert np.array_equal(np_(x), np_(y))
+
+
+def test_gradient_identities_on_gpu_outputs():
+    from tests.gpu_util import np_, run_backward, run_forward
+    w = with_offsets("ident", [500, 300], heads=2, d=32, topk=15, seed=6)
+    t, out, idx, score = run_forward(w)
+    dq, dk, dv = (np_(x).astype(np.float64) for x in run_backward(w, t, idx, score))
+    for lo, hi in orc.graph_ranges(w.offsets, w.n):
+        sdo = w.dout[lo:hi].astype(np.float64).sum(0)
+        assert np.allclose(dv[lo:hi].sum(0), sdo, atol=1e-3 * np.abs(sdo).max() + 1e-4)
+        assert np.abs(dk[lo:hi].sum(0)).max() <= 1e-3 * np.abs(dk[lo:hi]).sum(0).max() + 1e-5

@@ -68,16 +68,15 @@ size_t kmip_backward_workspace_bytes(int64_t N, int H, int d, int topk, int num_
   return backward_ws(N, H, d, topk);
 }
 
-kmip_status_t kmip_forward(const void* q, const void* k, const void* v, int64_t N, int H,
-                           int d, int topk, const int32_t* graph_offsets, int num_graphs,
-                           float* out, int32_t* topk_idx, float* topk_score, void* workspace,
-                           size_t workspace_bytes, kmip_stream_t stream) {
-  if (!q || !k || !v || !out || !topk_idx || !topk_score) return KMIP_ERR_INVALID_VALUE;
+kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, int d, int topk,
+                              const int32_t* graph_offsets, int num_graphs, int32_t* topk_idx,
+                              float* topk_score, void* workspace, size_t workspace_bytes,
+                              kmip_stream_t stream) {
+  if (!q || !k || !topk_idx || !topk_score) return KMIP_ERR_INVALID_VALUE;
   kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
   if (st != KMIP_OK) return st;
   if (num_graphs > 1 && graph_offsets == nullptr) return KMIP_ERR_INVALID_VALUE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(topk_idx, 4) || !aligned(topk_score, 4))
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(topk_idx, 4) || !aligned(topk_score, 4))
     return KMIP_ERR_INVALID_VALUE;
   const bool single = single_graph(graph_offsets, num_graphs);
   const size_t need = single ? 0 : forward_ws(N, num_graphs);
@@ -95,13 +94,39 @@ kmip_status_t kmip_forward(const void* q, const void* k, const void* v, int64_t 
                                         tiles, s));
     if (st != KMIP_OK) return st;
   }
-  st = launch_status(launch_score_topk(static_cast<const uint16_t*>(q),
-                                       static_cast<const uint16_t*>(k), N, H, d, topk,
-                                       single ? nullptr : graph_offsets, num_graphs, tiles,
-                                       max_tiles, topk_idx, topk_score, s));
+  return launch_status(launch_score_topk(static_cast<const uint16_t*>(q),
+                                         static_cast<const uint16_t*>(k), N, H, d, topk,
+                                         single ? nullptr : graph_offsets, num_graphs, tiles,
+                                         max_tiles, topk_idx, topk_score, s));
+}
+
+kmip_status_t kmip_gather_softmax_av(const void* v, int64_t N, int H, int d, int topk,
+                                     const int32_t* topk_idx, const float* topk_score,
+                                     float* out, kmip_stream_t stream) {
+  if (!v || !topk_idx || !topk_score || !out) return KMIP_ERR_INVALID_VALUE;
+  kmip_status_t st = check_shape(N, H, d, topk, 0);
   if (st != KMIP_OK) return st;
+  if (!aligned(v, 16) || !aligned(out, 16) || !aligned(topk_idx, 4) || !aligned(topk_score, 4))
+    return KMIP_ERR_INVALID_VALUE;
   return launch_status(launch_gather_av(static_cast<const uint16_t*>(v), N, H, d, topk,
-                                        topk_idx, topk_score, out, s));
+                                        topk_idx, topk_score, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+kmip_status_t kmip_forward(const void* q, const void* k, const void* v, int64_t N, int H,
+                           int d, int topk, const int32_t* graph_offsets, int num_graphs,
+                           float* out, int32_t* topk_idx, float* topk_score, void* workspace,
+                           size_t workspace_bytes, kmip_stream_t stream) {
+  if (!q || !k || !v || !out || !topk_idx || !topk_score) return KMIP_ERR_INVALID_VALUE;
+  if (!aligned(v, 16) || !aligned(out, 16)) {
+    const kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
+    return st != KMIP_OK ? st : KMIP_ERR_INVALID_VALUE;
+  }
+  const kmip_status_t st = kmip_score_topk(q, k, N, H, d, topk, graph_offsets, num_graphs,
+                                           topk_idx, topk_score, workspace, workspace_bytes,
+                                           stream);
+  if (st != KMIP_OK) return st;
+  return kmip_gather_softmax_av(v, N, H, d, topk, topk_idx, topk_score, out, stream);
 }
 
 kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t N, int H,

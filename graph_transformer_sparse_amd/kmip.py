@@ -49,12 +49,17 @@ def lib() -> ctypes.CDLL:
     L.kmip_backward.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
                                 vp, vp, sz, vp]
     L.kmip_backward.restype = i32
+    L.kmip_score_topk.argtypes = [vp, vp, i64, i32, i32, i32, vp, i32, vp, vp, vp, sz, vp]
+    L.kmip_score_topk.restype = i32
+    L.kmip_gather_softmax_av.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp]
+    L.kmip_gather_softmax_av.restype = i32
     _lib = L
     return L
 
 
 EXPORTED = ["kmip_status_string", "kmip_version", "kmip_forward_workspace_bytes",
-            "kmip_backward_workspace_bytes", "kmip_forward", "kmip_backward"]
+            "kmip_backward_workspace_bytes", "kmip_forward", "kmip_backward",
+            "kmip_score_topk", "kmip_gather_softmax_av"]
 
 
 def status_string(status: int) -> str:
@@ -123,6 +128,44 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
     if st != KMIP_OK:
         raise KmipError(st, "kmip_forward")
     return out, topk_idx, topk_score
+
+
+def score_topk(q: torch.Tensor, k: torch.Tensor, topk: int,
+               graph_offsets: Optional[torch.Tensor] = None, *, topk_idx=None,
+               topk_score=None, workspace=None, stream=None):
+    """Top-k selection only.  Returns (topk_idx int32, topk_score fp32)."""
+    _check_qkv(q, k, k)
+    N, H, d = q.shape
+    go, B = _graphs(graph_offsets)
+    dev = q.device
+    if topk_idx is None:
+        topk_idx = torch.empty((N, H, topk), dtype=torch.int32, device=dev)
+    if topk_score is None:
+        topk_score = torch.empty((N, H, topk), dtype=torch.float32, device=dev)
+    need = forward_workspace_bytes(N, H, d, topk, B)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().kmip_score_topk(_ptr(q), _ptr(k), N, H, d, topk, _ptr(go), B, _ptr(topk_idx),
+                               _ptr(topk_score), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != KMIP_OK:
+        raise KmipError(st, "kmip_score_topk")
+    return topk_idx, topk_score
+
+
+def gather_softmax_av(v: torch.Tensor, topk_idx: torch.Tensor, topk_score: torch.Tensor, *,
+                      out=None, stream=None):
+    """Softmax over saved scores and weighted sum of selected V rows."""
+    _check_qkv(v, v, v)
+    N, H, d = v.shape
+    topk = int(topk_idx.shape[-1])
+    if out is None:
+        out = torch.empty((N, H, d), dtype=torch.float32, device=v.device)
+    st = lib().kmip_gather_softmax_av(_ptr(v), N, H, d, topk, _ptr(topk_idx), _ptr(topk_score),
+                                      _ptr(out), _stream(stream))
+    if st != KMIP_OK:
+        raise KmipError(st, "kmip_gather_softmax_av")
+    return out
 
 
 def backward(q, k, v, topk: int, topk_idx, topk_score, dout,

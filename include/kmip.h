@@ -98,6 +98,32 @@ kmip_status_t kmip_forward(const void* q, const void* k, const void* v, int64_t 
                            void* workspace, size_t workspace_bytes, kmip_stream_t stream);
 
 /*
+ * First stage of kmip_forward: the top-k selection alone (page "k-Maximum
+ * Inner Product Attention for Graph Transformers ...", Abstract: the key
+ * nodes with the k largest inner products per query).  Writes topk_idx and
+ * topk_score exactly as kmip_forward does; the N x N scores exist only as
+ * register tiles.  Arguments, workspace and errors as for kmip_forward
+ * (v and out are not taken).
+ */
+kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, int d, int topk,
+                              const int32_t* graph_offsets, int num_graphs, int32_t* topk_idx,
+                              float* topk_score, void* workspace, size_t workspace_bytes,
+                              kmip_stream_t stream);
+
+/*
+ * Second stage of kmip_forward: softmax over the saved scores of each row and
+ * the weighted sum of the selected value rows (same page, Abstract).
+ *  v                        in   bf16 [N][H][d]
+ *  topk_idx, topk_score     in   as written by kmip_score_topk (rows sorted
+ *                                best first; -1 / -inf on unused slots)
+ *  out                      out  fp32 [N][H][d]
+ * Needs no workspace.  Errors as for kmip_forward.
+ */
+kmip_status_t kmip_gather_softmax_av(const void* v, int64_t N, int H, int d, int topk,
+                                     const int32_t* topk_idx, const float* topk_score,
+                                     float* out, kmip_stream_t stream);
+
+/*
  * k-MIP attention backward with the forward selection held fixed: gradients
  * of L = sum(dout * out) flow through the selected entries only.  With
  * p = softmax of the saved scores, dp_ij = dout_i . v_j,

@@ -2,6 +2,6 @@
 imported by the GPU library)."""
 from .kmip_oracle import (  # noqa: F401
     bf16_bits_to_f64, graph_ranges, scores_block, select_topk_row, softmax_selected,
-    kmip_forward, attend_on_sets, query_grads, kmip_backward_on_sets, kmip_backward, row_scores,
+    kmip_forward, attend_on_sets, query_grads, kmip_backward_on_sets, kmip_backward_rows, kmip_backward, row_scores,
     dq_rows_on_sets, dkv_keys_on_sets,
 )

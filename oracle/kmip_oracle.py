@@ -197,6 +197,31 @@ def kmip_backward_on_sets(q, k, v, idx, dout, scale: float = 1.0):
     return dq, dk, dv
 
 
+def kmip_backward_rows(q, k, v, rows, idx_rows, dout, scale: float = 1.0):
+    """Backward contributions of a subset of query rows (selection fixed).
+
+    idx_rows: int [R][H][topk] for the node ids in rows.  Returns dq of those
+    rows [R][H][d] and the dk, dv contributions they make ([N][H][d]); the
+    full gradients are the sums of such contributions over all rows.
+    """
+    n, heads, d = q.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((rows.size, heads, d))
+    dk = np.zeros((n, heads, d))
+    dv = np.zeros((n, heads, d))
+    for r, i in enumerate(rows):
+        for h in range(heads):
+            sel = idx_rows[r, h]
+            js = sel[sel >= 0]
+            if js.size == 0:
+                continue
+            p, ds, dq[r, h, :] = query_grads(q[i, h, :], k[js, h, :], v[js, h, :],
+                                             dout[i, h, :], scale)
+            np.add.at(dk[:, h, :], js, scale * ds[:, None] * q[i, h, :][None, :])
+            np.add.at(dv[:, h, :], js, p[:, None] * dout[i, h, :][None, :])
+    return dq, dk, dv
+
+
 def kmip_backward(q, k, v, offsets, topk: int, dout, scale: float = 1.0):
     """Forward selection, then the fixed-selection gradients."""
     fw = kmip_forward(q, k, v, offsets, topk, scale=scale)

@@ -23,6 +23,10 @@ CFLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
     # Packed fp32 VALU ops are kept out of every kernel.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Inputs are finite by contract: min/max need no NaN canonicalisation.
+    "-fno-honor-nans",
+    # MFMA accumulators live in VGPRs, read by the VALU without copies.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

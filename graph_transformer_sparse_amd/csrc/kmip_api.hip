@@ -26,10 +26,15 @@ kmip_status_t check_shape(int64_t N, int H, int d, int topk, int num_graphs) {
   return KMIP_OK;
 }
 
-size_t forward_ws(int64_t N, int num_graphs) {
-  if (num_graphs <= 1) return 0;
-  const int64_t tiles = scan_max_tiles(N, num_graphs);
-  return align256((size_t)(num_graphs + 1) * 4) + align256((size_t)tiles * sizeof(int2));
+// Forward workspace: per-row score thresholds [N*H] fp32, then (batched
+// graphs only) the tile plan.
+size_t forward_ws(int64_t N, int H, int num_graphs) {
+  size_t b = align256((size_t)N * H * sizeof(float));
+  if (num_graphs > 1) {
+    const int64_t tiles = scan_max_tiles(N, num_graphs);
+    b += align256((size_t)(num_graphs + 1) * 4) + align256((size_t)tiles * sizeof(int2));
+  }
+  return b;
 }
 
 size_t backward_ws(int64_t N, int H, int d, int topk) {
@@ -60,7 +65,7 @@ int kmip_version(void) { return kVersion; }
 
 size_t kmip_forward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
   if (check_shape(N, H, d, topk, num_graphs) != KMIP_OK) return 0;
-  return forward_ws(N, num_graphs);
+  return forward_ws(N, H, num_graphs);
 }
 
 size_t kmip_backward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
@@ -79,15 +84,17 @@ kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, in
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(topk_idx, 4) || !aligned(topk_score, 4))
     return KMIP_ERR_INVALID_VALUE;
   const bool single = single_graph(graph_offsets, num_graphs);
-  const size_t need = single ? 0 : forward_ws(N, num_graphs);
-  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return KMIP_ERR_WORKSPACE;
-  if (need > 0 && !aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
+  const size_t need = forward_ws(N, H, single ? 0 : num_graphs);
+  if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t max_tiles = scan_max_tiles(N, num_graphs);
+  char* w = static_cast<char*>(workspace);
+  float* thr = reinterpret_cast<float*>(w);
+  w += align256((size_t)N * H * sizeof(float));
   int2* tiles = nullptr;
   if (!single) {
-    char* w = static_cast<char*>(workspace);
     int32_t* tile_start = reinterpret_cast<int32_t*>(w);
     tiles = reinterpret_cast<int2*>(w + align256((size_t)(num_graphs + 1) * 4));
     st = launch_status(launch_tile_plan(graph_offsets, num_graphs, max_tiles, tile_start,
@@ -97,7 +104,7 @@ kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, in
   return launch_status(launch_score_topk(static_cast<const uint16_t*>(q),
                                          static_cast<const uint16_t*>(k), N, H, d, topk,
                                          single ? nullptr : graph_offsets, num_graphs, tiles,
-                                         max_tiles, topk_idx, topk_score, s));
+                                         max_tiles, thr, topk_idx, topk_score, s));
 }
 
 kmip_status_t kmip_gather_softmax_av(const void* v, int64_t N, int H, int d, int topk,

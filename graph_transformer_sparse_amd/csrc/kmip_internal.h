@@ -19,6 +19,7 @@ constexpr int SCAN_WAVES = 4;
 constexpr int SCAN_QPW = 32;
 constexpr int SCAN_QT = SCAN_WAVES * SCAN_QPW;   // queries per workgroup tile
 constexpr int SCAN_CAP = 16;                      // per-lane candidate buffer entries
+constexpr int SCAN_CHUNKS = 32;                   // threshold pass: chunks per lane
 
 // Key-side backward: consecutive sorted (key, pair) positions per slice.
 constexpr int SEG_SLICE = 64;
@@ -52,11 +53,13 @@ inline int64_t scan_max_tiles(int64_t N, int num_graphs) {
 hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_tiles,
                             int32_t* tile_start, int2* tiles, hipStream_t s);
 
-// Fused score scan + running top-k.  Writes topk_idx / topk_score.
+// Score scan in two passes: a threshold pass writing a per-row lower bound
+// of the k-th score into thr[N*H], then the exact running top-k seeded with
+// it.  Writes topk_idx / topk_score.
 hipError_t launch_score_topk(const uint16_t* q, const uint16_t* k, int64_t N, int H, int d,
                              int topk, const int32_t* offsets, int num_graphs,
-                             const int2* tiles, int64_t max_tiles, int32_t* topk_idx,
-                             float* topk_score, hipStream_t s);
+                             const int2* tiles, int64_t max_tiles, float* thr,
+                             int32_t* topk_idx, float* topk_score, hipStream_t s);
 
 // Gather the selected V rows, softmax over saved scores, weighted sum.
 hipError_t launch_gather_av(const uint16_t* v, int64_t N, int H, int d, int topk,

@@ -62,15 +62,35 @@ __device__ __forceinline__ void list_insert(float (&ls)[KP], int (&lj)[KP], floa
   lj[0] = b[0] ? j : lj[0];
 }
 
-template <int D, int KP>
+// Largest float below x (x finite or -inf; -inf stays -inf).
+__device__ __forceinline__ float next_down(float x) {
+  if (x == -kInf) return x;
+  if (x == 0.f) return __uint_as_float(0x80000001u);
+  const unsigned u = __float_as_uint(x);
+  return __uint_as_float(x > 0.f ? u - 1u : u + 1u);
+}
+
+// One kernel, two passes (PRE selects the pass).
+//
+// Pass 1 (PRE): the same MFMA scan, keeping only the running maximum of each
+// of SCAN_CHUNKS consecutive chunks of every lane's key stream.  Chunk maxima
+// are scores of distinct keys, so the k-th largest of a query's 2*SCAN_CHUNKS
+// chunk maxima is a lower bound T on its k-th largest score; it is written to
+// thr_buf.  A key with score < T cannot be selected.
+//
+// Pass 2 (!PRE): the exact running top-k, seeded with the threshold
+// next_down(T) (a key scoring exactly T may still win on id), so that only a
+// handful of keys per query ever reach the insertion path.
+template <int D, int KP, bool PRE>
 __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int64_t N, int H,
     int topk, const int32_t* __restrict__ offsets, int single_graph,
-    const int2* __restrict__ tiles, int32_t* __restrict__ out_idx,
-    float* __restrict__ out_score) {
+    const int2* __restrict__ tiles, float* __restrict__ thr_buf,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   using S = ScanShape<D>;
+  static_assert(SCAN_CAP * 8 == SCAN_CHUNKS * 4, "candidate and chunk areas share LDS");
   __shared__ __attribute__((aligned(16))) unsigned char kbuf[2 * S::CHUNK_BYTES];
-  __shared__ uint2 cbuf[SCAN_WAVES * SCAN_CAP * 64];
+  __shared__ __attribute__((aligned(16))) unsigned char wbuf[SCAN_WAVES * SCAN_CAP * 64 * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,6 +119,7 @@ __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
   const int64_t qrow = q0 + wave * SCAN_QPW + lrow;
   const bool qvalid = qrow < q1;
   const bool wave_active = (q0 + wave * SCAN_QPW) < q1;
+  const int64_t orow = qrow * H + h;
 
   // MFMA B operand: Q[query][16m + 8*lhalf .. +7] for query = lane%32.
   bf16x8_t qb[S::NM];
@@ -110,7 +131,7 @@ __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
   }
 
   // Slots [0, KP-topk) hold +inf sentinels that nothing displaces, so the
-  // live top-k always occupies the tail and the threshold is ls[KP-1].
+  // live top-k always occupies the tail and its k-th score is ls[KP-1].
   const int nsent = KP - topk;
   float ls[KP];
   int lj[KP];
@@ -119,9 +140,26 @@ __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
     ls[t] = t < nsent ? kInf : -kInf;
     lj[t] = -1;
   }
-  float thr = qvalid ? -kInf : kInf;
+
+  // Pass 1 state: running chunk maximum; chunk i of this lane at cml[i*64].
+  const int64_t nkeys = ke - kb;
+  const int nsub = (int)((nkeys + 31) / 32);
+  const int spc = (nsub + SCAN_CHUNKS - 1) / SCAN_CHUNKS;   // sub-blocks per chunk
+  float* cml = reinterpret_cast<float*>(wbuf) + wave * SCAN_CHUNKS * 64 + lane;
+  float cm = -kInf;
+  // Pass 2 state: reject threshold and the lane's candidate buffer.
+  float thr = kInf;
   int cnt = 0;
-  uint2* cb = cbuf + wave * SCAN_CAP * 64 + lane;   // entry c lives at cb[c * 64]
+  uint2* cb = reinterpret_cast<uint2*>(wbuf) + wave * SCAN_CAP * 64 + lane;
+  if constexpr (PRE) {
+#pragma unroll 1
+    for (int i = 0; i < SCAN_CHUNKS; ++i) cml[i * 64] = -kInf;
+  } else {
+    if (qvalid) thr = next_down(thr_buf[orow]);
+  }
+  // Retire the operand loads here so that the loop's MFMAs never wait on the
+  // vector-memory counter, which the K prefetch keeps busy.
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
 
   auto drain = [&]() __attribute__((always_inline)) {
     for (int c = 0; __ballot(c < cnt) != 0ull; ++c) {
@@ -130,15 +168,15 @@ __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
         const float sv = __uint_as_float(e.x);
         if (sv > thr) {
           list_insert<KP>(ls, lj, sv, (int)e.y);
-          thr = ls[KP - 1];
+          thr = fmaxf(thr, ls[KP - 1]);
         }
       }
     }
     cnt = 0;
   };
 
-  const int64_t nkeys = ke - kb;
   const int nchunks = (int)((nkeys + S::TK - 1) / S::TK);
+
   // Each thread moves PPT 16-byte pieces of a key chunk: global -> VGPR -> LDS.
   uint4 stg0, stg1;
   static_assert(S::PPT == 2, "two staging pieces per thread");
@@ -172,47 +210,72 @@ __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
     const int64_t cbase = kb + (int64_t)c * S::TK;
     const bool partial = cbase + S::TK > ke;
     if (wave_active) {
+      // Software pipeline: the MFMAs of sub-block st+1 are issued before the
+      // scores of sub-block st are examined.
+      floatx16_t acc[2];
+#define KMIP_MFMA(st, dst)                                                          \
+  {                                                                               \
+    dst = floatx16_t{};                                                           \
+    _Pragma("unroll") for (int m = 0; m < S::NM; ++m) {                           \
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(                      \
+          kc + ((st) * 32 + lrow) * S::ROWB + m * 32 + lhalf * 16);               \
+      dst = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[m], dst, 0, 0, 0);      \
+    }                                                                             \
+  }
+      KMIP_MFMA(0, acc[0]);
 #pragma unroll
       for (int st = 0; st < S::SUBT; ++st) {
-        floatx16_t acc = {};
-#pragma unroll
-        for (int m = 0; m < S::NM; ++m) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              kc + (st * 32 + lrow) * S::ROWB + m * 32 + lhalf * 16);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[m], acc, 0, 0, 0);
-        }
+        if (st + 1 < S::SUBT) KMIP_MFMA(st + 1, acc[(st + 1) & 1]);
         // acc[r] = <k_key, q_query>, key = key0 + 8*(r/4) + (r%4), query = lane%32.
         const int key0 = (int)(cbase + st * 32 + 4 * lhalf);
         float s[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = acc[r];
+        for (int r = 0; r < 16; ++r) s[r] = acc[st & 1][r];
         if (partial) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (key0 + 8 * (r >> 2) + (r & 3) >= ke) s[r] = -kInf;
         }
-        float g[4];
+        if constexpr (PRE) {
+          cm = fmaxf(fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                           fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))),
+                     fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
+                           fmaxf(fmaxf(s[12], s[13]), fmaxf(fmaxf(s[14], s[15]), cm))));
+          const int t = c * S::SUBT + st;              // sub-block index, uniform
+          if ((t + 1) % spc == 0 || t + 1 == nsub) {
+            if (t < nsub) cml[(t / spc) * 64] = cm;
+            cm = -kInf;
+          }
+        } else {
+          float g[4];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          g[qq] = fmaxf(fmaxf(s[4 * qq], s[4 * qq + 1]), fmaxf(s[4 * qq + 2], s[4 * qq + 3]));
-        const float mx = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
-        if (__ballot(mx > thr) != 0ull) {
+          for (int qq = 0; qq < 4; ++qq)
+            g[qq] = fmaxf(fmaxf(s[4 * qq], s[4 * qq + 1]), fmaxf(s[4 * qq + 2], s[4 * qq + 3]));
+          const float mx = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
+          if (__ballot(mx > thr) != 0ull) {
+            // At most 4 appends per passing quarter: make room first, so the
+            // sub-block has a single drain site.
+            int room = cnt;
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            if (__ballot(g[qq] > thr) != 0ull) {
-              if (__ballot(cnt > SCAN_CAP - 4) != 0ull) drain();
+            for (int qq = 0; qq < 4; ++qq) room += g[qq] > thr ? 4 : 0;
+            if (__ballot(room > SCAN_CAP) != 0ull) drain();
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float sv = s[4 * qq + r];
-                if (sv > thr) {
-                  cb[cnt * 64] = make_uint2(__float_as_uint(sv), (unsigned)(key0 + 8 * qq + r));
-                  ++cnt;
+            for (int qq = 0; qq < 4; ++qq) {
+              if (__ballot(g[qq] > thr) != 0ull) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const float sv = s[4 * qq + r];
+                  if (sv > thr) {
+                    cb[cnt * 64] = make_uint2(__float_as_uint(sv), (unsigned)(key0 + 8 * qq + r));
+                    ++cnt;
+                  }
                 }
               }
             }
           }
         }
       }
+#undef KMIP_MFMA
     }
     if (c + 1 < nchunks) KMIP_LSTORE((c + 1) & 1);
     __syncthreads();
@@ -220,37 +283,56 @@ __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
 #undef KMIP_GLOAD
 #undef KMIP_LSTORE
   if (!wave_active) return;
-  drain();
 
-  // Merge the two half-lists of each query by rank: live entry t of my list
-  // (slots [nsent, KP)) lands at (t - nsent) + the number of partner live
-  // entries ordered before it.  Lower-half lanes win exact (score, id) ties,
-  // which only padding entries (-inf, -1) can produce.
-  float ps[KP];
-  int pj[KP];
-#pragma unroll
-  for (int t = 0; t < KP; ++t) {
-    ps[t] = __shfl_xor(ls[t], 32);
-    pj[t] = __shfl_xor(lj[t], 32);
-  }
-  if (!qvalid) return;
-  const bool lower = lhalf == 0;
-  int32_t* oi = out_idx + (qrow * H + h) * topk;
-  float* os = out_score + (qrow * H + h) * topk;
-#pragma unroll
-  for (int t = 0; t < KP; ++t) {
-    if (t >= nsent) {
-      int rank = t - nsent;
-#pragma unroll
-      for (int u = 0; u < KP; ++u) {
-        const bool before = u >= nsent &&
-                            (ps[u] > ls[t] ||
-                             (ps[u] == ls[t] && (lower ? pj[u] < lj[t] : pj[u] <= lj[t])));
-        rank += before ? 1 : 0;
+  if constexpr (PRE) {
+    // k-th largest of the query's chunk maxima: this lane's and its partner's
+    // (lane ^ 32 scans the other half of the same query's keys).
+    __builtin_amdgcn_wave_barrier();
+    const float* cmp = reinterpret_cast<const float*>(wbuf) + wave * SCAN_CHUNKS * 64 + (lane ^ 32);
+    float t = -kInf;
+#pragma unroll 1
+    for (int i = 0; i < 2 * SCAN_CHUNKS; ++i) {
+      const float v = (i & 1) ? cmp[(i >> 1) * 64] : cml[(i >> 1) * 64];
+      if (v > t) {
+        list_insert<KP>(ls, lj, v, 0);
+        t = ls[KP - 1];
       }
-      if (rank < topk) {
-        oi[rank] = lj[t];
-        os[rank] = lj[t] < 0 ? -kInf : ls[t];
+    }
+    if (qvalid && lhalf == 0) thr_buf[orow] = t;
+    return;
+  } else {
+    drain();
+
+    // Merge the two half-lists of each query by rank: live entry t of my list
+    // (slots [nsent, KP)) lands at (t - nsent) + the number of partner live
+    // entries ordered before it.  Lower-half lanes win exact (score, id)
+    // ties, which only padding entries (-inf, -1) can produce.
+    float ps[KP];
+    int pj[KP];
+#pragma unroll
+    for (int t = 0; t < KP; ++t) {
+      ps[t] = __shfl_xor(ls[t], 32);
+      pj[t] = __shfl_xor(lj[t], 32);
+    }
+    if (!qvalid) return;
+    const bool lower = lhalf == 0;
+    int32_t* oi = out_idx + orow * topk;
+    float* os = out_score + orow * topk;
+#pragma unroll
+    for (int t = 0; t < KP; ++t) {
+      if (t >= nsent) {
+        int rank = t - nsent;
+#pragma unroll
+        for (int u = 0; u < KP; ++u) {
+          const bool before = u >= nsent &&
+                              (ps[u] > ls[t] ||
+                               (ps[u] == ls[t] && (lower ? pj[u] < lj[t] : pj[u] <= lj[t])));
+          rank += before ? 1 : 0;
+        }
+        if (rank < topk) {
+          oi[rank] = lj[t];
+          os[rank] = lj[t] < 0 ? -kInf : ls[t];
+        }
       }
     }
   }
@@ -307,26 +389,30 @@ __global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B,
 template <int D, int KP>
 hipError_t launch_scan_t(const uint16_t* q, const uint16_t* k, int64_t N, int H, int topk,
                          const int32_t* offsets, int single, const int2* tiles,
-                         int64_t ntiles, int32_t* idx, float* score, hipStream_t s) {
-  hipLaunchKernelGGL((score_topk_kernel<D, KP>), dim3((unsigned)(ntiles * H)),
-                     dim3(SCAN_WAVES * 64), 0, s, q, k, N, H, topk, offsets, single, tiles,
-                     idx, score);
+                         int64_t ntiles, float* thr, int32_t* idx, float* score, hipStream_t s) {
+  const dim3 grid((unsigned)(ntiles * H)), block(SCAN_WAVES * 64);
+  hipLaunchKernelGGL((score_topk_kernel<D, KP, true>), grid, block, 0, s, q, k, N, H, topk,
+                     offsets, single, tiles, thr, idx, score);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((score_topk_kernel<D, KP, false>), grid, block, 0, s, q, k, N, H, topk,
+                     offsets, single, tiles, thr, idx, score);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_scan_d(int kp, const uint16_t* q, const uint16_t* k, int64_t N, int H,
                          int topk, const int32_t* offsets, int single, const int2* tiles,
-                         int64_t ntiles, int32_t* idx, float* score, hipStream_t s) {
+                         int64_t ntiles, float* thr, int32_t* idx, float* score, hipStream_t s) {
   switch (kp) {
-    case 5: return launch_scan_t<D, 5>(q, k, N, H, topk, offsets, single, tiles, ntiles, idx, score, s);
-    case 8: return launch_scan_t<D, 8>(q, k, N, H, topk, offsets, single, tiles, ntiles, idx, score, s);
-    case 15: return launch_scan_t<D, 15>(q, k, N, H, topk, offsets, single, tiles, ntiles, idx, score, s);
-    case 16: return launch_scan_t<D, 16>(q, k, N, H, topk, offsets, single, tiles, ntiles, idx, score, s);
-    case 32: return launch_scan_t<D, 32>(q, k, N, H, topk, offsets, single, tiles, ntiles, idx, score, s);
-    case 45: return launch_scan_t<D, 45>(q, k, N, H, topk, offsets, single, tiles, ntiles, idx, score, s);
-    case 48: return launch_scan_t<D, 48>(q, k, N, H, topk, offsets, single, tiles, ntiles, idx, score, s);
-    case 64: return launch_scan_t<D, 64>(q, k, N, H, topk, offsets, single, tiles, ntiles, idx, score, s);
+    case 5: return launch_scan_t<D, 5>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
+    case 8: return launch_scan_t<D, 8>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
+    case 15: return launch_scan_t<D, 15>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
+    case 16: return launch_scan_t<D, 16>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
+    case 32: return launch_scan_t<D, 32>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
+    case 45: return launch_scan_t<D, 45>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
+    case 48: return launch_scan_t<D, 48>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
+    case 64: return launch_scan_t<D, 64>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -354,17 +440,17 @@ hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_
 
 hipError_t launch_score_topk(const uint16_t* q, const uint16_t* k, int64_t N, int H, int d,
                              int topk, const int32_t* offsets, int num_graphs,
-                             const int2* tiles, int64_t max_tiles, int32_t* topk_idx,
-                             float* topk_score, hipStream_t s) {
+                             const int2* tiles, int64_t max_tiles, float* thr,
+                             int32_t* topk_idx, float* topk_score, hipStream_t s) {
   const int kp = scan_list_len(topk);
   const int single = (offsets == nullptr || num_graphs <= 1) ? 1 : 0;
   const int64_t ntiles = single ? ceil_div(N, SCAN_QT) : max_tiles;
   if (d == 32)
-    return launch_scan_d<32>(kp, q, k, N, H, topk, offsets, single, tiles, ntiles, topk_idx,
-                             topk_score, s);
+    return launch_scan_d<32>(kp, q, k, N, H, topk, offsets, single, tiles, ntiles, thr,
+                             topk_idx, topk_score, s);
   if (d == 64)
-    return launch_scan_d<64>(kp, q, k, N, H, topk, offsets, single, tiles, ntiles, topk_idx,
-                             topk_score, s);
+    return launch_scan_d<64>(kp, q, k, N, H, topk, offsets, single, tiles, ntiles, thr,
+                             topk_idx, topk_score, s);
   return hipErrorInvalidValue;
 }
 

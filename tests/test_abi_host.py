@@ -56,6 +56,8 @@ def _bwd(N=128, H=2, d=32, topk=15, ws=FAKE, ws_bytes=1 << 40, dq=FAKE, offs=Non
     (dict(topk=65), UNSUPPORTED), (dict(N=1 << 30, H=4), UNSUPPORTED),
     (dict(B=4, offs=FAKE, ws=None, ws_bytes=0), WORKSPACE),
     (dict(B=4, offs=FAKE, ws=FAKE, ws_bytes=16), WORKSPACE),
+    (dict(ws=None, ws_bytes=0), WORKSPACE),
+    (dict(ws=FAKE, ws_bytes=1024), WORKSPACE),
 ])
 def test_forward_rejects(kw, status):
     assert _fwd(**kw) == status
@@ -73,8 +75,8 @@ def test_backward_rejects(kw, status):
 def test_workspace_sizes_are_linear_in_n():
     f = kmip.forward_workspace_bytes
     b = kmip.backward_workspace_bytes
-    assert f(100000, 4, 32, 15, 0) == 0                     # one graph: no scratch
-    assert f(100000, 4, 32, 15, 64) > 0
+    assert f(100000, 4, 32, 15, 0) == 100000 * 4 * 4         # one fp32 threshold per row
+    assert f(100000, 4, 32, 15, 64) > f(100000, 4, 32, 15, 0)  # plus the tile plan
     b1, b2 = b(100000, 4, 32, 15), b(200000, 4, 32, 15)
     assert 1.9 < b2 / b1 < 2.1                              # O(N * H * k)
     assert b(500000, 4, 32, 15) < 1.5e9

@@ -15,10 +15,10 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------- tiling
 // Score scan: a workgroup of SCAN_WAVES wavefronts, each owning 32 query rows
 // of one head (one 32x32 MFMA output block: keys x queries).
-constexpr int SCAN_WAVES = 4;
+constexpr int SCAN_WAVES = 16;
 constexpr int SCAN_QPW = 32;
 constexpr int SCAN_QT = SCAN_WAVES * SCAN_QPW;   // queries per workgroup tile
-constexpr int SCAN_CAP = 16;                      // per-lane candidate buffer entries
+constexpr int SCAN_CAP = 8;                       // per-lane candidate buffer entries
 constexpr int SCAN_CHUNKS = 32;                   // threshold pass: chunks per lane
 
 // Key-side backward: consecutive sorted (key, pair) positions per slice.

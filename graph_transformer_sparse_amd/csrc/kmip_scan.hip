@@ -1,4 +1,4 @@
-// Score scan with a fused running top-k (the O(N^2) part of k-MIP attention)
+// Score scan with the top-k selection (the O(N^2) part of k-MIP attention)
 // and the ragged tile plan.
 //
 // Page "k-Maximum Inner Product Attention for Graph Transformers and the
@@ -7,42 +7,66 @@
 // are never stored as an N x N matrix.
 //
 // Design (gfx950):
-//  * A workgroup owns 128 query rows of one head and one graph (4 wavefronts
-//    x 32 queries).  Each wavefront keeps its Q block in VGPRs as the MFMA B
-//    operand for the whole scan.
-//  * The graph's keys stream through LDS in chunks (coalesced 16-byte global
-//    loads, double buffered, rows padded by 16 bytes so the MFMA A-operand
-//    reads are free of bank conflicts).
-//  * v_mfma_f32_32x32x16_bf16 computes a 32 keys x 32 queries score block
-//    (fp32 accumulation of exact bf16 products).  Lane l holds query l%32 and
-//    16 of the 32 keys, so every lane sees a private half of each query's key
-//    stream, in ascending key order.
-//  * Per lane: a sorted top-k list in registers and a threshold (the list's
-//    k-th score).  A block is rejected with a max tree and one compare.  Hits
-//    are appended to a per-lane LDS candidate buffer; when any lane's buffer
-//    is nearly full the whole wavefront drains in lockstep, inserting
-//    candidates into its register list, so the costly insertions run with
-//    most lanes active.
-//  * At the end the two half-lists of a query (lanes l and l^32) are merged
-//    by rank counting with the tie rule (score descending, id ascending) and
-//    written as the final topk_idx / topk_score rows.
+//  * Work is split into sub-tiles of up to 256 query rows of one head and one
+//    graph: 4 wavefronts x 2 query blocks of 32.  Each wavefront keeps the Q
+//    rows of its blocks in VGPRs as MFMA B operands for the whole scan.
+//  * The graph's keys stream through a 3-deep LDS ring in 8 KB chunks (128
+//    keys at d = 32, 64 at d = 64), fetched with direct global->LDS loads
+//    issued two chunks ahead.  Each key row is stored with its 16-byte pieces
+//    XOR-permuted by a function of the row, which keeps the MFMA A-operand
+//    reads free of bank conflicts.
+//  * v_mfma_f32_32x32x16_bf16 scores 32 keys x 32 queries (fp32 accumulation
+//    of exact bf16 products); one A operand serves both query blocks of the
+//    wavefront.  Lane l holds query l%32 and 16 of the 32 keys, so each lane
+//    sees a private half of every query's key stream, in ascending key order.
+//  * Two passes.  The threshold pass keeps, per lane and query, the top-k of
+//    the maxima of SCAN_CHUNKS consecutive key chunks (uniform, lockstep
+//    insertions); chunk maxima are scores of distinct keys, so the k-th
+//    largest over both halves is a lower bound T of the query's k-th score.
+//    The selection pass then runs the exact running top-k seeded with
+//    next_down(T): a block of scores is rejected with a max tree and one
+//    compare, rare hits go to a per-lane LDS candidate buffer, and buffers
+//    are drained in lockstep into per-lane register lists.  At the end the
+//    two half-lists of a query (lanes l, l^32) are merged by rank with the
+//    tie rule (score descending, id ascending).
+//  * One graph: a persistent grid of exactly the co-resident workgroups, each
+//    taking an equal contiguous range of query blocks (no partial last round),
+//    with logical ids permuted so that the workgroups of one XCD share a head
+//    and its keys in that XCD's L2.  Batched graphs: one workgroup per planned
+//    sub-tile.
 #include "kmip_internal.h"
 
 namespace kmip {
 namespace {
 
 constexpr float kInf = __builtin_inff();
+constexpr int QB = 1;                       // query blocks of 32 per wavefront
+constexpr int SUB_ROWS = SCAN_WAVES * QB * 32;
+constexpr int NBUF = 3;                     // LDS ring depth
+static_assert(SUB_ROWS == SCAN_QT, "sub-tile rows");
+// Sub-blocks per batch (LDS reads, then MFMAs, then scores) for each pass.
+#ifndef KMIP_SCAN_BATCH
+#define KMIP_SCAN_BATCH 2
+#endif
+template <bool PRE> struct PassCfg { static constexpr int BATCH = KMIP_SCAN_BATCH; };
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <int D>
 struct ScanShape {
   static constexpr int NM = D / 16;                 // K=16 MFMAs per 32x32 block
-  static constexpr int ROWB = 2 * D + 16;           // padded LDS bytes per key row
-  static constexpr int TK = (D == 32) ? 128 : 64;   // keys per LDS chunk
-  static constexpr int SUBT = TK / 32;              // 32-key sub-blocks per chunk
-  static constexpr int CHUNK_BYTES = TK * ROWB;
-  static constexpr int PPR = (2 * D) / 16;          // 16-byte pieces per key row
-  static constexpr int PPT = TK * PPR / (SCAN_WAVES * 64);  // pieces per thread
-  static_assert(TK * PPR % (SCAN_WAVES * 64) == 0, "chunk must split evenly");
+  static constexpr int ROWB = 2 * D;                // bytes per key row in LDS
+  static constexpr int PPR = ROWB / 16;             // 16-byte pieces per row
+  static constexpr int CHUNK_BYTES = 1024 * SCAN_WAVES;   // one 1 KB load per wave
+  static constexpr int TK = CHUNK_BYTES / ROWB;      // keys per chunk
+  static constexpr int SUBT = TK / 32;               // 32-key sub-blocks per chunk
+  static constexpr int LPW = 1;
+  // Piece permutation of row r (conflict-free A-operand reads for 32- and
+  // 64-bank LDS models).
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 32) return ((r >> 1) ^ (r >> 3)) & 3;
+    else return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2);
+  }
 };
 
 // Insert (s, j) into a descending list.  The caller guarantees s beats the
@@ -62,6 +86,16 @@ __device__ __forceinline__ void list_insert(float (&ls)[KP], int (&lj)[KP], floa
   lj[0] = b[0] ? j : lj[0];
 }
 
+template <int KP>
+__device__ __forceinline__ void value_insert(float (&ls)[KP], float s) {
+  bool b[KP];
+#pragma unroll
+  for (int t = 0; t < KP; ++t) b[t] = s > ls[t];
+#pragma unroll
+  for (int t = KP - 1; t >= 1; --t) ls[t] = b[t - 1] ? ls[t - 1] : (b[t] ? s : ls[t]);
+  ls[0] = b[0] ? s : ls[0];
+}
+
 // Largest float below x (x finite or -inf; -inf stays -inf).
 __device__ __forceinline__ float next_down(float x) {
   if (x == -kInf) return x;
@@ -70,271 +104,358 @@ __device__ __forceinline__ float next_down(float x) {
   return __uint_as_float(x > 0.f ? u - 1u : u + 1u);
 }
 
-// One kernel, two passes (PRE selects the pass).
-//
-// Pass 1 (PRE): the same MFMA scan, keeping only the running maximum of each
-// of SCAN_CHUNKS consecutive chunks of every lane's key stream.  Chunk maxima
-// are scores of distinct keys, so the k-th largest of a query's 2*SCAN_CHUNKS
-// chunk maxima is a lower bound T on its k-th largest score; it is written to
-// thr_buf.  A key with score < T cannot be selected.
-//
-// Pass 2 (!PRE): the exact running top-k, seeded with the threshold
-// next_down(T) (a key scoring exactly T may still win on id), so that only a
-// handful of keys per query ever reach the insertion path.
+struct SubTile {
+  int h;
+  int64_t q0, q1;     // query rows [q0, q1)
+  int64_t kb, ke;     // key range of the graph
+};
+
 template <int D, int KP, bool PRE>
-__global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int64_t N, int H,
-    int topk, const int32_t* __restrict__ offsets, int single_graph,
-    const int2* __restrict__ tiles, float* __restrict__ thr_buf,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+struct Scanner {
   using S = ScanShape<D>;
-  static_assert(SCAN_CAP * 8 == SCAN_CHUNKS * 4, "candidate and chunk areas share LDS");
-  __shared__ __attribute__((aligned(16))) unsigned char kbuf[2 * S::CHUNK_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char wbuf[SCAN_WAVES * SCAN_CAP * 64 * 8];
+  unsigned char* kbuf;        // NBUF chunks
+  uint2* cbuf;                // per-lane candidate buffers (selection pass)
+  const uint16_t* Q;
+  const uint16_t* K;
+  int H, topk;
+  float* thr_buf;
+  int32_t* out_idx;
+  float* out_score;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int64_t lin = blockIdx.x;
-  const int h = (int)(lin % H);
-  const int64_t tile = lin / H;
-
-  int64_t q0, kb, ke;
-  if (single_graph) {
-    q0 = tile * SCAN_QT;
-    kb = 0;
-    ke = N;
-  } else {
-    const int2 t = tiles[tile];
-    if (t.x < 0) return;                 // beyond the planned tiles
-    q0 = t.y;
-    kb = offsets[t.x];
-    ke = offsets[t.x + 1];
-  }
-  if (q0 >= ke) return;
-  const int64_t q1 = (q0 + SCAN_QT < ke) ? q0 + SCAN_QT : ke;
-
-  const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
-  const int64_t qrow = q0 + wave * SCAN_QPW + lrow;
-  const bool qvalid = qrow < q1;
-  const bool wave_active = (q0 + wave * SCAN_QPW) < q1;
-  const int64_t orow = qrow * H + h;
-
-  // MFMA B operand: Q[query][16m + 8*lhalf .. +7] for query = lane%32.
-  bf16x8_t qb[S::NM];
-  {
-    const int64_t ql = qvalid ? qrow : (q1 - 1);
-    const uint16_t* qp = Q + (ql * H + h) * D + 8 * lhalf;
+  __device__ __forceinline__ void issue(const SubTile& t, int c, int wave, int lane) {
+    unsigned char* dst = kbuf + (c % NBUF) * S::CHUNK_BYTES;
+    const uint16_t* kh = K + (int64_t)t.h * D;
+    const int64_t kst = (int64_t)H * D;
 #pragma unroll
-    for (int m = 0; m < S::NM; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
+    for (int i = 0; i < S::LPW; ++i) {
+      const int P = (wave * S::LPW + i) * 64 + lane;       // 16-byte slot in the chunk
+      const int row = P / S::PPR;
+      const int part = (P % S::PPR) ^ S::swz(row);
+      int64_t key = t.kb + (int64_t)c * S::TK + row;
+      key = key < t.ke ? key : t.ke - 1;
+      __builtin_amdgcn_global_load_lds(kh + key * kst + part * 8,
+                                       LDS_PTR(dst + (wave * S::LPW + i) * 1024), 16, 0, 0);
+    }
   }
 
-  // Slots [0, KP-topk) hold +inf sentinels that nothing displaces, so the
-  // live top-k always occupies the tail and its k-th score is ls[KP-1].
-  const int nsent = KP - topk;
-  float ls[KP];
-  int lj[KP];
+  static __device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xffffffff));
+    const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+  }
+
+  __device__ __forceinline__ void run(const SubTile& tin) {
+    // The sub-tile is the same for the whole workgroup: keep it in SGPRs.
+    const SubTile t{__builtin_amdgcn_readfirstlane(tin.h), uniform64(tin.q0), uniform64(tin.q1),
+                    uniform64(tin.kb), uniform64(tin.ke)};
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int64_t nkeys = t.ke - t.kb;
+    const int nchunks = (int)((nkeys + S::TK - 1) / S::TK);
+
+    // The ring may still be read by slower waves of the previous sub-tile.
+    __syncthreads();
 #pragma unroll
-  for (int t = 0; t < KP; ++t) {
-    ls[t] = t < nsent ? kInf : -kInf;
-    lj[t] = -1;
-  }
+    for (int c = 0; c < NBUF - 1; ++c)
+      if (c < nchunks) issue(t, c, wave, lane);
 
-  // Pass 1 state: running chunk maximum; chunk i of this lane at cml[i*64].
-  const int64_t nkeys = ke - kb;
-  const int nsub = (int)((nkeys + 31) / 32);
-  const int spc = (nsub + SCAN_CHUNKS - 1) / SCAN_CHUNKS;   // sub-blocks per chunk
-  float* cml = reinterpret_cast<float*>(wbuf) + wave * SCAN_CHUNKS * 64 + lane;
-  float cm = -kInf;
-  // Pass 2 state: reject threshold and the lane's candidate buffer.
-  float thr = kInf;
-  int cnt = 0;
-  uint2* cb = reinterpret_cast<uint2*>(wbuf) + wave * SCAN_CAP * 64 + lane;
-  if constexpr (PRE) {
-#pragma unroll 1
-    for (int i = 0; i < SCAN_CHUNKS; ++i) cml[i * 64] = -kInf;
-  } else {
-    if (qvalid) thr = next_down(thr_buf[orow]);
-  }
-  // Retire the operand loads here so that the loop's MFMAs never wait on the
-  // vector-memory counter, which the K prefetch keeps busy.
-  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    int64_t qrow[QB];
+    bool qvalid[QB], bact[QB];
+    bf16x8_t qb[QB][S::NM];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int64_t first = t.q0 + (wave * QB + b) * 32;
+      qrow[b] = first + lrow;
+      bact[b] = first < t.q1;
+      qvalid[b] = qrow[b] < t.q1;
+      const int64_t ql = qvalid[b] ? qrow[b] : t.q1 - 1;
+      const uint16_t* qp = Q + (ql * H + t.h) * D + 8 * lhalf;
+#pragma unroll
+      for (int m = 0; m < S::NM; ++m) qb[b][m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
+    }
+    const bool wave_active = bact[0];
+    int aoff[S::NM];
+#pragma unroll
+    for (int m = 0; m < S::NM; ++m)
+      aoff[m] = lrow * S::ROWB + ((2 * m + lhalf) ^ S::swz(lrow)) * 16;
 
-  auto drain = [&]() __attribute__((always_inline)) {
-    for (int c = 0; __ballot(c < cnt) != 0ull; ++c) {
-      if (c < cnt) {
-        const uint2 e = cb[c * 64];
-        const float sv = __uint_as_float(e.x);
-        if (sv > thr) {
-          list_insert<KP>(ls, lj, sv, (int)e.y);
-          thr = fmaxf(thr, ls[KP - 1]);
-        }
+    // Lists: slots [0, KP-topk) hold +inf sentinels that nothing displaces, so
+    // the live top-k occupies the tail and its k-th score is ls[.][KP-1].
+    const int nsent = KP - topk;
+    float ls[QB][KP];
+    int lj[QB][KP];
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        ls[b][i] = i < nsent ? kInf : -kInf;
+        lj[b][i] = -1;
+      }
+    float thr[QB], cm[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      cm[b] = -kInf;
+      thr[b] = kInf;
+      if constexpr (!PRE) {
+        if (qvalid[b]) thr[b] = next_down(thr_buf[qrow[b] * H + t.h]);
       }
     }
-    cnt = 0;
-  };
+    const int nsub = (int)((nkeys + 31) / 32);
+    const int spc = (nsub + SCAN_CHUNKS - 1) / SCAN_CHUNKS;   // sub-blocks per chunk
+    int cleft = spc;                                          // sub-blocks left in chunk
+    int cnt = 0;
+    uint2* cb = cbuf + wave * SCAN_CAP * 64 + lane;           // entry c at cb[c * 64]
 
-  const int nchunks = (int)((nkeys + S::TK - 1) / S::TK);
-
-  // Each thread moves PPT 16-byte pieces of a key chunk: global -> VGPR -> LDS.
-  uint4 stg0, stg1;
-  static_assert(S::PPT == 2, "two staging pieces per thread");
-  const int prow0 = tid / S::PPR, ppart0 = tid % S::PPR;
-  const int prow1 = (tid + SCAN_WAVES * 64) / S::PPR, ppart1 = (tid + SCAN_WAVES * 64) % S::PPR;
-  const uint16_t* kh = K + (int64_t)h * D;
-  const int64_t kstride = (int64_t)H * D;
-#define KMIP_GLOAD(c)                                                              \
-  {                                                                                \
-    int64_t k0 = kb + (int64_t)(c) * S::TK + prow0;                                \
-    int64_t k1 = kb + (int64_t)(c) * S::TK + prow1;                                \
-    k0 = k0 < ke ? k0 : ke - 1;                                                    \
-    k1 = k1 < ke ? k1 : ke - 1;                                                    \
-    stg0 = *reinterpret_cast<const uint4*>(kh + k0 * kstride + ppart0 * 8);        \
-    stg1 = *reinterpret_cast<const uint4*>(kh + k1 * kstride + ppart1 * 8);        \
-  }
-#define KMIP_LSTORE(buf)                                                           \
-  {                                                                                \
-    unsigned char* kd = kbuf + (buf) * S::CHUNK_BYTES;                             \
-    *reinterpret_cast<uint4*>(kd + prow0 * S::ROWB + ppart0 * 16) = stg0;          \
-    *reinterpret_cast<uint4*>(kd + prow1 * S::ROWB + ppart1 * 16) = stg1;          \
-  }
-
-  KMIP_GLOAD(0);
-  KMIP_LSTORE(0);
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) KMIP_GLOAD(c + 1);
-    const unsigned char* kc = kbuf + (c & 1) * S::CHUNK_BYTES;
-    const int64_t cbase = kb + (int64_t)c * S::TK;
-    const bool partial = cbase + S::TK > ke;
-    if (wave_active) {
-      // Software pipeline: the MFMAs of sub-block st+1 are issued before the
-      // scores of sub-block st are examined.
-      floatx16_t acc[2];
-#define KMIP_MFMA(st, dst)                                                          \
-  {                                                                               \
-    dst = floatx16_t{};                                                           \
-    _Pragma("unroll") for (int m = 0; m < S::NM; ++m) {                           \
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(                      \
-          kc + ((st) * 32 + lrow) * S::ROWB + m * 32 + lhalf * 16);               \
-      dst = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[m], dst, 0, 0, 0);      \
-    }                                                                             \
-  }
-      KMIP_MFMA(0, acc[0]);
+    auto drain = [&]() __attribute__((always_inline)) {
+      for (int c = 0; __ballot(c < cnt) != 0ull; ++c) {
+        if (c < cnt) {
+          const uint2 e = cb[c * 64];
+          const float sv = __uint_as_float(e.x);
+          const int key = (int)(e.y & 0x7fffffffu);
+          const int tag = (int)(e.y >> 31);
 #pragma unroll
-      for (int st = 0; st < S::SUBT; ++st) {
-        if (st + 1 < S::SUBT) KMIP_MFMA(st + 1, acc[(st + 1) & 1]);
+          for (int b = 0; b < QB; ++b) {
+            if (tag == b && sv > thr[b]) {
+              list_insert<KP>(ls[b], lj[b], sv, key);
+              thr[b] = fmaxf(thr[b], ls[b][KP - 1]);
+            }
+          }
+        }
+      }
+      cnt = 0;
+    };
+
+    for (int c = 0; c < nchunks; ++c) {
+      // Chunk c's loads were followed by at most one later chunk's loads.
+      if (c + 1 < nchunks) __builtin_amdgcn_s_waitcnt(0x0f70 | S::LPW);
+      else __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+      if (c + NBUF - 1 < nchunks) issue(t, c + NBUF - 1, wave, lane);
+      if (!wave_active) continue;
+      const unsigned char* kc = kbuf + (c % NBUF) * S::CHUNK_BYTES;
+      const int64_t cbase = t.kb + (int64_t)c * S::TK;
+      const bool partial = (c + 1) * S::TK > (int)nkeys;
+
+      // Sub-blocks are processed in batches of BS: all LDS reads of the
+      // batch, then all its MFMAs (independent accumulation chains), then the
+      // scores, so a wavefront keeps several MFMAs in flight.  The swizzle of
+      // row st*32+lrow does not depend on st, so a lane reads at a fixed
+      // offset plus st * 32 rows.
+      constexpr int BS = PassCfg<PRE>::BATCH < S::SUBT ? PassCfg<PRE>::BATCH : S::SUBT;
+      static_assert(S::SUBT % BS == 0, "batches tile the chunk");
+      floatx16_t acc[BS][QB];
+      bf16x8_t areg[BS][S::NM];
+      auto aload = [&](int st, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < S::NM; ++m)
+          areg[slot][m] = *reinterpret_cast<const bf16x8_t*>(kc + st * 32 * S::ROWB + aoff[m]);
+      };
+      auto mfma = [&](int slot_a, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) acc[slot][b] = floatx16_t{};
+#pragma unroll
+        for (int m = 0; m < S::NM; ++m) {
+#pragma unroll
+          for (int b = 0; b < QB; ++b)
+            if (bact[b])
+              acc[slot][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  areg[slot_a][m], qb[b][m], acc[slot][b], 0, 0, 0);
+        }
+      };
+      auto examine = [&](int st, int slot) __attribute__((always_inline)) {
         // acc[r] = <k_key, q_query>, key = key0 + 8*(r/4) + (r%4), query = lane%32.
         const int key0 = (int)(cbase + st * 32 + 4 * lhalf);
-        float s[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = acc[st & 1][r];
+        floatx16_t(&s)[QB] = acc[slot];
         if (partial) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key0 + 8 * (r >> 2) + (r & 3) >= ke) s[r] = -kInf;
+          for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (key0 + 8 * (r >> 2) + (r & 3) >= t.ke) s[b][r] = -kInf;
         }
         if constexpr (PRE) {
-          cm = fmaxf(fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                           fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))),
-                     fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
-                           fmaxf(fmaxf(s[12], s[13]), fmaxf(fmaxf(s[14], s[15]), cm))));
-          const int t = c * S::SUBT + st;              // sub-block index, uniform
-          if ((t + 1) % spc == 0 || t + 1 == nsub) {
-            if (t < nsub) cml[(t / spc) * 64] = cm;
-            cm = -kInf;
+#pragma unroll
+          for (int b = 0; b < QB; ++b)
+            cm[b] = fmaxf(fmaxf(fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])),
+                                fmaxf(fmaxf(s[b][4], s[b][5]), fmaxf(s[b][6], s[b][7]))),
+                          fmaxf(fmaxf(fmaxf(s[b][8], s[b][9]), fmaxf(s[b][10], s[b][11])),
+                                fmaxf(fmaxf(s[b][12], s[b][13]),
+                                      fmaxf(fmaxf(s[b][14], s[b][15]), cm[b]))));
+          const int ti = c * S::SUBT + st;            // sub-block index, uniform
+          if (--cleft == 0 || ti + 1 == nsub) {
+            cleft = spc;
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+              if (cm[b] > ls[b][KP - 1]) value_insert<KP>(ls[b], cm[b]);
+              cm[b] = -kInf;
+            }
           }
         } else {
-          float g[4];
+          float g[QB][4], mx[QB];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-            g[qq] = fmaxf(fmaxf(s[4 * qq], s[4 * qq + 1]), fmaxf(s[4 * qq + 2], s[4 * qq + 3]));
-          const float mx = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
-          if (__ballot(mx > thr) != 0ull) {
-            // At most 4 appends per passing quarter: make room first, so the
-            // sub-block has a single drain site.
-            int room = cnt;
+          for (int b = 0; b < QB; ++b) {
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) room += g[qq] > thr ? 4 : 0;
-            if (__ballot(room > SCAN_CAP) != 0ull) drain();
+            for (int qq = 0; qq < 4; ++qq)
+              g[b][qq] = fmaxf(fmaxf(s[b][4 * qq], s[b][4 * qq + 1]),
+                               fmaxf(s[b][4 * qq + 2], s[b][4 * qq + 3]));
+            mx[b] = fmaxf(fmaxf(g[b][0], g[b][1]), fmaxf(g[b][2], g[b][3]));
+          }
+          bool hit = false;
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              if (__ballot(g[qq] > thr) != 0ull) {
+          for (int b = 0; b < QB; ++b) hit = hit || (mx[b] > thr[b]);
+          if (__ballot(hit) != 0ull) {
+            // Appends go in halves of two quarters (at most 8 = SCAN_CAP per
+            // lane): make room first, so each half has a single drain site
+            // and the buffer index stays below SCAN_CAP.
+            static_assert(SCAN_CAP >= 8, "a half sub-block appends up to 8 scores");
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  const float sv = s[4 * qq + r];
-                  if (sv > thr) {
-                    cb[cnt * 64] = make_uint2(__float_as_uint(sv), (unsigned)(key0 + 8 * qq + r));
-                    ++cnt;
+            for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              int room = cnt;
+#pragma unroll
+              for (int qq = 2 * hf; qq < 2 * hf + 2; ++qq) room += g[b][qq] > thr[b] ? 4 : 0;
+              if (__ballot(room > SCAN_CAP) != 0ull) drain();
+#pragma unroll
+              for (int qq = 2 * hf; qq < 2 * hf + 2; ++qq) {
+                if (__ballot(g[b][qq] > thr[b]) != 0ull) {
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) {
+                    const float sv = s[b][4 * qq + r];
+                    if (sv > thr[b]) {
+                      cb[cnt * 64] = make_uint2(__float_as_uint(sv),
+                                                (unsigned)(key0 + 8 * qq + r) |
+                                                    ((unsigned)b << 31));
+                      ++cnt;
+                    }
                   }
                 }
               }
             }
           }
         }
+      };
+#pragma unroll
+      for (int st0 = 0; st0 < S::SUBT; st0 += BS) {
+#pragma unroll
+        for (int i = 0; i < BS; ++i) aload(st0 + i, i);
+#pragma unroll
+        for (int i = 0; i < BS; ++i) mfma(i, i);
+#pragma unroll
+        for (int i = 0; i < BS; ++i) examine(st0 + i, i);
       }
-#undef KMIP_MFMA
     }
-    if (c + 1 < nchunks) KMIP_LSTORE((c + 1) & 1);
-    __syncthreads();
+    if (!wave_active) return;
+
+    if constexpr (PRE) {
+      // k-th largest chunk maximum over both halves of each query.
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        float ps[KP];
+#pragma unroll
+        for (int i = 0; i < KP; ++i) ps[i] = __shfl_xor(ls[b][i], 32);
+#pragma unroll
+        for (int i = 0; i < KP; ++i)
+          if (i >= nsent && ps[i] > ls[b][KP - 1]) value_insert<KP>(ls[b], ps[i]);
+        if (qvalid[b] && lhalf == 0) thr_buf[qrow[b] * H + t.h] = ls[b][KP - 1];
+      }
+    } else {
+      drain();
+      // Merge the two half-lists of each query by rank: live entry i of my
+      // list (slots [nsent, KP)) lands at (i - nsent) + the number of partner
+      // live entries ordered before it.  Lower-half lanes win exact (score,
+      // id) ties, which only padding entries (-inf, -1) can produce.
+      const bool lower = lhalf == 0;
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        float ps[KP];
+        int pj[KP];
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+          ps[i] = __shfl_xor(ls[b][i], 32);
+          pj[i] = __shfl_xor(lj[b][i], 32);
+        }
+        if (qvalid[b]) {
+          int32_t* oi = out_idx + (qrow[b] * H + t.h) * topk;
+          float* os = out_score + (qrow[b] * H + t.h) * topk;
+#pragma unroll
+          for (int i = 0; i < KP; ++i) {
+            if (i >= nsent) {
+              int rank = i - nsent;
+#pragma unroll
+              for (int u = 0; u < KP; ++u) {
+                const bool before =
+                    u >= nsent && (ps[u] > ls[b][i] ||
+                                   (ps[u] == ls[b][i] && (lower ? pj[u] < lj[b][i]
+                                                                : pj[u] <= lj[b][i])));
+                rank += before ? 1 : 0;
+              }
+              if (rank < topk) {
+                oi[rank] = lj[b][i];
+                os[rank] = lj[b][i] < 0 ? -kInf : ls[b][i];
+              }
+            }
+          }
+        }
+      }
+    }
   }
-#undef KMIP_GLOAD
-#undef KMIP_LSTORE
-  if (!wave_active) return;
+};
 
-  if constexpr (PRE) {
-    // k-th largest of the query's chunk maxima: this lane's and its partner's
-    // (lane ^ 32 scans the other half of the same query's keys).
-    __builtin_amdgcn_wave_barrier();
-    const float* cmp = reinterpret_cast<const float*>(wbuf) + wave * SCAN_CHUNKS * 64 + (lane ^ 32);
-    float t = -kInf;
-#pragma unroll 1
-    for (int i = 0; i < 2 * SCAN_CHUNKS; ++i) {
-      const float v = (i & 1) ? cmp[(i >> 1) * 64] : cml[(i >> 1) * 64];
-      if (v > t) {
-        list_insert<KP>(ls, lj, v, 0);
-        t = ls[KP - 1];
-      }
-    }
-    if (qvalid && lhalf == 0) thr_buf[orow] = t;
-    return;
+// Persistent grid for one graph: nwg workgroups split the H * nbph query
+// blocks (32 rows each) into equal contiguous ranges.  Batched graphs: one
+// workgroup per (planned tile, head).
+template <int D, int KP, bool PRE>
+__global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int64_t N, int H,
+    int topk, const int32_t* __restrict__ offsets, const int2* __restrict__ tiles, int nwg,
+    float* __restrict__ thr_buf, int32_t* __restrict__ out_idx,
+    float* __restrict__ out_score) {
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[NBUF * 1024 * SCAN_WAVES];
+  __shared__ __attribute__((aligned(16))) uint2 cbuf[PRE ? 1 : SCAN_WAVES * SCAN_CAP * 64];
+  Scanner<D, KP, PRE> sc{kbuf, cbuf, Q, K, H, topk, thr_buf, out_idx, out_score};
+  // Query blocks [b, be) of the flattened (head, 32-row block) space for one
+  // graph; a single planned sub-tile for batched graphs.
+  const int64_t nbph = (N + 31) / 32;
+  int64_t b = 0, be = 0;
+  int rh = 0;
+  int64_t rq0 = 0, rq1 = 0, rkb = 0, rke = 0;
+  if (tiles == nullptr) {
+    // Logical id: the 8 XCDs receive workgroups round-robin; give each XCD a
+    // contiguous range so its workgroups share a head (and its keys in L2).
+    const int per = nwg / 8;
+    const int L = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    const int64_t total = nbph * H;
+    b = total * L / nwg;
+    be = total * (L + 1) / nwg;
   } else {
-    drain();
-
-    // Merge the two half-lists of each query by rank: live entry t of my list
-    // (slots [nsent, KP)) lands at (t - nsent) + the number of partner live
-    // entries ordered before it.  Lower-half lanes win exact (score, id)
-    // ties, which only padding entries (-inf, -1) can produce.
-    float ps[KP];
-    int pj[KP];
-#pragma unroll
-    for (int t = 0; t < KP; ++t) {
-      ps[t] = __shfl_xor(ls[t], 32);
-      pj[t] = __shfl_xor(lj[t], 32);
+    const int2 tl = tiles[blockIdx.x / H];
+    if (tl.x < 0) return;                 // beyond the planned tiles
+    rh = (int)(blockIdx.x % H);
+    rkb = offsets[tl.x];
+    rke = offsets[tl.x + 1];
+    if (tl.y >= rke) return;
+    rq0 = tl.y;
+    rq1 = tl.y + SUB_ROWS < rke ? tl.y + SUB_ROWS : rke;
+    be = 1;
+  }
+  while (b < be) {
+    SubTile st;
+    if (tiles == nullptr) {
+      // Spread the remaining blocks evenly over the sub-tiles still needed.
+      const int h = (int)(b / nbph);
+      const int64_t nb0 = b % nbph;
+      const int64_t rem = be - b;
+      const int64_t nst = (rem + SCAN_WAVES * QB - 1) / (SCAN_WAVES * QB);
+      int64_t n = (rem + nst - 1) / nst;
+      n = n < nbph - nb0 ? n : nbph - nb0;
+      st = SubTile{h, nb0 * 32, (nb0 + n) * 32 < N ? (nb0 + n) * 32 : N, 0, N};
+      b += n;
+    } else {
+      st = SubTile{rh, rq0, rq1, rkb, rke};
+      b = be;
     }
-    if (!qvalid) return;
-    const bool lower = lhalf == 0;
-    int32_t* oi = out_idx + orow * topk;
-    float* os = out_score + orow * topk;
-#pragma unroll
-    for (int t = 0; t < KP; ++t) {
-      if (t >= nsent) {
-        int rank = t - nsent;
-#pragma unroll
-        for (int u = 0; u < KP; ++u) {
-          const bool before = u >= nsent &&
-                              (ps[u] > ls[t] ||
-                               (ps[u] == ls[t] && (lower ? pj[u] < lj[t] : pj[u] <= lj[t])));
-          rank += before ? 1 : 0;
-        }
-        if (rank < topk) {
-          oi[rank] = lj[t];
-          os[rank] = lj[t] < 0 ? -kInf : ls[t];
-        }
-      }
-    }
+    sc.run(st);
   }
 }
 
@@ -386,35 +507,71 @@ __global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B,
   tiles[t] = make_int2(lo, offsets[lo] + (int)(t - tile_start[lo]) * SCAN_QT);
 }
 
+// Co-resident workgroups of a kernel on this device (one graph: the
+// persistent grid size, a multiple of 8 so each XCD gets an equal share).
+template <typename Kern>
+int resident_workgroups(Kern kern) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                   SCAN_WAVES * 64, 0) != hipSuccess)
+    return 0;
+  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  return n >= 8 ? n - n % 8 : 8;
+}
+
+template <int D, int KP, bool PRE>
+hipError_t launch_pass(const uint16_t* q, const uint16_t* k, int64_t N, int H, int topk,
+                       const int32_t* offsets, const int2* tiles, int64_t max_tiles,
+                       float* thr, int32_t* idx, float* score, hipStream_t s) {
+  auto kern = score_topk_kernel<D, KP, PRE>;
+  int nwg = 0;
+  dim3 grid;
+  if (tiles == nullptr) {
+    nwg = resident_workgroups(kern);
+    if (nwg <= 0) return hipErrorInvalidDevice;
+    grid = dim3((unsigned)nwg);
+  } else {
+    grid = dim3((unsigned)(max_tiles * H));
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(SCAN_WAVES * 64), 0, s, q, k, N, H, topk, offsets, tiles,
+                     nwg, thr, idx, score);
+  return hipGetLastError();
+}
+
 template <int D, int KP>
 hipError_t launch_scan_t(const uint16_t* q, const uint16_t* k, int64_t N, int H, int topk,
-                         const int32_t* offsets, int single, const int2* tiles,
-                         int64_t ntiles, float* thr, int32_t* idx, float* score, hipStream_t s) {
-  const dim3 grid((unsigned)(ntiles * H)), block(SCAN_WAVES * 64);
-  hipLaunchKernelGGL((score_topk_kernel<D, KP, true>), grid, block, 0, s, q, k, N, H, topk,
-                     offsets, single, tiles, thr, idx, score);
-  hipError_t e = hipGetLastError();
+                         const int32_t* offsets, const int2* tiles, int64_t max_tiles,
+                         float* thr, int32_t* idx, float* score, hipStream_t s) {
+  hipError_t e = launch_pass<D, KP, true>(q, k, N, H, topk, offsets, tiles, max_tiles, thr,
+                                          idx, score, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((score_topk_kernel<D, KP, false>), grid, block, 0, s, q, k, N, H, topk,
-                     offsets, single, tiles, thr, idx, score);
-  return hipGetLastError();
+  return launch_pass<D, KP, false>(q, k, N, H, topk, offsets, tiles, max_tiles, thr, idx,
+                                   score, s);
 }
 
 template <int D>
 hipError_t launch_scan_d(int kp, const uint16_t* q, const uint16_t* k, int64_t N, int H,
-                         int topk, const int32_t* offsets, int single, const int2* tiles,
-                         int64_t ntiles, float* thr, int32_t* idx, float* score, hipStream_t s) {
+                         int topk, const int32_t* offsets, const int2* tiles, int64_t max_tiles,
+                         float* thr, int32_t* idx, float* score, hipStream_t s) {
+#define KMIP_CASE(L)                                                                   \
+  case L:                                                                              \
+    return launch_scan_t<D, L>(q, k, N, H, topk, offsets, tiles, max_tiles, thr, idx, \
+                               score, s);
   switch (kp) {
-    case 5: return launch_scan_t<D, 5>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
-    case 8: return launch_scan_t<D, 8>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
-    case 15: return launch_scan_t<D, 15>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
-    case 16: return launch_scan_t<D, 16>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
-    case 32: return launch_scan_t<D, 32>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
-    case 45: return launch_scan_t<D, 45>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
-    case 48: return launch_scan_t<D, 48>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
-    case 64: return launch_scan_t<D, 64>(q, k, N, H, topk, offsets, single, tiles, ntiles, thr, idx, score, s);
+    KMIP_CASE(5)
+    KMIP_CASE(8)
+    KMIP_CASE(15)
+    KMIP_CASE(16)
+    KMIP_CASE(32)
+    KMIP_CASE(45)
+    KMIP_CASE(48)
+    KMIP_CASE(64)
     default: return hipErrorInvalidValue;
   }
+#undef KMIP_CASE
 }
 
 }  // namespace
@@ -443,14 +600,14 @@ hipError_t launch_score_topk(const uint16_t* q, const uint16_t* k, int64_t N, in
                              const int2* tiles, int64_t max_tiles, float* thr,
                              int32_t* topk_idx, float* topk_score, hipStream_t s) {
   const int kp = scan_list_len(topk);
-  const int single = (offsets == nullptr || num_graphs <= 1) ? 1 : 0;
-  const int64_t ntiles = single ? ceil_div(N, SCAN_QT) : max_tiles;
+  const bool single = (offsets == nullptr || num_graphs <= 1);
+  const int2* t = single ? nullptr : tiles;
   if (d == 32)
-    return launch_scan_d<32>(kp, q, k, N, H, topk, offsets, single, tiles, ntiles, thr,
-                             topk_idx, topk_score, s);
+    return launch_scan_d<32>(kp, q, k, N, H, topk, offsets, t, max_tiles, thr, topk_idx,
+                             topk_score, s);
   if (d == 64)
-    return launch_scan_d<64>(kp, q, k, N, H, topk, offsets, single, tiles, ntiles, thr,
-                             topk_idx, topk_score, s);
+    return launch_scan_d<64>(kp, q, k, N, H, topk, offsets, t, max_tiles, thr, topk_idx,
+                             topk_score, s);
   return hipErrorInvalidValue;
 }
 

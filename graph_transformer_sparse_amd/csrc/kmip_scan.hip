@@ -7,21 +7,21 @@
 // are never stored as an N x N matrix.
 //
 // Design (gfx950):
-//  * Work is split into sub-tiles of up to 256 query rows of one head and one
-//    graph: 4 wavefronts x 2 query blocks of 32.  Each wavefront keeps the Q
-//    rows of its blocks in VGPRs as MFMA B operands for the whole scan.
-//  * The graph's keys stream through a 3-deep LDS ring in 8 KB chunks (128
-//    keys at d = 32, 64 at d = 64), fetched with direct global->LDS loads
-//    issued two chunks ahead.  Each key row is stored with its 16-byte pieces
-//    XOR-permuted by a function of the row, which keeps the MFMA A-operand
-//    reads free of bank conflicts.
+//  * Work is split into sub-tiles of up to 512 query rows of one head and one
+//    graph: a workgroup of 16 wavefronts, each owning 32 rows.  A wavefront
+//    keeps its Q rows in VGPRs as MFMA B operands for the whole scan.
+//  * The graph's keys stream through an LDS ring of two chunks (64 KB, 1024
+//    keys at d = 32, in the threshold pass; 32 KB in the selection pass, which
+//    also holds candidate buffers), fetched with direct global->LDS loads one
+//    chunk ahead.  A chunk is stored in MFMA operand order (see ScanShape), so
+//    each A operand is one contiguous, conflict-free 1 KB LDS read.
 //  * v_mfma_f32_32x32x16_bf16 scores 32 keys x 32 queries (fp32 accumulation
-//    of exact bf16 products); one A operand serves both query blocks of the
-//    wavefront.  Lane l holds query l%32 and 16 of the 32 keys, so each lane
-//    sees a private half of every query's key stream, in ascending key order.
+//    of exact bf16 products).  Lane l holds query l%32 and 16 of the 32 keys,
+//    so each lane sees a private half of every query's key stream, in
+//    ascending key order.
 //  * Two passes.  The threshold pass keeps, per lane and query, the top-k of
-//    the maxima of SCAN_CHUNKS consecutive key chunks (uniform, lockstep
-//    insertions); chunk maxima are scores of distinct keys, so the k-th
+//    the maxima of SCAN_CHUNKS consecutive key ranges (uniform, lockstep
+//    insertions); these maxima are scores of distinct keys, so the k-th
 //    largest over both halves is a lower bound T of the query's k-th score.
 //    The selection pass then runs the exact running top-k seeded with
 //    next_down(T): a block of scores is rejected with a max tree and one
@@ -33,7 +33,7 @@
 //    taking an equal contiguous range of query blocks (no partial last round),
 //    with logical ids permuted so that the workgroups of one XCD share a head
 //    and its keys in that XCD's L2.  Batched graphs: one workgroup per planned
-//    sub-tile.
+//    sub-tile; sub-blocks past a graph's last key are skipped.
 #include "kmip_internal.h"
 
 namespace kmip {
@@ -42,31 +42,42 @@ namespace {
 constexpr float kInf = __builtin_inff();
 constexpr int QB = 1;                       // query blocks of 32 per wavefront
 constexpr int SUB_ROWS = SCAN_WAVES * QB * 32;
-constexpr int NBUF = 3;                     // LDS ring depth
 static_assert(SUB_ROWS == SCAN_QT, "sub-tile rows");
-// Sub-blocks per batch (LDS reads, then MFMAs, then scores) for each pass.
+// Per pass: LDS chunk size in 16 KB units (LPW: 1 KB loads per wavefront and
+// chunk), ring depth, and sub-blocks per batch (LDS reads, then MFMAs, then
+// scores).  Large chunks amortise the workgroup barrier of every chunk; the
+// selection pass keeps room for its candidate buffers.  With a ring of two,
+// chunk c + 1 is fetched while chunk c is scored.
 #ifndef KMIP_SCAN_BATCH
 #define KMIP_SCAN_BATCH 2
 #endif
-template <bool PRE> struct PassCfg { static constexpr int BATCH = KMIP_SCAN_BATCH; };
+template <bool PRE> struct PassCfg;
+template <> struct PassCfg<true> {
+  static constexpr int LPW = 4, NBUF = 2, BATCH = KMIP_SCAN_BATCH;
+};
+template <> struct PassCfg<false> {
+  static constexpr int LPW = 2, NBUF = 2, BATCH = KMIP_SCAN_BATCH;
+};
 
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-template <int D>
+// Chunk layout in LDS ("operand order"): the chunk is a sequence of 1 KB
+// blocks, one per (32-key sub-block st, K-slice m of the MFMA), block index
+// st * NM + m.  Inside a block, lane l's 16 bytes sit at l * 16 and hold the
+// bf16 elements [16m + 8(l/32), 16m + 8(l/32) + 8) of key st*32 + l%32: the
+// A operand of v_mfma_f32_32x32x16_bf16 for that lane.  A wavefront then reads
+// each operand as one contiguous 1 KB ds_read_b128 (no bank conflicts), and
+// the direct global->LDS load that fills a block writes it in the same lane
+// order.
+template <int D, bool PRE>
 struct ScanShape {
   static constexpr int NM = D / 16;                 // K=16 MFMAs per 32x32 block
-  static constexpr int ROWB = 2 * D;                // bytes per key row in LDS
-  static constexpr int PPR = ROWB / 16;             // 16-byte pieces per row
-  static constexpr int CHUNK_BYTES = 1024 * SCAN_WAVES;   // one 1 KB load per wave
+  static constexpr int ROWB = 2 * D;                // bytes per key row
+  static constexpr int LPW = PassCfg<PRE>::LPW;     // operand blocks loaded per wave
+  static constexpr int NBUF = PassCfg<PRE>::NBUF;   // LDS ring depth
+  static constexpr int CHUNK_BYTES = 1024 * SCAN_WAVES * LPW;
   static constexpr int TK = CHUNK_BYTES / ROWB;      // keys per chunk
   static constexpr int SUBT = TK / 32;               // 32-key sub-blocks per chunk
-  static constexpr int LPW = 1;
-  // Piece permutation of row r (conflict-free A-operand reads for 32- and
-  // 64-bank LDS models).
-  static __device__ __forceinline__ int swz(int r) {
-    if constexpr (D == 32) return ((r >> 1) ^ (r >> 3)) & 3;
-    else return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2);
-  }
+  static_assert(SUBT * NM == SCAN_WAVES * LPW, "LPW operand blocks per wavefront");
+  static_assert(NBUF == 2 || NBUF == 3, "ring depth");
 };
 
 // Insert (s, j) into a descending list.  The caller guarantees s beats the
@@ -112,8 +123,9 @@ struct SubTile {
 
 template <int D, int KP, bool PRE>
 struct Scanner {
-  using S = ScanShape<D>;
-  unsigned char* kbuf;        // NBUF chunks
+  using S = ScanShape<D, PRE>;
+  unsigned char* kbuf;        // S::NBUF chunks (read side)
+  unsigned kbuf_lds;          // LDS byte address of kbuf (direct-load side)
   uint2* cbuf;                // per-lane candidate buffers (selection pass)
   const uint16_t* Q;
   const uint16_t* K;
@@ -122,19 +134,30 @@ struct Scanner {
   int32_t* out_idx;
   float* out_score;
 
+  // Direct global->LDS load of chunk c into ring slot c % NBUF: wave w fills
+  // operand blocks w + i * SCAN_WAVES (i < LPW), lane l writing 16 bytes at
+  // l * 16 of the block.  The address is a per-chunk uniform base (SGPRs)
+  // plus a 32-bit lane offset; rows past the graph's last key re-read the
+  // last key.  Written as inline assembly so that the compiler does not treat
+  // ring reads as aliasing the loads in flight: completion is tracked by the
+  // explicit vmcnt waits of the chunk loop.  The instruction writes no VGPR.
   __device__ __forceinline__ void issue(const SubTile& t, int c, int wave, int lane) {
-    unsigned char* dst = kbuf + (c % NBUF) * S::CHUNK_BYTES;
-    const uint16_t* kh = K + (int64_t)t.h * D;
-    const int64_t kst = (int64_t)H * D;
+    const int64_t first = t.kb + (int64_t)c * S::TK;
+    const int64_t left = t.ke - first;
+    const int rmax = (int)(left < S::TK ? left : S::TK) - 1;
+    const uint16_t* base = K + (first * H + t.h) * D;
 #pragma unroll
     for (int i = 0; i < S::LPW; ++i) {
-      const int P = (wave * S::LPW + i) * 64 + lane;       // 16-byte slot in the chunk
-      const int row = P / S::PPR;
-      const int part = (P % S::PPR) ^ S::swz(row);
-      int64_t key = t.kb + (int64_t)c * S::TK + row;
-      key = key < t.ke ? key : t.ke - 1;
-      __builtin_amdgcn_global_load_lds(kh + key * kst + part * 8,
-                                       LDS_PTR(dst + (wave * S::LPW + i) * 1024), 16, 0, 0);
+      const int blk = wave + i * SCAN_WAVES;
+      const int row = (blk / S::NM) * 32 + (lane & 31);
+      const int piece = 2 * (blk % S::NM) + (lane >> 5);
+      const unsigned off =
+          (unsigned)(row < rmax ? row : rmax) * (unsigned)(H * S::ROWB) + (unsigned)piece * 16u;
+      const unsigned lds =
+          kbuf_lds + (unsigned)((c % S::NBUF) * S::CHUNK_BYTES + blk * 1024);
+      asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+                   "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                   : "memory");
     }
   }
 
@@ -148,16 +171,15 @@ struct Scanner {
     // The sub-tile is the same for the whole workgroup: keep it in SGPRs.
     const SubTile t{__builtin_amdgcn_readfirstlane(tin.h), uniform64(tin.q0), uniform64(tin.q1),
                     uniform64(tin.kb), uniform64(tin.ke)};
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform: keep it (and all that derives from it) scalar.
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 31, lhalf = lane >> 5;
     const int64_t nkeys = t.ke - t.kb;
     const int nchunks = (int)((nkeys + S::TK - 1) / S::TK);
 
     // The ring may still be read by slower waves of the previous sub-tile.
     __syncthreads();
-#pragma unroll
-    for (int c = 0; c < NBUF - 1; ++c)
-      if (c < nchunks) issue(t, c, wave, lane);
 
     int64_t qrow[QB];
     bool qvalid[QB], bact[QB];
@@ -174,10 +196,7 @@ struct Scanner {
       for (int m = 0; m < S::NM; ++m) qb[b][m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
     }
     const bool wave_active = bact[0];
-    int aoff[S::NM];
-#pragma unroll
-    for (int m = 0; m < S::NM; ++m)
-      aoff[m] = lrow * S::ROWB + ((2 * m + lhalf) ^ S::swz(lrow)) * 16;
+    const int aoff = lane * 16;
 
     // Lists: slots [0, KP-topk) hold +inf sentinels that nothing displaces, so
     // the live top-k occupies the tail and its k-th score is ls[.][KP-1].
@@ -200,6 +219,13 @@ struct Scanner {
         if (qvalid[b]) thr[b] = next_down(thr_buf[qrow[b] * H + t.h]);
       }
     }
+    // Q operands and thresholds have arrived before the first key load is
+    // issued, so the chunk loop waits on key loads only.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+#pragma unroll
+    for (int c = 0; c < S::NBUF - 1; ++c)
+      if (c < nchunks) issue(t, c, wave, lane);
+
     const int nsub = (int)((nkeys + 31) / 32);
     const int spc = (nsub + SCAN_CHUNKS - 1) / SCAN_CHUNKS;   // sub-blocks per chunk
     int cleft = spc;                                          // sub-blocks left in chunk
@@ -226,21 +252,26 @@ struct Scanner {
     };
 
     for (int c = 0; c < nchunks; ++c) {
-      // Chunk c's loads were followed by at most one later chunk's loads.
-      if (c + 1 < nchunks) __builtin_amdgcn_s_waitcnt(0x0f70 | S::LPW);
-      else __builtin_amdgcn_s_waitcnt(0x0f70);
+      // Chunk c's loads (LPW instructions per wavefront) were followed by
+      // those of at most NBUF - 2 later chunks.
+      if constexpr (S::NBUF == 3) {
+        static_assert(S::LPW <= 15, "vmcnt field");
+        if (c + 1 < nchunks) __builtin_amdgcn_s_waitcnt(0x0f70 | S::LPW);
+        else __builtin_amdgcn_s_waitcnt(0x0f70);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+      }
       __syncthreads();
-      if (c + NBUF - 1 < nchunks) issue(t, c + NBUF - 1, wave, lane);
+      if (c + S::NBUF - 1 < nchunks) issue(t, c + S::NBUF - 1, wave, lane);
       if (!wave_active) continue;
-      const unsigned char* kc = kbuf + (c % NBUF) * S::CHUNK_BYTES;
-      const int64_t cbase = t.kb + (int64_t)c * S::TK;
-      const bool partial = (c + 1) * S::TK > (int)nkeys;
+      const unsigned char* kc = kbuf + (c % S::NBUF) * S::CHUNK_BYTES;
+      const int crel = c * S::TK;                 // first key of the chunk, graph-relative
+      const int nk = (int)nkeys;
+      const bool partial = crel + S::TK > nk;
 
       // Sub-blocks are processed in batches of BS: all LDS reads of the
       // batch, then all its MFMAs (independent accumulation chains), then the
-      // scores, so a wavefront keeps several MFMAs in flight.  The swizzle of
-      // row st*32+lrow does not depend on st, so a lane reads at a fixed
-      // offset plus st * 32 rows.
+      // scores, so a wavefront keeps several MFMAs in flight.
       constexpr int BS = PassCfg<PRE>::BATCH < S::SUBT ? PassCfg<PRE>::BATCH : S::SUBT;
       static_assert(S::SUBT % BS == 0, "batches tile the chunk");
       floatx16_t acc[BS][QB];
@@ -248,7 +279,8 @@ struct Scanner {
       auto aload = [&](int st, int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int m = 0; m < S::NM; ++m)
-          areg[slot][m] = *reinterpret_cast<const bf16x8_t*>(kc + st * 32 * S::ROWB + aoff[m]);
+          areg[slot][m] =
+              *reinterpret_cast<const bf16x8_t*>(kc + (st * S::NM + m) * 1024 + aoff);
       };
       auto mfma = [&](int slot_a, int slot) __attribute__((always_inline)) {
 #pragma unroll
@@ -264,14 +296,15 @@ struct Scanner {
       };
       auto examine = [&](int st, int slot) __attribute__((always_inline)) {
         // acc[r] = <k_key, q_query>, key = key0 + 8*(r/4) + (r%4), query = lane%32.
-        const int key0 = (int)(cbase + st * 32 + 4 * lhalf);
+        const int rel0 = crel + st * 32 + 4 * lhalf;
+        const int key0 = (int)t.kb + rel0;
         floatx16_t(&s)[QB] = acc[slot];
         if (partial) {
 #pragma unroll
           for (int b = 0; b < QB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (key0 + 8 * (r >> 2) + (r & 3) >= t.ke) s[b][r] = -kInf;
+              if (rel0 + 8 * (r >> 2) + (r & 3) >= nk) s[b][r] = -kInf;
         }
         if constexpr (PRE) {
 #pragma unroll
@@ -337,6 +370,7 @@ struct Scanner {
       };
 #pragma unroll
       for (int st0 = 0; st0 < S::SUBT; st0 += BS) {
+        if (crel + st0 * 32 >= nk) break;       // only padding left in a last chunk
 #pragma unroll
         for (int i = 0; i < BS; ++i) aload(st0 + i, i);
 #pragma unroll
@@ -411,9 +445,12 @@ __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
     int topk, const int32_t* __restrict__ offsets, const int2* __restrict__ tiles, int nwg,
     float* __restrict__ thr_buf, int32_t* __restrict__ out_idx,
     float* __restrict__ out_score) {
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[NBUF * 1024 * SCAN_WAVES];
+  using S = ScanShape<D, PRE>;
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[S::NBUF * S::CHUNK_BYTES];
   __shared__ __attribute__((aligned(16))) uint2 cbuf[PRE ? 1 : SCAN_WAVES * SCAN_CAP * 64];
-  Scanner<D, KP, PRE> sc{kbuf, cbuf, Q, K, H, topk, thr_buf, out_idx, out_score};
+  const unsigned kbuf_lds =
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kbuf;
+  Scanner<D, KP, PRE> sc{kbuf, kbuf_lds, cbuf, Q, K, H, topk, thr_buf, out_idx, out_score};
   // Query blocks [b, be) of the flattened (head, 32-row block) space for one
   // graph; a single planned sub-tile for batched graphs.
   const int64_t nbph = (N + 31) / 32;

@@ -18,6 +18,8 @@ kmip_status_t check_shape(int64_t N, int H, int d, int topk, int num_graphs) {
   if (N < 1 || H < 1 || num_graphs < 0) return KMIP_ERR_INVALID_VALUE;
   if (d != 32 && d != 64) return KMIP_ERR_UNSUPPORTED;
   if (topk < 1 || topk > 64) return KMIP_ERR_UNSUPPORTED;
+  // Key-row offsets inside a scan chunk are 32-bit: (row < 1024) * H * d * 2.
+  if ((int64_t)H * d > (int64_t)1 << 20) return KMIP_ERR_UNSUPPORTED;
   const int64_t NH = N * (int64_t)H;
   if (N > (int64_t)INT32_MAX || NH * topk >= (int64_t)INT32_MAX - 1 ||
       NH >= (int64_t)INT32_MAX - 2)

@@ -39,7 +39,7 @@
  *      not 16-byte aligned, workspace not aligned (16 bytes forward,
  *      256 bytes backward)                     -> KMIP_ERR_INVALID_VALUE
  *      d not in {32, 64}, topk not in [1, 64],
- *      N * H * topk >= 2^31                      -> KMIP_ERR_UNSUPPORTED
+ *      N * H * topk >= 2^31, H * d > 2^20        -> KMIP_ERR_UNSUPPORTED
  *      workspace smaller than the *_workspace_bytes figure
  *                                               -> KMIP_ERR_WORKSPACE
  *      a launch error reported by hipGetLastError -> KMIP_ERR_LAUNCH

@@ -59,6 +59,7 @@ def _bwd(N=128, H=2, d=32, topk=15, ws=FAKE, ws_bytes=1 << 40, dq=FAKE, offs=Non
     (dict(q=ctypes.c_void_p((1 << 20) + 8)), INVALID),
     (dict(d=48), UNSUPPORTED), (dict(d=128), UNSUPPORTED), (dict(topk=0), UNSUPPORTED),
     (dict(topk=65), UNSUPPORTED), (dict(N=1 << 30, H=4), UNSUPPORTED),
+    (dict(N=2, H=(1 << 15) + 1, d=32), UNSUPPORTED), (dict(N=2, H=1 << 14, d=64), WORKSPACE),
     (dict(B=4, offs=FAKE, ws=None, ws_bytes=0), WORKSPACE),
     (dict(B=4, offs=FAKE, ws=FAKE, ws_bytes=16), WORKSPACE),
     (dict(ws=None, ws_bytes=0), WORKSPACE),

@@ -7,11 +7,14 @@ setting at N = 10^5 nodes, H = 4 heads, d = 32, k = 15 with clustered
 Gaussian Q/K (256 clusters) and i.i.d. V and dO.  Inputs are resident in HBM
 before the timed region starts.
 
-Prints one JSON line.  `roofline` is for the dominant kernel, the score scan:
-algorithmic flops 2*d*H*sum_b n_b^2 per launch over its average duration,
-measured with events on the stream it runs on, against the dense bf16 MFMA
-peak.  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
-workload on the host cores.
+Prints one JSON line.  `roofline` is for the dominant kernel, the score scan
+(one launch = its threshold and selection passes): algorithmic flops
+2*d*H*sum_b n_b^2 per launch over its average duration, measured with events
+on the stream it runs on, against the dense bf16 MFMA peak.  `traffic` is the
+HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+summary (calibrated against a plain device copy), null once the scan sources
+differ from the ones profiled.  `cpu_baseline` times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -43,6 +46,29 @@ def backward_bytes_per_row(d, k):
     transpose (3 x 4k + 4) and key side (pair id, (p, ds), q row, dO row),
     plus dO, dq, dk, dv."""
     return k * (40 + 10 * d) + 16 * d + 4
+
+
+def scan_traffic(workload: str):
+    """HBM bytes per score-scan launch from the committed rocprofv3 summary,
+    or None when it was taken for another workload or the scan sources have
+    changed since (the summary records their SHA-256)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_" + workload.replace("train_clustered_", "train_")
+                        + ".md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        key, sep, val = line.strip().partition(": ")
+        if sep:
+            fields[key] = val
+    h = hashlib.sha256()
+    for f in ("kmip_scan.hip", "kmip_internal.h"):
+        with open(os.path.join(ROOT, "graph_transformer_sparse_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("workload") != workload or fields.get("scan_source_sha256") != h.hexdigest():
+        return None
+    return float(fields["score_topk_traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, nodes: int, seed: int = 7):
@@ -80,6 +106,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-nodes", type=int, default=16384,
                     help="query nodes in the CPU oracle sample (0 skips the CPU baseline)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy, whose byte "
+                         "counters calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -95,6 +124,13 @@ def main():
 
     w = get_workload(args.workload)
     dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
@@ -175,7 +211,7 @@ def main():
                    if w.backward else "forward"},
         "roofline": {"bound": "mfma", "achieved": scan_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": scan_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None, "kernel": "score_topk_kernel",
+                     "traffic": scan_traffic(w.name), "kernel": "score_topk_kernel",
                      "algorithmic_flop_per_launch": flops,
                      "avg_launch_ms": float(scan_ms.mean())},
         "phases_ms": {"score_topk": float(scan_ms.mean()),

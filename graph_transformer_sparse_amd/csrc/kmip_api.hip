@@ -163,7 +163,7 @@ kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t
   float2* pairs = reinterpret_cast<float2*>(w);
   w += align256((size_t)P * sizeof(float2));
   SortScratch sc;
-  sort_scratch_carve(w, P, HN, &sc);
+  sort_scratch_carve(w, pairs, P, HN, &sc);
   w += sort_scratch_bytes(P, HN);
   double* partials = reinterpret_cast<double*>(w);
 
@@ -174,7 +174,7 @@ kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t
   st = launch_status(launch_selection_transpose(topk_idx, N, H, topk, &sc, s));
   if (st != KMIP_OK) return st;
   return launch_status(launch_bwd_keys(static_cast<const uint16_t*>(q), dout, N, H, d, topk,
-                                       pairs, &sc, partials, dk, dv, s));
+                                       &sc, partials, dk, dv, s));
 }
 
 }  // extern "C"

@@ -8,12 +8,14 @@
 //
 // The forward leaves the selection as rows of k keys per query.  The key
 // side needs the transpose, so:
-//  1. every pair (row*k + slot) gets the sort key h*N + j (padding slots get
-//     the sentinel H*N) and key counts are histogrammed;
-//  2. a stable LSD radix sort (8-bit digits) orders the pairs by key; within
-//     a key the pairs stay in ascending pair id, i.e. ascending query;
-//  3. an exclusive scan of the counts gives the key segment pointers;
-//  4. fixed-length slices of the sorted pairs are reduced by 16-lane groups
+//  1. a stable LSD radix sort (8-bit digits) orders the pairs (row*k + slot)
+//     by the key h*N + j (padding slots get the sentinel H*N); within a key
+//     the pairs stay in ascending pair id, i.e. ascending query.  The first
+//     pass derives the keys from topk_idx and the pair ids from positions;
+//     every pass carries the pair's (p, ds), so the reduction reads them in
+//     sorted order instead of gathering 8 bytes per pair;
+//  2. key segment pointers come from a binary search of the sorted keys;
+//  3. fixed-length slices of the sorted pairs are reduced by 16-lane groups
 //     (no atomics).  Runs that cover a whole key segment are written
 //     directly; runs cut by a slice boundary go to per-slice partials, which
 //     a fix-up pass adds in slice order.  Keys selected by no query get exact
@@ -23,24 +25,12 @@
 namespace kmip {
 namespace {
 
-__global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
-// keys[pid] = h*N + j (or H*N for padding), vals[pid] = pid, counts[key]++.
-__global__ void make_keys_kernel(const int32_t* __restrict__ idx, int64_t P, int64_t N, int H,
-                                 int topk, uint32_t* __restrict__ keys,
-                                 uint32_t* __restrict__ vals, int32_t* __restrict__ counts) {
-  const int64_t pid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (pid >= P) return;
-  const int64_t row = pid / topk;
-  const int h = (int)(row % H);
+// Sort key of pair pid (row-major [N][H][k] slots of topk_idx).
+__device__ __forceinline__ uint32_t pair_key(const int32_t* __restrict__ idx, int64_t pid,
+                                             int64_t N, int H, int topk) {
+  const int h = (int)((pid / topk) % H);
   const int32_t j = idx[pid];
-  const uint32_t key = j < 0 ? (uint32_t)(N * H) : (uint32_t)(h * N + j);
-  keys[pid] = key;
-  vals[pid] = (uint32_t)pid;
-  atomicAdd(&counts[key], 1);   // integer counts: order-independent result
+  return j < 0 ? (uint32_t)(N * H) : (uint32_t)(h * N + j);
 }
 
 // ------------------------------------------------------------ device scan
@@ -121,9 +111,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_down_kernel(
 }
 
 // ------------------------------------------------------------ radix sort
+// Digit histogram of one tile.  First pass (keys == nullptr): the keys are
+// derived from topk_idx.
 __global__ __launch_bounds__(SORT_THREADS) void radix_hist_kernel(
-    const uint32_t* __restrict__ keys, int64_t P, int shift, int32_t* __restrict__ hist,
-    int64_t nblk) {
+    const uint32_t* __restrict__ keys, const int32_t* __restrict__ idx, int64_t N, int H,
+    int topk, int64_t P, int shift, int32_t* __restrict__ hist, int64_t nblk) {
   __shared__ int32_t cnt[SORT_BINS];
   cnt[threadIdx.x] = 0;
   __syncthreads();
@@ -131,7 +123,10 @@ __global__ __launch_bounds__(SORT_THREADS) void radix_hist_kernel(
 #pragma unroll
   for (int i = 0; i < SORT_ITEMS; ++i) {
     const int64_t e = base + i * SORT_THREADS + threadIdx.x;
-    if (e < P) atomicAdd(&cnt[(keys[e] >> shift) & (SORT_BINS - 1)], 1);
+    if (e < P) {
+      const uint32_t k = keys ? keys[e] : pair_key(idx, e, N, H, topk);
+      atomicAdd(&cnt[(k >> shift) & (SORT_BINS - 1)], 1);
+    }
   }
   __syncthreads();
   hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = cnt[threadIdx.x];
@@ -141,16 +136,29 @@ __global__ __launch_bounds__(SORT_THREADS) void radix_hist_kernel(
 // [tile + w*1024, +1024) in order, 64 at a time: equal digits inside a
 // 64-element chunk are found with 8 ballots, and a per-wave running count
 // per digit carries the rank across chunks.  Waves are then offset by the
-// counts of the earlier waves, blocks by the scanned histogram.
+// counts of the earlier waves, the tile is reordered by digit in LDS, and
+// each digit's run is written at the block's offset from the scanned
+// histogram.
+// First pass (keys_in == nullptr): keys come from topk_idx and pair ids are
+// the positions.
 __global__ __launch_bounds__(SORT_THREADS) void radix_scatter_kernel(
-    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t P,
-    int shift, const int32_t* __restrict__ hist_scan, int64_t nblk,
-    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out) {
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
+    const float2* __restrict__ pay_in, const int32_t* __restrict__ idx, int64_t N, int H,
+    int topk, int64_t P, int shift, const int32_t* __restrict__ hist_scan, int64_t nblk,
+    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
+    float2* __restrict__ pay_out) {
   constexpr int NW = SORT_THREADS / 64;
   constexpr int PER_WAVE = SORT_TILE / NW;
   constexpr int CHUNKS = PER_WAVE / 64;
+  static_assert(SORT_THREADS == SCAN_THREADS && SORT_BINS == SORT_THREADS,
+                "one digit per thread; block_excl_scan covers the block");
   __shared__ int32_t wcnt[NW][SORT_BINS];
   __shared__ int32_t gbase[SORT_BINS];
+  __shared__ int32_t dstart[SORT_BINS];
+  __shared__ int32_t sh[SORT_THREADS / 64];
+  __shared__ uint32_t lk[SORT_TILE];
+  __shared__ uint32_t lv[SORT_TILE];
+  __shared__ float2 lpay[SORT_TILE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int w = 0; w < NW; ++w) wcnt[w][threadIdx.x] = 0;
@@ -159,14 +167,17 @@ __global__ __launch_bounds__(SORT_THREADS) void radix_scatter_kernel(
 
   const uint64_t lt = (1ull << lane) - 1ull;
   const int64_t wbase = (int64_t)blockIdx.x * SORT_TILE + (int64_t)wave * PER_WAVE;
+  const bool first = keys_in == nullptr;
   uint32_t k[CHUNKS], v[CHUNKS];
+  float2 pl[CHUNKS];
   int32_t rank[CHUNKS];
 #pragma unroll
   for (int c = 0; c < CHUNKS; ++c) {
     const int64_t e = wbase + c * 64 + lane;
     const bool valid = e < P;
-    k[c] = valid ? keys_in[e] : 0u;
-    v[c] = valid ? vals_in[e] : 0u;
+    k[c] = !valid ? 0u : first ? pair_key(idx, e, N, H, topk) : keys_in[e];
+    v[c] = !valid ? 0u : first ? (uint32_t)e : vals_in[e];
+    pl[c] = valid ? pay_in[e] : make_float2(0.f, 0.f);
     const int dg = (int)((k[c] >> shift) & (SORT_BINS - 1));
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -181,26 +192,40 @@ __global__ __launch_bounds__(SORT_THREADS) void radix_scatter_kernel(
     if (leader) wcnt[wave][dg] = before + __popcll(peers);
   }
   __syncthreads();
+  int32_t dtot = 0;
   {   // exclusive prefix over waves, one digit per thread
     const int d = threadIdx.x;
-    int32_t run = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const int32_t c = wcnt[w][d];
-      wcnt[w][d] = run;
-      run += c;
+      wcnt[w][d] = dtot;
+      dtot += c;
     }
   }
+  // Block-local start of every digit's run, then the tile is staged in LDS
+  // in digit order so that the global writes go out as contiguous runs.
+  int32_t tile_total;
+  dstart[threadIdx.x] = block_excl_scan(dtot, sh, &tile_total);
   __syncthreads();
 #pragma unroll
   for (int c = 0; c < CHUNKS; ++c) {
     const int64_t e = wbase + c * 64 + lane;
     if (e < P) {
       const int dg = (int)((k[c] >> shift) & (SORT_BINS - 1));
-      const int64_t pos = (int64_t)gbase[dg] + wcnt[wave][dg] + rank[c];
-      keys_out[pos] = k[c];
-      vals_out[pos] = v[c];
+      const int lp = dstart[dg] + wcnt[wave][dg] + rank[c];
+      lk[lp] = k[c];
+      lv[lp] = v[c];
+      lpay[lp] = pl[c];
     }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < tile_total; i += SORT_THREADS) {
+    const uint32_t kk = lk[i];
+    const int dg = (int)((kk >> shift) & (SORT_BINS - 1));
+    const int64_t pos = (int64_t)gbase[dg] + (i - dstart[dg]);
+    keys_out[pos] = kk;
+    vals_out[pos] = lv[i];
+    pay_out[pos] = lpay[i];
   }
 }
 
@@ -252,7 +277,7 @@ constexpr int SEG_GROUPS = 16;     // 16-lane groups per 256-thread block
 template <int D>
 __global__ __launch_bounds__(256) void segreduce_kernel(
     const uint16_t* __restrict__ Q, const float* __restrict__ dout,
-    const float2* __restrict__ pairs, const uint32_t* __restrict__ skeys,
+    const float2* __restrict__ spay, const uint32_t* __restrict__ skeys,
     const uint32_t* __restrict__ svals, const int32_t* __restrict__ key_ptr, int64_t N, int H,
     int topk, int64_t nslices, double* __restrict__ partials, float* __restrict__ dk,
     float* __restrict__ dv) {
@@ -307,7 +332,7 @@ __global__ __launch_bounds__(256) void segreduce_kernel(
     }
     const uint32_t pid = svals[t];
     const int64_t row = pid / (uint32_t)topk;
-    const float2 pr = pairs[pid];
+    const float2 pr = spay[t];
     float qx[EPL], gx[EPL];
     load_bf16_cols<EPL>(Q + row * D + l16 * EPL, qx);
     load_f32_cols<EPL>(dout + row * D + l16 * EPL, gx);
@@ -361,6 +386,20 @@ __global__ __launch_bounds__(256) void segfix_kernel(const int32_t* __restrict__
   store_f32_cols<EPL>(dv + orow * D + l16 * EPL, fv);
 }
 
+// key_ptr[key] = first position of the sorted keys that is >= key, for
+// key in [0, H*N + 1]: the segment of key is [key_ptr[key], key_ptr[key+1]).
+__global__ void key_ptr_kernel(const uint32_t* __restrict__ skeys, int64_t P, int64_t nkeys,
+                               int32_t* __restrict__ key_ptr) {
+  const int64_t key = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (key >= nkeys) return;
+  int64_t lo = 0, hi = P;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if ((int64_t)skeys[mid] < key) lo = mid + 1; else hi = mid;
+  }
+  key_ptr[key] = (int32_t)lo;
+}
+
 int sort_passes(int64_t max_key) {
   int bits = 0;
   while ((max_key >> bits) != 0) ++bits;
@@ -385,27 +424,29 @@ hipError_t launch_exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int
 size_t sort_scratch_bytes(int64_t P, int64_t HN) {
   const int64_t nblk = ceil_div(P, SORT_TILE);
   const int64_t hist_n = (int64_t)SORT_BINS * nblk;
-  const int64_t aux_n = scan_aux_elems(hist_n > HN + 2 ? hist_n : HN + 2);
+  const int64_t aux_n = scan_aux_elems(hist_n);
   size_t b = 0;
   b += 4 * align256((size_t)P * 4);            // keys[2], vals[2]
+  b += align256((size_t)P * sizeof(float2));   // pay[1]
   b += align256((size_t)hist_n * 4);
   b += align256((size_t)aux_n * 4);
-  b += 2 * align256((size_t)(HN + 2) * 4);     // counts, key_ptr
+  b += align256((size_t)(HN + 2) * 4);         // key_ptr
   return b;
 }
 
-void sort_scratch_carve(void* base, int64_t P, int64_t HN, SortScratch* sc) {
+void sort_scratch_carve(void* base, float2* pairs, int64_t P, int64_t HN, SortScratch* sc) {
   const int64_t nblk = ceil_div(P, SORT_TILE);
   const int64_t hist_n = (int64_t)SORT_BINS * nblk;
-  const int64_t aux_n = scan_aux_elems(hist_n > HN + 2 ? hist_n : HN + 2);
+  const int64_t aux_n = scan_aux_elems(hist_n);
   char* p = static_cast<char*>(base);
   sc->keys[0] = reinterpret_cast<uint32_t*>(p); p += align256((size_t)P * 4);
   sc->keys[1] = reinterpret_cast<uint32_t*>(p); p += align256((size_t)P * 4);
   sc->vals[0] = reinterpret_cast<uint32_t*>(p); p += align256((size_t)P * 4);
   sc->vals[1] = reinterpret_cast<uint32_t*>(p); p += align256((size_t)P * 4);
+  sc->pay[0] = pairs;
+  sc->pay[1] = reinterpret_cast<float2*>(p); p += align256((size_t)P * sizeof(float2));
   sc->hist = reinterpret_cast<int32_t*>(p); p += align256((size_t)hist_n * 4);
   sc->scan_aux = reinterpret_cast<int32_t*>(p); p += align256((size_t)aux_n * 4);
-  sc->counts = reinterpret_cast<int32_t*>(p); p += align256((size_t)(HN + 2) * 4);
   sc->key_ptr = reinterpret_cast<int32_t*>(p);
   sc->final_buf = 0;
 }
@@ -414,29 +455,28 @@ hipError_t launch_selection_transpose(const int32_t* topk_idx, int64_t N, int H,
                                       SortScratch* sc, hipStream_t s) {
   const int64_t P = N * H * topk;
   const int64_t HN = N * H;
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)ceil_div(HN + 2, 256)), dim3(256), 0, s,
-                     sc->counts, HN + 2, 0);
-  hipLaunchKernelGGL(make_keys_kernel, dim3((unsigned)ceil_div(P, 256)), dim3(256), 0, s,
-                     topk_idx, P, N, H, topk, sc->keys[0], sc->vals[0], sc->counts);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int64_t nblk = ceil_div(P, SORT_TILE);
   const int passes = sort_passes(HN);
+  hipError_t e = hipSuccess;
   int cur = 0;
   for (int ps = 0; ps < passes; ++ps) {
     const int shift = ps * SORT_BITS;
-    hipLaunchKernelGGL(radix_hist_kernel, dim3((unsigned)nblk), dim3(SORT_THREADS), 0, s,
-                       sc->keys[cur], P, shift, sc->hist, nblk);
+    // Pass 0 reads topk_idx and the caller's pairs (pay[0]); later passes
+    // ping-pong between the buffer pairs.
+    const uint32_t* kin = ps == 0 ? nullptr : sc->keys[cur];
+    const uint32_t* vin = ps == 0 ? nullptr : sc->vals[cur];
+    hipLaunchKernelGGL(radix_hist_kernel, dim3((unsigned)nblk), dim3(SORT_THREADS), 0, s, kin,
+                       topk_idx, N, H, topk, P, shift, sc->hist, nblk);
     e = launch_exclusive_scan(sc->hist, sc->hist, (int64_t)SORT_BINS * nblk, sc->scan_aux, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(radix_scatter_kernel, dim3((unsigned)nblk), dim3(SORT_THREADS), 0, s,
-                       sc->keys[cur], sc->vals[cur], P, shift, sc->hist, nblk,
-                       sc->keys[cur ^ 1], sc->vals[cur ^ 1]);
+                       kin, vin, sc->pay[cur], topk_idx, N, H, topk, P, shift, sc->hist, nblk,
+                       sc->keys[cur ^ 1], sc->vals[cur ^ 1], sc->pay[cur ^ 1]);
     cur ^= 1;
   }
   sc->final_buf = cur;
-  e = launch_exclusive_scan(sc->counts, sc->key_ptr, HN + 2, sc->scan_aux, s);
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(key_ptr_kernel, dim3((unsigned)ceil_div(HN + 2, 256)), dim3(256), 0, s,
+                     sc->keys[cur], P, HN + 2, sc->key_ptr);
   return hipGetLastError();
 }
 
@@ -446,8 +486,8 @@ size_t segreduce_scratch_bytes(int64_t P, int d) {
 }
 
 hipError_t launch_bwd_keys(const uint16_t* q, const float* dout, int64_t N, int H, int d,
-                           int topk, const float2* pairs, const SortScratch* sc,
-                           double* partials, float* dk, float* dv, hipStream_t s) {
+                           int topk, const SortScratch* sc, double* partials, float* dk,
+                           float* dv, hipStream_t s) {
   const int64_t P = N * H * topk;
   const int64_t HN = N * H;
   const int64_t nslices = ceil_div(P, SEG_SLICE);
@@ -455,13 +495,14 @@ hipError_t launch_bwd_keys(const uint16_t* q, const float* dout, int64_t N, int 
   const unsigned b2 = (unsigned)ceil_div(HN, SEG_GROUPS);
   const uint32_t* sk = sc->keys[sc->final_buf];
   const uint32_t* sv = sc->vals[sc->final_buf];
+  const float2* sp = sc->pay[sc->final_buf];
   if (d == 32) {
-    hipLaunchKernelGGL(segreduce_kernel<32>, dim3(b1), dim3(256), 0, s, q, dout, pairs, sk, sv,
+    hipLaunchKernelGGL(segreduce_kernel<32>, dim3(b1), dim3(256), 0, s, q, dout, sp, sk, sv,
                        sc->key_ptr, N, H, topk, nslices, partials, dk, dv);
     hipLaunchKernelGGL(segfix_kernel<32>, dim3(b2), dim3(256), 0, s, sc->key_ptr, N, H,
                        partials, dk, dv);
   } else if (d == 64) {
-    hipLaunchKernelGGL(segreduce_kernel<64>, dim3(b1), dim3(256), 0, s, q, dout, pairs, sk, sv,
+    hipLaunchKernelGGL(segreduce_kernel<64>, dim3(b1), dim3(256), 0, s, q, dout, sp, sk, sv,
                        sc->key_ptr, N, H, topk, nslices, partials, dk, dv);
     hipLaunchKernelGGL(segfix_kernel<64>, dim3(b2), dim3(256), 0, s, sc->key_ptr, N, H,
                        partials, dk, dv);

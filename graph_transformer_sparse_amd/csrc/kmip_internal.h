@@ -71,27 +71,29 @@ hipError_t launch_bwd_query(const uint16_t* k, const uint16_t* v, int64_t N, int
                             int topk, const int32_t* topk_idx, const float* topk_score,
                             const float* dout, float* dq, float2* pairs, hipStream_t s);
 
-// Backward, selection transpose: stable sort of pairs by key h*N + j, key
-// segment pointers key_ptr[H*N + 2].
+// Backward, selection transpose: stable sort of the pairs by key h*N + j
+// (padding slots: H*N), carrying each pair's id and its (p, ds); key segment
+// pointers key_ptr[H*N + 2].  The pairs array itself is the first pass's
+// payload input and is overwritten by later passes.
 struct SortScratch {
   uint32_t* keys[2];
-  uint32_t* vals[2];
+  uint32_t* vals[2];      // pair ids
+  float2* pay[2];         // (p, ds); pay[0] is the caller's pairs array
   int32_t* hist;          // SORT_BINS * nblocks
   int32_t* scan_aux;      // block sums of the device-wide scan
-  int32_t* counts;        // H*N + 2
   int32_t* key_ptr;       // H*N + 2
-  int final_buf;          // which of keys/vals holds the sorted result
+  int final_buf;          // which of keys/vals/pay holds the sorted result
 };
 size_t sort_scratch_bytes(int64_t P, int64_t HN);
-void sort_scratch_carve(void* base, int64_t P, int64_t HN, SortScratch* sc);
+void sort_scratch_carve(void* base, float2* pairs, int64_t P, int64_t HN, SortScratch* sc);
 hipError_t launch_selection_transpose(const int32_t* topk_idx, int64_t N, int H, int topk,
                                       SortScratch* sc, hipStream_t s);
 
 // Backward, key side: dk, dv by segmented reduction over the sorted pairs.
 size_t segreduce_scratch_bytes(int64_t P, int d);
 hipError_t launch_bwd_keys(const uint16_t* q, const float* dout, int64_t N, int H, int d,
-                           int topk, const float2* pairs, const SortScratch* sc,
-                           double* partials, float* dk, float* dv, hipStream_t s);
+                           int topk, const SortScratch* sc, double* partials, float* dk,
+                           float* dv, hipStream_t s);
 
 // Device-wide exclusive scan of int32 (aux: scan_aux_elems(n) ints).
 int64_t scan_aux_elems(int64_t n);

@@ -35,6 +35,8 @@ size_t forward_ws(int64_t N, int H, int num_graphs) {
   if (num_graphs > 1) {
     const int64_t tiles = scan_max_tiles(N, num_graphs);
     b += align256((size_t)(num_graphs + 1) * 4) + align256((size_t)tiles * sizeof(int2));
+  } else {
+    b += query_order_bytes(N, H);
   }
   return b;
 }
@@ -93,20 +95,32 @@ kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t max_tiles = scan_max_tiles(N, num_graphs);
   char* w = static_cast<char*>(workspace);
-  float* thr = reinterpret_cast<float*>(w);
+  ScanArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.N = N;
+  a.H = H;
+  a.topk = topk;
+  a.max_tiles = max_tiles;
+  a.thr = reinterpret_cast<float*>(w);
+  a.idx = topk_idx;
+  a.score = topk_score;
   w += align256((size_t)N * H * sizeof(float));
-  int2* tiles = nullptr;
   if (!single) {
     int32_t* tile_start = reinterpret_cast<int32_t*>(w);
-    tiles = reinterpret_cast<int2*>(w + align256((size_t)(num_graphs + 1) * 4));
+    int2* tiles = reinterpret_cast<int2*>(w + align256((size_t)(num_graphs + 1) * 4));
     st = launch_status(launch_tile_plan(graph_offsets, num_graphs, max_tiles, tile_start,
                                         tiles, s));
     if (st != KMIP_OK) return st;
+    a.offsets = graph_offsets;
+    a.tiles = tiles;
+  } else {
+    int32_t* perm = nullptr;
+    st = launch_status(launch_query_order(a.q, N, H, d, w, &perm, s));
+    if (st != KMIP_OK) return st;
+    a.perm = perm;
   }
-  return launch_status(launch_score_topk(static_cast<const uint16_t*>(q),
-                                         static_cast<const uint16_t*>(k), N, H, d, topk,
-                                         single ? nullptr : graph_offsets, num_graphs, tiles,
-                                         max_tiles, thr, topk_idx, topk_score, s));
+  return launch_status(launch_score_topk(a, d, s));
 }
 
 kmip_status_t kmip_gather_softmax_av(const void* v, int64_t N, int H, int d, int topk,

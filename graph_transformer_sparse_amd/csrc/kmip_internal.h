@@ -55,11 +55,29 @@ hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_
 
 // Score scan in two passes: a threshold pass writing a per-row lower bound
 // of the k-th score into thr[N*H], then the exact running top-k seeded with
-// it.  Writes topk_idx / topk_score.
-hipError_t launch_score_topk(const uint16_t* q, const uint16_t* k, int64_t N, int H, int d,
-                             int topk, const int32_t* offsets, int num_graphs,
-                             const int2* tiles, int64_t max_tiles, float* thr,
-                             int32_t* topk_idx, float* topk_score, hipStream_t s);
+// it.  Writes idx / score.  One graph: tiles == nullptr, and perm (may be
+// null) gives each head's query order [H][N]; batched graphs: the tile plan.
+struct ScanArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t N;
+  int H, topk;
+  const int32_t* offsets;
+  const int2* tiles;
+  int64_t max_tiles;
+  const int32_t* perm;
+  float* thr;
+  int32_t* idx;
+  float* score;
+};
+hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s);
+
+// Query order for one graph: groups each head's queries by a sign-random-
+// projection code of q.  Workspace: query_order_bytes(N, H); *perm points
+// into it ([H][N] node ids).
+size_t query_order_bytes(int64_t N, int H);
+hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* ws,
+                              int32_t** perm, hipStream_t s);
 
 // Gather the selected V rows, softmax over saved scores, weighted sum.
 hipError_t launch_gather_av(const uint16_t* v, int64_t N, int H, int d, int topk,

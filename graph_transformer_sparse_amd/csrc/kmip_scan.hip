@@ -129,6 +129,8 @@ struct Scanner {
   uint2* cbuf;                // per-lane candidate buffers (selection pass)
   const uint16_t* Q;
   const uint16_t* K;
+  const int32_t* perm;        // query order per head, [H][N] (one graph), or null
+  int64_t N;
   int H, topk;
   float* thr_buf;
   int32_t* out_idx;
@@ -187,11 +189,13 @@ struct Scanner {
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       const int64_t first = t.q0 + (wave * QB + b) * 32;
-      qrow[b] = first + lrow;
+      // Positions [q0, q1) index the head's query order; rows are node ids.
+      const int64_t pos = first + lrow;
       bact[b] = first < t.q1;
-      qvalid[b] = qrow[b] < t.q1;
-      const int64_t ql = qvalid[b] ? qrow[b] : t.q1 - 1;
-      const uint16_t* qp = Q + (ql * H + t.h) * D + 8 * lhalf;
+      qvalid[b] = pos < t.q1;
+      const int64_t pl = qvalid[b] ? pos : t.q1 - 1;
+      qrow[b] = perm ? (int64_t)perm[t.h * N + pl] : pl;
+      const uint16_t* qp = Q + (qrow[b] * H + t.h) * D + 8 * lhalf;
 #pragma unroll
       for (int m = 0; m < S::NM; ++m) qb[b][m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
     }
@@ -440,17 +444,18 @@ struct Scanner {
 // blocks (32 rows each) into equal contiguous ranges.  Batched graphs: one
 // workgroup per (planned tile, head).
 template <int D, int KP, bool PRE>
-__global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int64_t N, int H,
-    int topk, const int32_t* __restrict__ offsets, const int2* __restrict__ tiles, int nwg,
-    float* __restrict__ thr_buf, int32_t* __restrict__ out_idx,
-    float* __restrict__ out_score) {
+__global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(ScanArgs a, int nwg) {
+  const int64_t N = a.N;
+  const int H = a.H;
+  const int2* tiles = a.tiles;
+  const int32_t* offsets = a.offsets;
   using S = ScanShape<D, PRE>;
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[S::NBUF * S::CHUNK_BYTES];
   __shared__ __attribute__((aligned(16))) uint2 cbuf[PRE ? 1 : SCAN_WAVES * SCAN_CAP * 64];
   const unsigned kbuf_lds =
       (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kbuf;
-  Scanner<D, KP, PRE> sc{kbuf, kbuf_lds, cbuf, Q, K, H, topk, thr_buf, out_idx, out_score};
+  Scanner<D, KP, PRE> sc{kbuf,  kbuf_lds, cbuf,   a.q,   a.k,      a.perm,
+                         a.N,   a.H,      a.topk, a.thr, a.idx,    a.score};
   // Query blocks [b, be) of the flattened (head, 32-row block) space for one
   // graph; a single planned sub-tile for batched graphs.
   const int64_t nbph = (N + 31) / 32;
@@ -560,55 +565,112 @@ int resident_workgroups(Kern kern) {
 }
 
 template <int D, int KP, bool PRE>
-hipError_t launch_pass(const uint16_t* q, const uint16_t* k, int64_t N, int H, int topk,
-                       const int32_t* offsets, const int2* tiles, int64_t max_tiles,
-                       float* thr, int32_t* idx, float* score, hipStream_t s) {
+hipError_t launch_pass(const ScanArgs& a, hipStream_t s) {
   auto kern = score_topk_kernel<D, KP, PRE>;
   int nwg = 0;
   dim3 grid;
-  if (tiles == nullptr) {
+  if (a.tiles == nullptr) {
     nwg = resident_workgroups(kern);
     if (nwg <= 0) return hipErrorInvalidDevice;
     grid = dim3((unsigned)nwg);
   } else {
-    grid = dim3((unsigned)(max_tiles * H));
+    grid = dim3((unsigned)(a.max_tiles * a.H));
   }
-  hipLaunchKernelGGL(kern, grid, dim3(SCAN_WAVES * 64), 0, s, q, k, N, H, topk, offsets, tiles,
-                     nwg, thr, idx, score);
+  hipLaunchKernelGGL(kern, grid, dim3(SCAN_WAVES * 64), 0, s, a, nwg);
   return hipGetLastError();
 }
 
 template <int D, int KP>
-hipError_t launch_scan_t(const uint16_t* q, const uint16_t* k, int64_t N, int H, int topk,
-                         const int32_t* offsets, const int2* tiles, int64_t max_tiles,
-                         float* thr, int32_t* idx, float* score, hipStream_t s) {
-  hipError_t e = launch_pass<D, KP, true>(q, k, N, H, topk, offsets, tiles, max_tiles, thr,
-                                          idx, score, s);
+hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
+  hipError_t e = launch_pass<D, KP, true>(a, s);
   if (e != hipSuccess) return e;
-  return launch_pass<D, KP, false>(q, k, N, H, topk, offsets, tiles, max_tiles, thr, idx,
-                                   score, s);
+  return launch_pass<D, KP, false>(a, s);
 }
 
 template <int D>
-hipError_t launch_scan_d(int kp, const uint16_t* q, const uint16_t* k, int64_t N, int H,
-                         int topk, const int32_t* offsets, const int2* tiles, int64_t max_tiles,
-                         float* thr, int32_t* idx, float* score, hipStream_t s) {
-#define KMIP_CASE(L)                                                                   \
-  case L:                                                                              \
-    return launch_scan_t<D, L>(q, k, N, H, topk, offsets, tiles, max_tiles, thr, idx, \
-                               score, s);
+hipError_t launch_scan_d(int kp, const ScanArgs& a, hipStream_t s) {
   switch (kp) {
-    KMIP_CASE(5)
-    KMIP_CASE(8)
-    KMIP_CASE(15)
-    KMIP_CASE(16)
-    KMIP_CASE(32)
-    KMIP_CASE(45)
-    KMIP_CASE(48)
-    KMIP_CASE(64)
+    case 5: return launch_scan_t<D, 5>(a, s);
+    case 8: return launch_scan_t<D, 8>(a, s);
+    case 15: return launch_scan_t<D, 15>(a, s);
+    case 16: return launch_scan_t<D, 16>(a, s);
+    case 32: return launch_scan_t<D, 32>(a, s);
+    case 45: return launch_scan_t<D, 45>(a, s);
+    case 48: return launch_scan_t<D, 48>(a, s);
+    case 64: return launch_scan_t<D, 64>(a, s);
     default: return hipErrorInvalidValue;
   }
-#undef KMIP_CASE
+}
+
+// ------------------------------------------------------------ query order
+// Queries of one head are grouped by a 12-bit sign-random-projection code of
+// q (Rademacher directions fixed by the constants below), so that the 32
+// queries of a wavefront tend to point the same way and share their few
+// high-scoring keys: the selection pass then meets far fewer 32-key blocks
+// holding a candidate for any of its queries.  The order only changes which
+// queries share a wavefront; every query's result is independent of it.
+constexpr int LSH_BITS = 12;
+constexpr int LSH_BINS = 1 << LSH_BITS;
+// Each (head, code) count is split over LSH_COPIES counters picked by the
+// node id, which keeps atomic contention low when many queries share a code.
+constexpr int LSH_COPIES = 16;
+__constant__ uint32_t kLshSigns[LSH_BITS][2] = {
+    {0x9e3779b9u, 0x7f4a7c15u}, {0xf39cc060u, 0x5ced1d6bu}, {0xbf58476du, 0x1ce4e5b9u},
+    {0x94d049bbu, 0x133111ebu}, {0x2545f491u, 0x4f6cdd1du}, {0xd6e8feb8u, 0x6658e9a5u},
+    {0x85ebca6bu, 0xc2b2ae35u}, {0x27d4eb2fu, 0x165667b1u}, {0xa0761d64u, 0xe7037ed1u},
+    {0x8ebc6af0u, 0x589965ccu}, {0x1d8e4e27u, 0xc5ed3a8bu}, {0x6a09e667u, 0xbb67ae85u}};
+
+__global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// codes[h*N + i] and per-(head, code) counts.
+template <int D>
+__global__ void lsh_code_kernel(const uint16_t* __restrict__ Q, int64_t N, int H,
+                                uint16_t* __restrict__ codes, int32_t* __restrict__ counts) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // r = i*H + h
+  if (r >= N * H) return;
+  const int64_t i = r / H;
+  const int h = (int)(r % H);
+  float x[D];
+  const uint4* src = reinterpret_cast<const uint4*>(Q + r * D);
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const uint4 w = src[c];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * c + 2 * e] = __uint_as_float(ws[e] << 16);
+      x[8 * c + 2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
+    }
+  }
+  uint32_t code = 0;
+#pragma unroll
+  for (int b = 0; b < LSH_BITS; ++b) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      const bool neg = (kLshSigns[b][c >> 5] >> (c & 31)) & 1u;
+      acc += neg ? -x[c] : x[c];
+    }
+    code |= (acc > 0.f ? 1u : 0u) << b;
+  }
+  codes[h * N + i] = (uint16_t)code;
+  atomicAdd(&counts[((int64_t)h * LSH_BINS + code) * LSH_COPIES + (i & (LSH_COPIES - 1))], 1);
+}
+
+// perm[h*N + pos] = i, positions handed out per (head, code) from the
+// scanned counts.  The order inside a code group is immaterial.
+__global__ void lsh_place_kernel(const uint16_t* __restrict__ codes, int64_t N, int H,
+                                 int32_t* __restrict__ cursor, int32_t* __restrict__ perm) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // r = h*N + i
+  if (r >= N * H) return;
+  const int h = (int)(r / N);
+  const int64_t i = r % N;
+  const int pos = atomicAdd(
+      &cursor[((int64_t)h * LSH_BINS + codes[r]) * LSH_COPIES + (i & (LSH_COPIES - 1))], 1);
+  perm[pos] = (int32_t)i;
 }
 
 }  // namespace
@@ -632,19 +694,42 @@ hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_
   return hipGetLastError();
 }
 
-hipError_t launch_score_topk(const uint16_t* q, const uint16_t* k, int64_t N, int H, int d,
-                             int topk, const int32_t* offsets, int num_graphs,
-                             const int2* tiles, int64_t max_tiles, float* thr,
-                             int32_t* topk_idx, float* topk_score, hipStream_t s) {
-  const int kp = scan_list_len(topk);
-  const bool single = (offsets == nullptr || num_graphs <= 1);
-  const int2* t = single ? nullptr : tiles;
+size_t query_order_bytes(int64_t N, int H) {
+  const int64_t nb = (int64_t)H * LSH_BINS * LSH_COPIES;
+  return align256((size_t)N * H * 4) + align256((size_t)N * H * 2) + 2 * align256((size_t)nb * 4) +
+         align256((size_t)scan_aux_elems(nb) * 4);
+}
+
+hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* ws,
+                              int32_t** perm_out, hipStream_t s) {
+  const int64_t nb = (int64_t)H * LSH_BINS * LSH_COPIES;
+  char* p = static_cast<char*>(ws);
+  int32_t* perm = reinterpret_cast<int32_t*>(p); p += align256((size_t)N * H * 4);
+  uint16_t* codes = reinterpret_cast<uint16_t*>(p); p += align256((size_t)N * H * 2);
+  int32_t* counts = reinterpret_cast<int32_t*>(p); p += align256((size_t)nb * 4);
+  int32_t* cursor = reinterpret_cast<int32_t*>(p); p += align256((size_t)nb * 4);
+  int32_t* aux = reinterpret_cast<int32_t*>(p);
+  const unsigned rows = (unsigned)ceil_div(N * H, 256);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, s,
+                     counts, nb);
   if (d == 32)
-    return launch_scan_d<32>(kp, q, k, N, H, topk, offsets, t, max_tiles, thr, topk_idx,
-                             topk_score, s);
-  if (d == 64)
-    return launch_scan_d<64>(kp, q, k, N, H, topk, offsets, t, max_tiles, thr, topk_idx,
-                             topk_score, s);
+    hipLaunchKernelGGL(lsh_code_kernel<32>, dim3(rows), dim3(256), 0, s, q, N, H, codes, counts);
+  else
+    hipLaunchKernelGGL(lsh_code_kernel<64>, dim3(rows), dim3(256), 0, s, q, N, H, codes, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // Exclusive scan over (head, code, copy): head h's positions start at h*N.
+  e = launch_exclusive_scan(counts, cursor, nb, aux, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lsh_place_kernel, dim3(rows), dim3(256), 0, s, codes, N, H, cursor, perm);
+  *perm_out = perm;
+  return hipGetLastError();
+}
+
+hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s) {
+  const int kp = scan_list_len(args.topk);
+  if (d == 32) return launch_scan_d<32>(kp, args, s);
+  if (d == 64) return launch_scan_d<64>(kp, args, s);
   return hipErrorInvalidValue;
 }
 

@@ -19,20 +19,23 @@
 //    of exact bf16 products).  Lane l holds query l%32 and 16 of the 32 keys,
 //    so each lane sees a private half of every query's key stream, in
 //    ascending key order.
-//  * Two passes.  The threshold pass keeps, per lane and query, the top-k of
-//    the maxima of SCAN_CHUNKS consecutive key ranges (uniform, lockstep
-//    insertions); these maxima are scores of distinct keys, so the k-th
-//    largest over both halves is a lower bound T of the query's k-th score.
+//  * Two passes.  The threshold pass scores every fourth chunk only and
+//    keeps, per lane and query, the top-k of the maxima of SCAN_CHUNKS
+//    consecutive ranges of those keys (uniform, lockstep insertions); these
+//    maxima are scores of distinct keys, so the k-th largest over both halves
+//    is a lower bound T of the query's k-th score.
 //    The selection pass then runs the exact running top-k seeded with
 //    next_down(T): a block of scores is rejected with a max tree and one
 //    compare, rare hits go to a per-lane LDS candidate buffer, and buffers
 //    are drained in lockstep into per-lane register lists.  At the end the
 //    two half-lists of a query (lanes l, l^32) are merged by rank with the
 //    tie rule (score descending, id ascending).
-//  * One graph: a persistent grid of exactly the co-resident workgroups, each
-//    taking an equal contiguous range of query blocks (no partial last round),
-//    with logical ids permuted so that the workgroups of one XCD share a head
-//    and its keys in that XCD's L2.  Batched graphs: one workgroup per planned
+//  * One graph: each head's queries are first grouped by a sign-random-
+//    projection code, so a wavefront's 32 queries tend to share their
+//    candidate keys.  A persistent grid of exactly the co-resident
+//    workgroups, each taking an equal contiguous range of query blocks (no
+//    partial last round), with logical ids permuted so that the workgroups of
+//    one XCD share a head and its keys in that XCD's L2.  Batched graphs: one workgroup per planned
 //    sub-tile; sub-blocks past a graph's last key are skipped.
 #include "kmip_internal.h"
 
@@ -51,12 +54,18 @@ static_assert(SUB_ROWS == SCAN_QT, "sub-tile rows");
 #ifndef KMIP_SCAN_BATCH
 #define KMIP_SCAN_BATCH 2
 #endif
+#ifndef KMIP_PRE_SAMPLE
+#define KMIP_PRE_SAMPLE 4
+#endif
 template <bool PRE> struct PassCfg;
+// SAMPLE: the threshold pass scores every SAMPLE-th chunk only.  Any subset
+// of a query's keys yields a valid lower bound of its k-th score; a sparser
+// subset gives a looser bound, i.e. more candidates in the selection pass.
 template <> struct PassCfg<true> {
-  static constexpr int LPW = 4, NBUF = 2, BATCH = KMIP_SCAN_BATCH;
+  static constexpr int LPW = 4, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = KMIP_PRE_SAMPLE;
 };
 template <> struct PassCfg<false> {
-  static constexpr int LPW = 2, NBUF = 2, BATCH = KMIP_SCAN_BATCH;
+  static constexpr int LPW = 2, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = 1;
 };
 
 // Chunk layout in LDS ("operand order"): the chunk is a sequence of 1 KB
@@ -73,6 +82,7 @@ struct ScanShape {
   static constexpr int ROWB = 2 * D;                // bytes per key row
   static constexpr int LPW = PassCfg<PRE>::LPW;     // operand blocks loaded per wave
   static constexpr int NBUF = PassCfg<PRE>::NBUF;   // LDS ring depth
+  static constexpr int SAMPLE = PassCfg<PRE>::SAMPLE;  // chunk stride
   static constexpr int CHUNK_BYTES = 1024 * SCAN_WAVES * LPW;
   static constexpr int TK = CHUNK_BYTES / ROWB;      // keys per chunk
   static constexpr int SUBT = TK / 32;               // 32-key sub-blocks per chunk
@@ -136,14 +146,14 @@ struct Scanner {
   int32_t* out_idx;
   float* out_score;
 
-  // Direct global->LDS load of chunk c into ring slot c % NBUF: wave w fills
+  // Direct global->LDS load of chunk c into ring slot `slot`: wave w fills
   // operand blocks w + i * SCAN_WAVES (i < LPW), lane l writing 16 bytes at
   // l * 16 of the block.  The address is a per-chunk uniform base (SGPRs)
   // plus a 32-bit lane offset; rows past the graph's last key re-read the
   // last key.  Written as inline assembly so that the compiler does not treat
   // ring reads as aliasing the loads in flight: completion is tracked by the
   // explicit vmcnt waits of the chunk loop.  The instruction writes no VGPR.
-  __device__ __forceinline__ void issue(const SubTile& t, int c, int wave, int lane) {
+  __device__ __forceinline__ void issue(const SubTile& t, int c, int slot, int wave, int lane) {
     const int64_t first = t.kb + (int64_t)c * S::TK;
     const int64_t left = t.ke - first;
     const int rmax = (int)(left < S::TK ? left : S::TK) - 1;
@@ -156,7 +166,7 @@ struct Scanner {
       const unsigned off =
           (unsigned)(row < rmax ? row : rmax) * (unsigned)(H * S::ROWB) + (unsigned)piece * 16u;
       const unsigned lds =
-          kbuf_lds + (unsigned)((c % S::NBUF) * S::CHUNK_BYTES + blk * 1024);
+          kbuf_lds + (unsigned)(slot * S::CHUNK_BYTES + blk * 1024);
       asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
                    "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                    : "memory");
@@ -179,6 +189,8 @@ struct Scanner {
     const int lrow = lane & 31, lhalf = lane >> 5;
     const int64_t nkeys = t.ke - t.kb;
     const int nchunks = (int)((nkeys + S::TK - 1) / S::TK);
+    // Chunks scored by this pass: c = j * SAMPLE for j < nproc.
+    const int nproc = (nchunks + S::SAMPLE - 1) / S::SAMPLE;
 
     // The ring may still be read by slower waves of the previous sub-tile.
     __syncthreads();
@@ -227,10 +239,13 @@ struct Scanner {
     // issued, so the chunk loop waits on key loads only.
     __builtin_amdgcn_s_waitcnt(0x0f70);
 #pragma unroll
-    for (int c = 0; c < S::NBUF - 1; ++c)
-      if (c < nchunks) issue(t, c, wave, lane);
+    for (int j = 0; j < S::NBUF - 1; ++j)
+      if (j < nproc) issue(t, j * S::SAMPLE, j, wave, lane);
 
-    const int nsub = (int)((nkeys + 31) / 32);
+    // Scored sub-blocks: all of the first nproc - 1 scored chunks, plus the
+    // part of the last one that holds keys.
+    const int last_keys = (int)(nkeys - (int64_t)(nproc - 1) * S::SAMPLE * S::TK);
+    const int nsub = (nproc - 1) * S::SUBT + ((last_keys < S::TK ? last_keys : S::TK) + 31) / 32;
     const int spc = (nsub + SCAN_CHUNKS - 1) / SCAN_CHUNKS;   // sub-blocks per chunk
     int cleft = spc;                                          // sub-blocks left in chunk
     int cnt = 0;
@@ -255,20 +270,22 @@ struct Scanner {
       cnt = 0;
     };
 
-    for (int c = 0; c < nchunks; ++c) {
+    for (int j = 0; j < nproc; ++j) {
+      const int c = j * S::SAMPLE;
       // Chunk c's loads (LPW instructions per wavefront) were followed by
       // those of at most NBUF - 2 later chunks.
       if constexpr (S::NBUF == 3) {
         static_assert(S::LPW <= 15, "vmcnt field");
-        if (c + 1 < nchunks) __builtin_amdgcn_s_waitcnt(0x0f70 | S::LPW);
+        if (j + 1 < nproc) __builtin_amdgcn_s_waitcnt(0x0f70 | S::LPW);
         else __builtin_amdgcn_s_waitcnt(0x0f70);
       } else {
         __builtin_amdgcn_s_waitcnt(0x0f70);
       }
       __syncthreads();
-      if (c + S::NBUF - 1 < nchunks) issue(t, c + S::NBUF - 1, wave, lane);
+      if (j + S::NBUF - 1 < nproc)
+        issue(t, (j + S::NBUF - 1) * S::SAMPLE, (j + S::NBUF - 1) % S::NBUF, wave, lane);
       if (!wave_active) continue;
-      const unsigned char* kc = kbuf + (c % S::NBUF) * S::CHUNK_BYTES;
+      const unsigned char* kc = kbuf + (j % S::NBUF) * S::CHUNK_BYTES;
       const int crel = c * S::TK;                 // first key of the chunk, graph-relative
       const int nk = (int)nkeys;
       const bool partial = crel + S::TK > nk;
@@ -318,7 +335,7 @@ struct Scanner {
                           fmaxf(fmaxf(fmaxf(s[b][8], s[b][9]), fmaxf(s[b][10], s[b][11])),
                                 fmaxf(fmaxf(s[b][12], s[b][13]),
                                       fmaxf(fmaxf(s[b][14], s[b][15]), cm[b]))));
-          const int ti = c * S::SUBT + st;            // sub-block index, uniform
+          const int ti = j * S::SUBT + st;            // scored sub-block index, uniform
           if (--cleft == 0 || ti + 1 == nsub) {
             cleft = spc;
 #pragma unroll

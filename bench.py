@@ -102,7 +102,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU's clocks settle over the first ~100 ms of sustained work.
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-nodes", type=int, default=16384,
                     help="query nodes in the CPU oracle sample (0 skips the CPU baseline)")

@@ -25,7 +25,7 @@ constexpr int SCAN_CHUNKS = 32;                   // threshold pass: chunks per 
 constexpr int SEG_SLICE = 64;
 // Radix sort: elements per block tile, digit width.
 constexpr int SORT_THREADS = 256;
-constexpr int SORT_ITEMS = 16;
+constexpr int SORT_ITEMS = 8;
 constexpr int SORT_TILE = SORT_THREADS * SORT_ITEMS;
 constexpr int SORT_BITS = 8;
 constexpr int SORT_BINS = 1 << SORT_BITS;

@@ -321,25 +321,58 @@ __global__ __launch_bounds__(256) void segreduce_kernel(
     }
   };
 
-  for (int64_t t = s0; t < s1; ++t) {
-    const uint32_t key = skeys[t];
-    if (key != cur) {
-      flush(cur, run0, t);
+  // The slice's keys, pair ids and (p, ds) are read once, coalesced: lane l
+  // of the group holds pairs s0 + 16 i + l.  The loop then takes them by
+  // shuffles and requests the q and dO rows of four pairs at a time.
+  constexpr int PER_LANE = SEG_SLICE / 16;
+  const int n = (int)(s1 - s0);
+  uint32_t mk[PER_LANE], mv[PER_LANE];
+  float mpx[PER_LANE], mpy[PER_LANE];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ak[e] = av[e] = 0.0;
-      cur = key;
-      run0 = t;
+  for (int i = 0; i < PER_LANE; ++i) {
+    const int u = i * 16 + l16;
+    const bool ok = u < n;
+    mk[i] = ok ? skeys[s0 + u] : 0u;
+    mv[i] = ok ? svals[s0 + u] : 0u;
+    const float2 pr = ok ? spay[s0 + u] : make_float2(0.f, 0.f);
+    mpx[i] = pr.x;
+    mpy[i] = pr.y;
+  }
+#pragma unroll
+  for (int g4 = 0; g4 < SEG_SLICE; g4 += 4) {
+    if (g4 >= n) break;
+    uint32_t key[4];
+    float px[4], py[4], qx[4][EPL], gx[4][EPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ip = g4 + u, i = ip / 16, src = ip % 16;
+      key[u] = __shfl(mk[i], src, 16);
+      const uint32_t pid = __shfl(mv[i], src, 16);
+      px[u] = __shfl(mpx[i], src, 16);
+      py[u] = __shfl(mpy[i], src, 16);
+      if (ip < n) {
+        const int64_t row = pid / (uint32_t)topk;
+        load_bf16_cols<EPL>(Q + row * D + l16 * EPL, qx[u]);
+        load_f32_cols<EPL>(dout + row * D + l16 * EPL, gx[u]);
+      }
     }
-    const uint32_t pid = svals[t];
-    const int64_t row = pid / (uint32_t)topk;
-    const float2 pr = spay[t];
-    float qx[EPL], gx[EPL];
-    load_bf16_cols<EPL>(Q + row * D + l16 * EPL, qx);
-    load_f32_cols<EPL>(dout + row * D + l16 * EPL, gx);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      ak[e] = fma((double)pr.y, (double)qx[e], ak[e]);
-      av[e] = fma((double)pr.x, (double)gx[e], av[e]);
+    for (int u = 0; u < 4; ++u) {
+      const int ip = g4 + u;
+      if (ip >= n) break;
+      const int64_t t = s0 + ip;
+      if (key[u] != cur) {
+        flush(cur, run0, t);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ak[e] = av[e] = 0.0;
+        cur = key[u];
+        run0 = t;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        ak[e] = fma((double)py[u], (double)qx[u][e], ak[e]);
+        av[e] = fma((double)px[u], (double)gx[u][e], av[e]);
+      }
     }
   }
   flush(cur, run0, s1);

@@ -28,9 +28,16 @@ kmip_status_t check_shape(int64_t N, int H, int d, int topk, int num_graphs) {
   return KMIP_OK;
 }
 
-// Forward workspace: per-row score thresholds [N*H] fp32, then (batched
-// graphs only) the tile plan.
-size_t forward_ws(int64_t N, int H, int num_graphs) {
+// Forward workspace: per-row score thresholds [N*H] fp32; then the tile plan
+// (batched graphs) or the query order (one graph); then, for lists longer
+// than 16, the candidate arrays and their counts.
+size_t collect_ws(int64_t N, int H, int topk) {
+  if (scan_list_len(topk) <= 16) return 0;
+  return align256((size_t)2 * COLLECT_CAP * N * H * sizeof(uint2)) +
+         align256((size_t)2 * N * H * sizeof(int32_t));
+}
+
+size_t forward_ws(int64_t N, int H, int topk, int num_graphs) {
   size_t b = align256((size_t)N * H * sizeof(float));
   if (num_graphs > 1) {
     const int64_t tiles = scan_max_tiles(N, num_graphs);
@@ -38,7 +45,7 @@ size_t forward_ws(int64_t N, int H, int num_graphs) {
   } else {
     b += query_order_bytes(N, H);
   }
-  return b;
+  return b + collect_ws(N, H, topk);
 }
 
 size_t backward_ws(int64_t N, int H, int d, int topk) {
@@ -69,7 +76,7 @@ int kmip_version(void) { return kVersion; }
 
 size_t kmip_forward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
   if (check_shape(N, H, d, topk, num_graphs) != KMIP_OK) return 0;
-  return forward_ws(N, H, num_graphs);
+  return forward_ws(N, H, topk, num_graphs);
 }
 
 size_t kmip_backward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
@@ -88,7 +95,7 @@ kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, in
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(topk_idx, 4) || !aligned(topk_score, 4))
     return KMIP_ERR_INVALID_VALUE;
   const bool single = single_graph(graph_offsets, num_graphs);
-  const size_t need = forward_ws(N, H, single ? 0 : num_graphs);
+  const size_t need = forward_ws(N, H, topk, single ? 0 : num_graphs);
   if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
 
@@ -109,8 +116,10 @@ kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, in
   if (!single) {
     int32_t* tile_start = reinterpret_cast<int32_t*>(w);
     int2* tiles = reinterpret_cast<int2*>(w + align256((size_t)(num_graphs + 1) * 4));
-    st = launch_status(launch_tile_plan(graph_offsets, num_graphs, max_tiles, tile_start,
-                                        tiles, s));
+    w += align256((size_t)(num_graphs + 1) * 4) + align256((size_t)max_tiles * sizeof(int2));
+    const int tile_rows = scan_waves(scan_list_len(topk)) * SCAN_QPW;
+    st = launch_status(launch_tile_plan(graph_offsets, num_graphs, max_tiles, tile_rows,
+                                        tile_start, tiles, s));
     if (st != KMIP_OK) return st;
     a.offsets = graph_offsets;
     a.tiles = tiles;
@@ -119,6 +128,13 @@ kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, in
     st = launch_status(launch_query_order(a.q, N, H, d, w, &perm, s));
     if (st != KMIP_OK) return st;
     a.perm = perm;
+    w += query_order_bytes(N, H);
+  }
+  if (collect_ws(N, H, topk) > 0) {
+    a.cand = reinterpret_cast<uint2*>(w);
+    w += align256((size_t)2 * COLLECT_CAP * N * H * sizeof(uint2));
+    a.cand_cnt = reinterpret_cast<int32_t*>(w);
+    a.cap = COLLECT_CAP;
   }
   return launch_status(launch_score_topk(a, d, s));
 }

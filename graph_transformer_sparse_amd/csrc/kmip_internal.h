@@ -15,11 +15,13 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------- tiling
 // Score scan: a workgroup of SCAN_WAVES wavefronts, each owning 32 query rows
 // of one head (one 32x32 MFMA output block: keys x queries).
-constexpr int SCAN_WAVES = 16;
+constexpr int SCAN_WAVES = 16;                    // lists of up to 16 entries
+constexpr int SCAN_WAVES_LONG = 8;                // longer lists: 2 waves per SIMD
 constexpr int SCAN_QPW = 32;
-constexpr int SCAN_QT = SCAN_WAVES * SCAN_QPW;   // queries per workgroup tile
+constexpr int SCAN_QT_MIN = SCAN_WAVES_LONG * SCAN_QPW;   // smallest planned tile
 constexpr int SCAN_CAP = 8;                       // per-lane candidate buffer entries
 constexpr int SCAN_CHUNKS = 32;                   // threshold pass: chunks per lane
+constexpr int COLLECT_CAP = 128;                  // candidates per row and lane half
 
 // Key-side backward: consecutive sorted (key, pair) positions per slice.
 constexpr int SEG_SLICE = 64;
@@ -40,18 +42,23 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Smallest list length the scan kernel is instantiated for that holds k.
 int scan_list_len(int topk);
 
-// Maximum number of query tiles for N nodes in num_graphs graphs.
+// Wavefronts per scan workgroup for a list length: long register lists need
+// the VGPR budget of two wavefronts per SIMD.
+constexpr int scan_waves(int kp) { return kp <= 16 ? SCAN_WAVES : SCAN_WAVES_LONG; }
+
+// Maximum number of query tiles for N nodes in num_graphs graphs (for the
+// smallest tile).
 inline int64_t scan_max_tiles(int64_t N, int num_graphs) {
-  return ceil_div(N, SCAN_QT) + (num_graphs > 1 ? num_graphs : 0);
+  return ceil_div(N, SCAN_QT_MIN) + (num_graphs > 1 ? num_graphs : 0);
 }
 
 // ---------------------------------------------------------------- launchers
 // All return hipSuccess or the first launch error.  No allocation, no sync.
 
-// Ragged tile plan: tiles[t] = (graph, first query) for t < total, (-1, 0)
-// beyond; tile_start is [B+1] scratch.
+// Ragged tile plan: tiles of tile_rows queries, tiles[t] = (graph, first
+// query) for t < total, (-1, 0) beyond; tile_start is [B+1] scratch.
 hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_tiles,
-                            int32_t* tile_start, int2* tiles, hipStream_t s);
+                            int tile_rows, int32_t* tile_start, int2* tiles, hipStream_t s);
 
 // Score scan in two passes: a threshold pass writing a per-row lower bound
 // of the k-th score into thr[N*H], then the exact running top-k seeded with
@@ -69,6 +76,11 @@ struct ScanArgs {
   float* thr;
   int32_t* idx;
   float* score;
+  // Lists longer than 16: per-row candidate arrays [2 halves][cap][N*H] of
+  // (score bits, key id) and their counts [N*H][2].
+  uint2* cand;
+  int32_t* cand_cnt;
+  int cap;
 };
 hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s);
 

@@ -44,8 +44,6 @@ namespace {
 
 constexpr float kInf = __builtin_inff();
 constexpr int QB = 1;                       // query blocks of 32 per wavefront
-constexpr int SUB_ROWS = SCAN_WAVES * QB * 32;
-static_assert(SUB_ROWS == SCAN_QT, "sub-tile rows");
 // Per pass: LDS chunk size in 16 KB units (LPW: 1 KB loads per wavefront and
 // chunk), ring depth, and sub-blocks per batch (LDS reads, then MFMAs, then
 // scores).  Large chunks amortise the workgroup barrier of every chunk; the
@@ -57,14 +55,23 @@ static_assert(SUB_ROWS == SCAN_QT, "sub-tile rows");
 #ifndef KMIP_PRE_SAMPLE
 #define KMIP_PRE_SAMPLE 4
 #endif
-template <bool PRE> struct PassCfg;
-// SAMPLE: the threshold pass scores every SAMPLE-th chunk only.  Any subset
-// of a query's keys yields a valid lower bound of its k-th score; a sparser
-// subset gives a looser bound, i.e. more candidates in the selection pass.
-template <> struct PassCfg<true> {
+// Scan modes.  THRESH: per-row lower bound T of the k-th score.  SELECT:
+// exact running top-k in per-lane register lists.  COLLECT (lists longer
+// than 16): every key scoring above next_down(T) is appended to a per-row
+// candidate array, and a second kernel selects the top-k from it; rows whose
+// arrays overflow are then recomputed by SELECT.
+constexpr int M_THRESH = 0, M_SELECT = 1, M_COLLECT = 2;
+template <int MODE> struct PassCfg;
+// SAMPLE: THRESH scores every SAMPLE-th chunk only.  Any subset of a
+// query's keys yields a valid lower bound of its k-th score; a sparser subset
+// gives a looser bound, i.e. more candidates in the later pass.
+template <> struct PassCfg<M_THRESH> {
   static constexpr int LPW = 4, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = KMIP_PRE_SAMPLE;
 };
-template <> struct PassCfg<false> {
+template <> struct PassCfg<M_SELECT> {
+  static constexpr int LPW = 2, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = 1;
+};
+template <> struct PassCfg<M_COLLECT> {
   static constexpr int LPW = 2, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = 1;
 };
 
@@ -76,17 +83,17 @@ template <> struct PassCfg<false> {
 // each operand as one contiguous 1 KB ds_read_b128 (no bank conflicts), and
 // the direct global->LDS load that fills a block writes it in the same lane
 // order.
-template <int D, bool PRE>
+template <int D, int MODE, int W>
 struct ScanShape {
   static constexpr int NM = D / 16;                 // K=16 MFMAs per 32x32 block
   static constexpr int ROWB = 2 * D;                // bytes per key row
-  static constexpr int LPW = PassCfg<PRE>::LPW;     // operand blocks loaded per wave
-  static constexpr int NBUF = PassCfg<PRE>::NBUF;   // LDS ring depth
-  static constexpr int SAMPLE = PassCfg<PRE>::SAMPLE;  // chunk stride
-  static constexpr int CHUNK_BYTES = 1024 * SCAN_WAVES * LPW;
+  static constexpr int LPW = PassCfg<MODE>::LPW;     // operand blocks loaded per wave
+  static constexpr int NBUF = PassCfg<MODE>::NBUF;   // LDS ring depth
+  static constexpr int SAMPLE = PassCfg<MODE>::SAMPLE;  // chunk stride
+  static constexpr int CHUNK_BYTES = 1024 * W * LPW;
   static constexpr int TK = CHUNK_BYTES / ROWB;      // keys per chunk
   static constexpr int SUBT = TK / 32;               // 32-key sub-blocks per chunk
-  static_assert(SUBT * NM == SCAN_WAVES * LPW, "LPW operand blocks per wavefront");
+  static_assert(SUBT * NM == W * LPW, "LPW operand blocks per wavefront");
   static_assert(NBUF == 2 || NBUF == 3, "ring depth");
 };
 
@@ -131,12 +138,19 @@ struct SubTile {
   int64_t kb, ke;     // key range of the graph
 };
 
-template <int D, int KP, bool PRE>
+template <int D, int KP, int MODE>
 struct Scanner {
-  using S = ScanShape<D, PRE>;
+  static constexpr bool PRE = MODE == M_THRESH;
+  static constexpr int W = scan_waves(KP);    // wavefronts per workgroup
+  using S = ScanShape<D, MODE, W>;
+  // Chunk stride of this pass.  Long lists take a denser sample: their
+  // candidates must fit the per-row arrays of the collecting pass.
+  static constexpr int SAMPLE = PRE && KP > 16 ? 2 : S::SAMPLE;
   unsigned char* kbuf;        // S::NBUF chunks (read side)
   unsigned kbuf_lds;          // LDS byte address of kbuf (direct-load side)
-  uint2* cbuf;                // per-lane candidate buffers (selection pass)
+  uint2* cbuf;                // per-lane candidate buffers (SELECT)
+  int* wg_flag;               // one LDS word (SELECT restricted to flagged rows)
+  const ScanArgs& a;
   const uint16_t* Q;
   const uint16_t* K;
   const int32_t* perm;        // query order per head, [H][N] (one graph), or null
@@ -147,7 +161,7 @@ struct Scanner {
   float* out_score;
 
   // Direct global->LDS load of chunk c into ring slot `slot`: wave w fills
-  // operand blocks w + i * SCAN_WAVES (i < LPW), lane l writing 16 bytes at
+  // operand blocks w + i * W (i < LPW), lane l writing 16 bytes at
   // l * 16 of the block.  The address is a per-chunk uniform base (SGPRs)
   // plus a 32-bit lane offset; rows past the graph's last key re-read the
   // last key.  Written as inline assembly so that the compiler does not treat
@@ -160,7 +174,7 @@ struct Scanner {
     const uint16_t* base = K + (first * H + t.h) * D;
 #pragma unroll
     for (int i = 0; i < S::LPW; ++i) {
-      const int blk = wave + i * SCAN_WAVES;
+      const int blk = wave + i * W;
       const int row = (blk / S::NM) * 32 + (lane & 31);
       const int piece = 2 * (blk % S::NM) + (lane >> 5);
       const unsigned off =
@@ -190,7 +204,7 @@ struct Scanner {
     const int64_t nkeys = t.ke - t.kb;
     const int nchunks = (int)((nkeys + S::TK - 1) / S::TK);
     // Chunks scored by this pass: c = j * SAMPLE for j < nproc.
-    const int nproc = (nchunks + S::SAMPLE - 1) / S::SAMPLE;
+    const int nproc = (nchunks + SAMPLE - 1) / SAMPLE;
 
     // The ring may still be read by slower waves of the previous sub-tile.
     __syncthreads();
@@ -211,7 +225,26 @@ struct Scanner {
 #pragma unroll
       for (int m = 0; m < S::NM; ++m) qb[b][m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
     }
-    const bool wave_active = bact[0];
+    // Rows this call writes.  SELECT with candidate counts (after COLLECT)
+    // recomputes only the rows whose candidate arrays overflowed and skips
+    // sub-tiles that have none.
+    bool keep[QB];
+    bool wave_rows = bact[0];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) keep[b] = qvalid[b];
+    if constexpr (MODE == M_SELECT && KP > 16) {
+      if (a.cand_cnt != nullptr) {
+        const int64_t r = qrow[0] * H + t.h;
+        keep[0] = qvalid[0] && (a.cand_cnt[2 * r] > a.cap || a.cand_cnt[2 * r + 1] > a.cap);
+        wave_rows = __ballot(keep[0]) != 0ull;
+        if (tid == 0) *wg_flag = 0;
+        __syncthreads();
+        if (wave_rows && lane == 0) *wg_flag = 1;
+        __syncthreads();
+        if (*wg_flag == 0) return;            // uniform over the workgroup
+      }
+    }
+    const bool wave_active = wave_rows;
     const int aoff = lane * 16;
 
     // Lists: slots [0, KP-topk) hold +inf sentinels that nothing displaces, so
@@ -240,16 +273,30 @@ struct Scanner {
     __builtin_amdgcn_s_waitcnt(0x0f70);
 #pragma unroll
     for (int j = 0; j < S::NBUF - 1; ++j)
-      if (j < nproc) issue(t, j * S::SAMPLE, j, wave, lane);
+      if (j < nproc) issue(t, j * SAMPLE, j, wave, lane);
 
     // Scored sub-blocks: all of the first nproc - 1 scored chunks, plus the
     // part of the last one that holds keys.
-    const int last_keys = (int)(nkeys - (int64_t)(nproc - 1) * S::SAMPLE * S::TK);
+    const int last_keys = (int)(nkeys - (int64_t)(nproc - 1) * SAMPLE * S::TK);
     const int nsub = (nproc - 1) * S::SUBT + ((last_keys < S::TK ? last_keys : S::TK) + 31) / 32;
-    const int spc = (nsub + SCAN_CHUNKS - 1) / SCAN_CHUNKS;   // sub-blocks per chunk
+    // Key ranges per lane half: a query's bound is the k-th largest of
+    // 2 * NCH range maxima, so long lists need proportionally more ranges.
+    constexpr int NCH = KP <= 16 ? SCAN_CHUNKS : 4 * KP;
+    const int spc = (nsub + NCH - 1) / NCH;                   // sub-blocks per range
     int cleft = spc;                                          // sub-blocks left in chunk
     int cnt = 0;
     uint2* cb = cbuf + wave * SCAN_CAP * 64 + lane;           // entry c at cb[c * 64]
+    // COLLECT: candidates of row r, this lane's half, go to
+    // cand[(lhalf * cap + n) * NH + r] for n < cap; ccnt keeps counting past
+    // cap so that overflow is visible.
+    const int64_t NH = N * H;
+    int ccnt[QB];
+    int64_t crow[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      ccnt[b] = 0;
+      crow[b] = qrow[b] * H + t.h;
+    }
 
     auto drain = [&]() __attribute__((always_inline)) {
       for (int c = 0; __ballot(c < cnt) != 0ull; ++c) {
@@ -271,7 +318,7 @@ struct Scanner {
     };
 
     for (int j = 0; j < nproc; ++j) {
-      const int c = j * S::SAMPLE;
+      const int c = j * SAMPLE;
       // Chunk c's loads (LPW instructions per wavefront) were followed by
       // those of at most NBUF - 2 later chunks.
       if constexpr (S::NBUF == 3) {
@@ -283,7 +330,7 @@ struct Scanner {
       }
       __syncthreads();
       if (j + S::NBUF - 1 < nproc)
-        issue(t, (j + S::NBUF - 1) * S::SAMPLE, (j + S::NBUF - 1) % S::NBUF, wave, lane);
+        issue(t, (j + S::NBUF - 1) * SAMPLE, (j + S::NBUF - 1) % S::NBUF, wave, lane);
       if (!wave_active) continue;
       const unsigned char* kc = kbuf + (j % S::NBUF) * S::CHUNK_BYTES;
       const int crel = c * S::TK;                 // first key of the chunk, graph-relative
@@ -293,7 +340,7 @@ struct Scanner {
       // Sub-blocks are processed in batches of BS: all LDS reads of the
       // batch, then all its MFMAs (independent accumulation chains), then the
       // scores, so a wavefront keeps several MFMAs in flight.
-      constexpr int BS = PassCfg<PRE>::BATCH < S::SUBT ? PassCfg<PRE>::BATCH : S::SUBT;
+      constexpr int BS = PassCfg<MODE>::BATCH < S::SUBT ? PassCfg<MODE>::BATCH : S::SUBT;
       static_assert(S::SUBT % BS == 0, "batches tile the chunk");
       floatx16_t acc[BS][QB];
       bf16x8_t areg[BS][S::NM];
@@ -343,6 +390,38 @@ struct Scanner {
               if (cm[b] > ls[b][KP - 1]) value_insert<KP>(ls[b], cm[b]);
               cm[b] = -kInf;
             }
+          }
+        } else if constexpr (MODE == M_COLLECT) {
+          float g[QB][4], mx[QB];
+#pragma unroll
+          for (int b = 0; b < QB; ++b) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+              g[b][qq] = fmaxf(fmaxf(s[b][4 * qq], s[b][4 * qq + 1]),
+                               fmaxf(s[b][4 * qq + 2], s[b][4 * qq + 3]));
+            mx[b] = fmaxf(fmaxf(g[b][0], g[b][1]), fmaxf(g[b][2], g[b][3]));
+          }
+          bool hit = false;
+#pragma unroll
+          for (int b = 0; b < QB; ++b) hit = hit || (mx[b] > thr[b]);
+          if (__ballot(hit) != 0ull) {
+#pragma unroll
+            for (int b = 0; b < QB; ++b)
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                if (__ballot(g[b][qq] > thr[b]) != 0ull) {
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) {
+                    const float sv = s[b][4 * qq + r];
+                    if (sv > thr[b]) {
+                      if (ccnt[b] < a.cap)
+                        a.cand[(int64_t)(lhalf * a.cap + ccnt[b]) * NH + crow[b]] =
+                            make_uint2(__float_as_uint(sv), (unsigned)(key0 + 8 * qq + r));
+                      ++ccnt[b];
+                    }
+                  }
+                }
+              }
           }
         } else {
           float g[QB][4], mx[QB];
@@ -414,6 +493,10 @@ struct Scanner {
           if (i >= nsent && ps[i] > ls[b][KP - 1]) value_insert<KP>(ls[b], ps[i]);
         if (qvalid[b] && lhalf == 0) thr_buf[qrow[b] * H + t.h] = ls[b][KP - 1];
       }
+    } else if constexpr (MODE == M_COLLECT) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        if (qvalid[b]) a.cand_cnt[2 * crow[b] + lhalf] = ccnt[b];
     } else {
       drain();
       // Merge the two half-lists of each query by rank: live entry i of my
@@ -430,7 +513,7 @@ struct Scanner {
           ps[i] = __shfl_xor(ls[b][i], 32);
           pj[i] = __shfl_xor(lj[b][i], 32);
         }
-        if (qvalid[b]) {
+        if (keep[b]) {
           int32_t* oi = out_idx + (qrow[b] * H + t.h) * topk;
           float* os = out_score + (qrow[b] * H + t.h) * topk;
 #pragma unroll
@@ -460,19 +543,22 @@ struct Scanner {
 // Persistent grid for one graph: nwg workgroups split the H * nbph query
 // blocks (32 rows each) into equal contiguous ranges.  Batched graphs: one
 // workgroup per (planned tile, head).
-template <int D, int KP, bool PRE>
-__global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(ScanArgs a, int nwg) {
+template <int D, int KP, int MODE>
+__global__ __launch_bounds__(scan_waves(KP) * 64) void score_topk_kernel(ScanArgs a, int nwg) {
   const int64_t N = a.N;
   const int H = a.H;
   const int2* tiles = a.tiles;
   const int32_t* offsets = a.offsets;
-  using S = ScanShape<D, PRE>;
+  constexpr int W = scan_waves(KP);
+  constexpr int SUB_ROWS = W * QB * 32;
+  using S = ScanShape<D, MODE, W>;
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[S::NBUF * S::CHUNK_BYTES];
-  __shared__ __attribute__((aligned(16))) uint2 cbuf[PRE ? 1 : SCAN_WAVES * SCAN_CAP * 64];
+  __shared__ __attribute__((aligned(16))) uint2 cbuf[MODE == M_SELECT ? W * SCAN_CAP * 64 : 1];
+  __shared__ int wg_flag;
   const unsigned kbuf_lds =
       (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kbuf;
-  Scanner<D, KP, PRE> sc{kbuf,  kbuf_lds, cbuf,   a.q,   a.k,      a.perm,
-                         a.N,   a.H,      a.topk, a.thr, a.idx,    a.score};
+  Scanner<D, KP, MODE> sc{kbuf, kbuf_lds, cbuf,   &wg_flag, a,     a.q,   a.k,
+                          a.perm, a.N,    a.H,    a.topk,   a.thr, a.idx, a.score};
   // Query blocks [b, be) of the flattened (head, 32-row block) space for one
   // graph; a single planned sub-tile for batched graphs.
   const int64_t nbph = (N + 31) / 32;
@@ -505,7 +591,7 @@ __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(ScanArgs a,
       const int h = (int)(b / nbph);
       const int64_t nb0 = b % nbph;
       const int64_t rem = be - b;
-      const int64_t nst = (rem + SCAN_WAVES * QB - 1) / (SCAN_WAVES * QB);
+      const int64_t nst = (rem + W * QB - 1) / (W * QB);
       int64_t n = (rem + nst - 1) / nst;
       n = n < nbph - nb0 ? n : nbph - nb0;
       st = SubTile{h, nb0 * 32, (nb0 + n) * 32 < N ? (nb0 + n) * 32 : N, 0, N};
@@ -521,9 +607,9 @@ __global__ __launch_bounds__(SCAN_WAVES * 64) void score_topk_kernel(ScanArgs a,
 // ------------------------------------------------------------------ tile plan
 constexpr int PLAN_THREADS = 1024;
 
-// One block: tile_start[b] = sum over earlier graphs of ceil(n_b / SCAN_QT).
+// One block: tile_start[b] = sum over earlier graphs of ceil(n_b / tile_rows).
 __global__ __launch_bounds__(PLAN_THREADS) void tile_count_scan_kernel(
-    const int32_t* __restrict__ offsets, int B, int32_t* __restrict__ tile_start) {
+    const int32_t* __restrict__ offsets, int B, int tile_rows, int32_t* __restrict__ tile_start) {
   __shared__ int32_t buf[PLAN_THREADS];
   int32_t carry = 0;
   for (int base = 0; base < B; base += PLAN_THREADS) {
@@ -531,7 +617,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void tile_count_scan_kernel(
     int32_t c = 0;
     if (b < B) {
       const int32_t nb = offsets[b + 1] - offsets[b];
-      c = nb > 0 ? (nb + SCAN_QT - 1) / SCAN_QT : 0;
+      c = nb > 0 ? (nb + tile_rows - 1) / tile_rows : 0;
     }
     buf[threadIdx.x] = c;
     __syncthreads();
@@ -548,7 +634,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void tile_count_scan_kernel(
   if (threadIdx.x == 0) tile_start[B] = carry;
 }
 
-__global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B,
+__global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B, int tile_rows,
                                  const int32_t* __restrict__ tile_start, int64_t max_tiles,
                                  int2* __restrict__ tiles) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -563,45 +649,118 @@ __global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B,
     const int mid = (lo + hi + 1) >> 1;
     if (tile_start[mid] <= t) lo = mid; else hi = mid - 1;
   }
-  tiles[t] = make_int2(lo, offsets[lo] + (int)(t - tile_start[lo]) * SCAN_QT);
+  tiles[t] = make_int2(lo, offsets[lo] + (int)(t - tile_start[lo]) * tile_rows);
 }
 
 // Co-resident workgroups of a kernel on this device (one graph: the
 // persistent grid size, a multiple of 8 so each XCD gets an equal share).
 template <typename Kern>
-int resident_workgroups(Kern kern) {
+int resident_workgroups(Kern kern, int threads) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
-                                                   SCAN_WAVES * 64, 0) != hipSuccess)
+                                                   threads, 0) != hipSuccess)
     return 0;
   const int n = cus * (per_cu > 0 ? per_cu : 1);
   return n >= 8 ? n - n % 8 : 8;
 }
 
-template <int D, int KP, bool PRE>
+template <int D, int KP, int MODE>
 hipError_t launch_pass(const ScanArgs& a, hipStream_t s) {
-  auto kern = score_topk_kernel<D, KP, PRE>;
+  auto kern = score_topk_kernel<D, KP, MODE>;
+  constexpr int threads = scan_waves(KP) * 64;
   int nwg = 0;
   dim3 grid;
   if (a.tiles == nullptr) {
-    nwg = resident_workgroups(kern);
+    nwg = resident_workgroups(kern, threads);
     if (nwg <= 0) return hipErrorInvalidDevice;
     grid = dim3((unsigned)nwg);
   } else {
     grid = dim3((unsigned)(a.max_tiles * a.H));
   }
-  hipLaunchKernelGGL(kern, grid, dim3(SCAN_WAVES * 64), 0, s, a, nwg);
+  hipLaunchKernelGGL(kern, grid, dim3(threads), 0, s, a, nwg);
   return hipGetLastError();
+}
+
+// Insert (s, j) into a descending list under (score descending, id
+// ascending); candidates may come in any order.
+template <int KP>
+__device__ __forceinline__ void ordered_insert(float (&ls)[KP], int (&lj)[KP], float s, int j) {
+  bool b[KP];
+#pragma unroll
+  for (int t = 0; t < KP; ++t) b[t] = s > ls[t] || (s == ls[t] && (unsigned)j < (unsigned)lj[t]);
+#pragma unroll
+  for (int t = KP - 1; t >= 1; --t) {
+    ls[t] = b[t - 1] ? ls[t - 1] : (b[t] ? s : ls[t]);
+    lj[t] = b[t - 1] ? lj[t - 1] : (b[t] ? j : lj[t]);
+  }
+  ls[0] = b[0] ? s : ls[0];
+  lj[0] = b[0] ? j : lj[0];
+}
+
+// Top-k of each row's collected candidates, one thread per row.  Rows whose
+// arrays overflowed are left to the SELECT pass.  Empty slots hold (-inf, -1)
+// and rank after every candidate ((unsigned)-1 is the largest id); +inf
+// sentinels fill slots [0, KP - topk).
+template <int KP>
+__global__ __launch_bounds__(256) void collect_topk_kernel(ScanArgs a) {
+  const int64_t NH = a.N * a.H;
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= NH) return;
+  const int c0 = a.cand_cnt[2 * r], c1 = a.cand_cnt[2 * r + 1];
+  if (c0 > a.cap || c1 > a.cap) return;
+  const int nsent = KP - a.topk;
+  float ls[KP];
+  int lj[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    ls[i] = i < nsent ? kInf : -kInf;
+    lj[i] = -1;
+  }
+  for (int hf = 0; hf < 2; ++hf) {
+    const int n = hf ? c1 : c0;
+    const uint2* src = a.cand + (int64_t)hf * a.cap * NH + r;
+    for (int u = 0; u < n; ++u) {
+      const uint2 e = src[(int64_t)u * NH];
+      const float sv = __uint_as_float(e.x);
+      const int j = (int)e.y;
+      if (sv > ls[KP - 1] || (sv == ls[KP - 1] && (unsigned)j < (unsigned)lj[KP - 1]))
+        ordered_insert<KP>(ls, lj, sv, j);
+    }
+  }
+  int32_t* oi = a.idx + r * a.topk;
+  float* os = a.score + r * a.topk;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    if (i >= nsent) {
+      oi[i - nsent] = lj[i];
+      os[i - nsent] = lj[i] < 0 ? -kInf : ls[i];
+    }
+  }
 }
 
 template <int D, int KP>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
-  hipError_t e = launch_pass<D, KP, true>(a, s);
+  hipError_t e = launch_pass<D, KP, M_THRESH>(a, s);
   if (e != hipSuccess) return e;
-  return launch_pass<D, KP, false>(a, s);
+  if constexpr (KP > 16) {
+    // Long lists: collect candidates, select from them, then recompute the
+    // rows whose candidate arrays overflowed (that pass usually only checks
+    // the counts).
+    e = launch_pass<D, KP, M_COLLECT>(a, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(collect_topk_kernel<KP>, dim3((unsigned)ceil_div(a.N * a.H, 256)),
+                       dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_pass<D, KP, M_SELECT>(a, s);
+  } else {
+    ScanArgs b = a;
+    b.cand_cnt = nullptr;                      // SELECT writes every row
+    return launch_pass<D, KP, M_SELECT>(b, s);
+  }
 }
 
 template <int D>
@@ -700,14 +859,14 @@ int scan_list_len(int topk) {
 }
 
 hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_tiles,
-                            int32_t* tile_start, int2* tiles, hipStream_t s) {
+                            int tile_rows, int32_t* tile_start, int2* tiles, hipStream_t s) {
   hipLaunchKernelGGL(tile_count_scan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, offsets,
-                     num_graphs, tile_start);
+                     num_graphs, tile_rows, tile_start);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned blocks = (unsigned)ceil_div(max_tiles, 256);
   hipLaunchKernelGGL(tile_fill_kernel, dim3(blocks), dim3(256), 0, s, offsets, num_graphs,
-                     tile_start, max_tiles, tiles);
+                     tile_rows, tile_start, max_tiles, tiles);
   return hipGetLastError();
 }
 

@@ -106,6 +106,27 @@ def test_exact_ties_follow_ascending_id():
     assert np.array_equal(np_(idx), fw["idx"].astype(np.int32))
 
 
+@pytest.mark.parametrize("sizes,topk", [([1200], 45), ([700, 50, 400], 45), ([900], 32)])
+def test_long_lists_with_overflowing_candidates(sizes, topk):
+    """Lists longer than 16 go through per-row candidate arrays (128 per lane
+    half).  Heavily duplicated keys tie at the k-th score, so rows whose best
+    key has hundreds of copies overflow the arrays and are recomputed exactly;
+    rows whose best keys are distinct do not.  Both must match the oracle,
+    ties by ascending id."""
+    from tests.gpu_util import np_, run_forward
+    w = with_offsets(f"dup_{len(sizes)}_{topk}", sizes, heads=2, d=32, topk=topk,
+                     law="iid", seed=sum(sizes) + topk)
+    n = w.n
+    dup = np.arange(n) < (2 * n) // 3
+    w.k = w.k.copy()
+    w.k[dup] = w.k[np.arange(n)[dup] % 2]                # two key rows, many copies
+    t, out, idx, score = run_forward(w)
+    q, k, v = decode(w)
+    fw = orc.kmip_forward(q, k, v, w.offsets, w.topk)
+    assert np.array_equal(np_(idx), fw["idx"].astype(np.int32))
+    assert_rows_close(np_(out), fw["out"], "out")
+
+
 def test_full_attention_limit():
     """k >= n_b: every key of the graph is kept, so the output is full softmax
     attention (oracle pinned to torch SDPA in fp64)."""

@@ -31,6 +31,10 @@ kmip_status_t check_shape(int64_t N, int H, int d, int topk, int num_graphs) {
 // Forward workspace: per-row score thresholds [N*H] fp32; then the tile plan
 // (batched graphs) or the query order (one graph); then, for lists longer
 // than 16, the candidate arrays and their counts.
+// Grouping queries pays off only when there are many wavefronts of them;
+// small inputs skip it (and its six launches).
+bool use_query_order(int64_t N, int H) { return N * H >= 32768; }
+
 size_t collect_ws(int64_t N, int H, int topk) {
   if (scan_list_len(topk) <= 16) return 0;
   return align256((size_t)2 * COLLECT_CAP * N * H * sizeof(uint2)) +
@@ -42,7 +46,7 @@ size_t forward_ws(int64_t N, int H, int topk, int num_graphs) {
   if (num_graphs > 1) {
     const int64_t tiles = scan_max_tiles(N, num_graphs);
     b += align256((size_t)(num_graphs + 1) * 4) + align256((size_t)tiles * sizeof(int2));
-  } else {
+  } else if (use_query_order(N, H)) {
     b += query_order_bytes(N, H);
   }
   return b + collect_ws(N, H, topk);
@@ -123,7 +127,7 @@ kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, in
     if (st != KMIP_OK) return st;
     a.offsets = graph_offsets;
     a.tiles = tiles;
-  } else {
+  } else if (use_query_order(N, H)) {
     int32_t* perm = nullptr;
     st = launch_status(launch_query_order(a.q, N, H, d, w, &perm, s));
     if (st != KMIP_OK) return st;

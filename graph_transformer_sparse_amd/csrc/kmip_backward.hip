@@ -89,6 +89,32 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_aux_kernel(int32_t* __restr
   }
 }
 
+// One block scans up to SCAN_SINGLE_TILES tiles in order, carrying the sum.
+constexpr int SCAN_SINGLE_TILES = 4;
+__global__ __launch_bounds__(SCAN_THREADS) void scan_single_kernel(
+    const int32_t* __restrict__ in, int32_t* __restrict__ out, int64_t n) {
+  __shared__ int32_t sh[SCAN_THREADS / 64];
+  int32_t carry = 0;
+  for (int64_t tile = 0; tile < n; tile += SCAN_TILE_ELEMS) {
+    const int64_t base = tile + (int64_t)threadIdx.x * SCAN_ITEMS;
+    int32_t v[SCAN_ITEMS];
+    int32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < SCAN_ITEMS; ++i) {
+      v[i] = (base + i < n) ? in[base + i] : 0;
+      s += v[i];
+    }
+    int32_t tot;
+    int32_t run = block_excl_scan(s, sh, &tot) + carry;
+#pragma unroll
+    for (int i = 0; i < SCAN_ITEMS; ++i) {
+      if (base + i < n) out[base + i] = run;
+      run += v[i];
+    }
+    carry += tot;
+  }
+}
+
 __global__ __launch_bounds__(SCAN_THREADS) void scan_down_kernel(
     const int32_t* __restrict__ in, int32_t* __restrict__ out, int64_t n,
     const int32_t* __restrict__ aux) {
@@ -446,6 +472,10 @@ int64_t scan_aux_elems(int64_t n) { return ceil_div(n, SCAN_TILE_ELEMS) + 1; }
 hipError_t launch_exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* aux,
                                  hipStream_t s) {
   const int64_t nb = ceil_div(n, SCAN_TILE_ELEMS);
+  if (nb <= SCAN_SINGLE_TILES) {                 // small arrays: one launch
+    hipLaunchKernelGGL(scan_single_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, in, out, n);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(SCAN_THREADS), 0, s, in, n,
                      aux);
   hipLaunchKernelGGL(scan_aux_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, aux, nb);

@@ -117,7 +117,7 @@ def test_gps_layer_trains_one_step():
         loss = ((layer(x, offs) - target) ** 2).mean()
         loss.backward()
         opt.step()
-        losses.append(float(loss))
+        losses.append(float(loss.detach()))
     assert all(np.isfinite(losses))
     assert all(p.grad is not None and torch.isfinite(p.grad).all() for p in layer.parameters())
     idx = _np(layer.attn.last_topk_idx)

@@ -63,8 +63,9 @@ def scan_traffic(workload: str):
         if sep:
             fields[key] = val
     h = hashlib.sha256()
-    for f in ("kmip_scan.hip", "kmip_internal.h"):
-        with open(os.path.join(ROOT, "graph_transformer_sparse_amd", "csrc", f), "rb") as fh:
+    csrc = os.path.join(ROOT, "graph_transformer_sparse_amd", "csrc")
+    for f in sorted(x for x in os.listdir(csrc) if x.startswith("kmip_scan")) + ["kmip_internal.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     if fields.get("workload") != workload or fields.get("scan_source_sha256") != h.hexdigest():
         return None

@@ -14,7 +14,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkmip.so")
-SOURCES = ["kmip_scan.hip", "kmip_gather.hip", "kmip_backward.hip", "kmip_api.hip"]
+SOURCES = ["kmip_scan_d32.hip", "kmip_scan_d64.hip", "kmip_scan_d96.hip", "kmip_scan_d192.hip",
+           "kmip_scan.hip", "kmip_split.hip", "kmip_gather.hip", "kmip_backward.hip",
+           "kmip_api.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -6,7 +6,7 @@ using namespace kmip;
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -61,6 +61,93 @@ size_t backward_ws(int64_t N, int H, int d, int topk) {
 
 kmip_status_t launch_status(hipError_t e) { return e == hipSuccess ? KMIP_OK : KMIP_ERR_LAUNCH; }
 
+// fp32 entry points: the split-precision rows q3, k3 (bf16 [N*H][3d] each)
+// come first in the forward workspace.
+size_t split_ws(int64_t N, int H, int d) { return 2 * align256((size_t)N * H * 3 * d * 2); }
+
+// The selection on validated arguments.  q and k are bf16 rows of d_rows
+// elements (d, or 3d for split-precision rows); w is the forward workspace
+// past any split rows.
+kmip_status_t score_topk_core(const uint16_t* q, const uint16_t* k, int64_t N, int H, int d_rows,
+                              int topk, const int32_t* graph_offsets, int num_graphs,
+                              int32_t* topk_idx, float* topk_score, char* w, hipStream_t s) {
+  const bool single = single_graph(graph_offsets, num_graphs);
+  const int64_t max_tiles = scan_max_tiles(N, num_graphs);
+  ScanArgs a{};
+  a.q = q;
+  a.k = k;
+  a.N = N;
+  a.H = H;
+  a.topk = topk;
+  a.max_tiles = max_tiles;
+  a.thr = reinterpret_cast<float*>(w);
+  a.idx = topk_idx;
+  a.score = topk_score;
+  w += align256((size_t)N * H * sizeof(float));
+  kmip_status_t st = KMIP_OK;
+  if (!single) {
+    int32_t* tile_start = reinterpret_cast<int32_t*>(w);
+    int2* tiles = reinterpret_cast<int2*>(w + align256((size_t)(num_graphs + 1) * 4));
+    w += align256((size_t)(num_graphs + 1) * 4) + align256((size_t)max_tiles * sizeof(int2));
+    const int tile_rows = scan_waves(scan_list_len(topk)) * SCAN_QPW;
+    st = launch_status(launch_tile_plan(graph_offsets, num_graphs, max_tiles, tile_rows,
+                                        tile_start, tiles, s));
+    if (st != KMIP_OK) return st;
+    a.offsets = graph_offsets;
+    a.tiles = tiles;
+  } else if (use_query_order(N, H)) {
+    int32_t* perm = nullptr;
+    st = launch_status(launch_query_order(a.q, N, H, d_rows, w, &perm, s));
+    if (st != KMIP_OK) return st;
+    a.perm = perm;
+    w += query_order_bytes(N, H);
+  }
+  if (collect_ws(N, H, topk) > 0) {
+    a.cand = reinterpret_cast<uint2*>(w);
+    w += align256((size_t)2 * COLLECT_CAP * N * H * sizeof(uint2));
+    a.cand_cnt = reinterpret_cast<int32_t*>(w);
+    a.cap = COLLECT_CAP;
+  }
+  return launch_status(launch_score_topk(a, d_rows, s));
+}
+
+kmip_status_t backward_impl(const void* q, const void* k, const void* v, bool f32, int64_t N,
+                            int H, int d, int topk, const int32_t* graph_offsets,
+                            int num_graphs, const int32_t* topk_idx, const float* topk_score,
+                            const float* dout, float* dq, float* dk, float* dv,
+                            void* workspace, size_t workspace_bytes, kmip_stream_t stream) {
+  if (!q || !k || !v || !topk_idx || !topk_score || !dout || !dq || !dk || !dv)
+    return KMIP_ERR_INVALID_VALUE;
+  kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
+  if (st != KMIP_OK) return st;
+  if (num_graphs > 1 && graph_offsets == nullptr) return KMIP_ERR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(topk_idx, 4) ||
+      !aligned(topk_score, 4))
+    return KMIP_ERR_INVALID_VALUE;
+  const size_t need = backward_ws(N, H, d, topk);
+  if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return KMIP_ERR_INVALID_VALUE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t P = N * H * topk;
+  const int64_t HN = N * H;
+  char* w = static_cast<char*>(workspace);
+  float2* pairs = reinterpret_cast<float2*>(w);
+  w += align256((size_t)P * sizeof(float2));
+  SortScratch sc;
+  sort_scratch_carve(w, pairs, P, HN, &sc);
+  w += sort_scratch_bytes(P, HN);
+  double* partials = reinterpret_cast<double*>(w);
+
+  st = launch_status(launch_bwd_query(k, v, f32, N, H, d, topk, topk_idx, topk_score, dout, dq,
+                                      pairs, s));
+  if (st != KMIP_OK) return st;
+  st = launch_status(launch_selection_transpose(topk_idx, N, H, topk, &sc, s));
+  if (st != KMIP_OK) return st;
+  return launch_status(launch_bwd_keys(q, f32, dout, N, H, d, topk, &sc, partials, dk, dv, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,45 +189,9 @@ kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, in
   const size_t need = forward_ws(N, H, topk, single ? 0 : num_graphs);
   if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t max_tiles = scan_max_tiles(N, num_graphs);
-  char* w = static_cast<char*>(workspace);
-  ScanArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.N = N;
-  a.H = H;
-  a.topk = topk;
-  a.max_tiles = max_tiles;
-  a.thr = reinterpret_cast<float*>(w);
-  a.idx = topk_idx;
-  a.score = topk_score;
-  w += align256((size_t)N * H * sizeof(float));
-  if (!single) {
-    int32_t* tile_start = reinterpret_cast<int32_t*>(w);
-    int2* tiles = reinterpret_cast<int2*>(w + align256((size_t)(num_graphs + 1) * 4));
-    w += align256((size_t)(num_graphs + 1) * 4) + align256((size_t)max_tiles * sizeof(int2));
-    const int tile_rows = scan_waves(scan_list_len(topk)) * SCAN_QPW;
-    st = launch_status(launch_tile_plan(graph_offsets, num_graphs, max_tiles, tile_rows,
-                                        tile_start, tiles, s));
-    if (st != KMIP_OK) return st;
-    a.offsets = graph_offsets;
-    a.tiles = tiles;
-  } else if (use_query_order(N, H)) {
-    int32_t* perm = nullptr;
-    st = launch_status(launch_query_order(a.q, N, H, d, w, &perm, s));
-    if (st != KMIP_OK) return st;
-    a.perm = perm;
-    w += query_order_bytes(N, H);
-  }
-  if (collect_ws(N, H, topk) > 0) {
-    a.cand = reinterpret_cast<uint2*>(w);
-    w += align256((size_t)2 * COLLECT_CAP * N * H * sizeof(uint2));
-    a.cand_cnt = reinterpret_cast<int32_t*>(w);
-    a.cap = COLLECT_CAP;
-  }
-  return launch_status(launch_score_topk(a, d, s));
+  return score_topk_core(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), N,
+                         H, d, topk, graph_offsets, num_graphs, topk_idx, topk_score,
+                         static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 kmip_status_t kmip_gather_softmax_av(const void* v, int64_t N, int H, int d, int topk,
@@ -177,38 +228,52 @@ kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t
                             const int32_t* topk_idx, const float* topk_score,
                             const float* dout, float* dq, float* dk, float* dv,
                             void* workspace, size_t workspace_bytes, kmip_stream_t stream) {
-  if (!q || !k || !v || !topk_idx || !topk_score || !dout || !dq || !dk || !dv)
-    return KMIP_ERR_INVALID_VALUE;
+  return backward_impl(q, k, v, false, N, H, d, topk, graph_offsets, num_graphs, topk_idx,
+                       topk_score, dout, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+size_t kmip_forward_f32_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
+  if (check_shape(N, H, d, topk, num_graphs) != KMIP_OK) return 0;
+  return split_ws(N, H, d) + forward_ws(N, H, topk, num_graphs);
+}
+
+kmip_status_t kmip_forward_f32(const float* q, const float* k, const float* v, int64_t N, int H,
+                               int d, int topk, const int32_t* graph_offsets, int num_graphs,
+                               float* out, int32_t* topk_idx, float* topk_score,
+                               void* workspace, size_t workspace_bytes, kmip_stream_t stream) {
+  if (!q || !k || !v || !out || !topk_idx || !topk_score) return KMIP_ERR_INVALID_VALUE;
   kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
   if (st != KMIP_OK) return st;
   if (num_graphs > 1 && graph_offsets == nullptr) return KMIP_ERR_INVALID_VALUE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
-      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(topk_idx, 4) ||
-      !aligned(topk_score, 4))
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(topk_idx, 4) || !aligned(topk_score, 4))
     return KMIP_ERR_INVALID_VALUE;
-  const size_t need = backward_ws(N, H, d, topk);
+  const bool single = single_graph(graph_offsets, num_graphs);
+  const size_t need = split_ws(N, H, d) + forward_ws(N, H, topk, single ? 0 : num_graphs);
   if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return KMIP_ERR_INVALID_VALUE;
+  if (!aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t P = N * H * topk;
-  const int64_t HN = N * H;
   char* w = static_cast<char*>(workspace);
-  float2* pairs = reinterpret_cast<float2*>(w);
-  w += align256((size_t)P * sizeof(float2));
-  SortScratch sc;
-  sort_scratch_carve(w, pairs, P, HN, &sc);
-  w += sort_scratch_bytes(P, HN);
-  double* partials = reinterpret_cast<double*>(w);
+  uint16_t* q3 = reinterpret_cast<uint16_t*>(w);
+  uint16_t* k3 = reinterpret_cast<uint16_t*>(w + split_ws(N, H, d) / 2);
+  st = launch_status(launch_split_rows(q, k, N * H, d, q3, k3, s));
+  if (st != KMIP_OK) return st;
+  st = score_topk_core(q3, k3, N, H, 3 * d, topk, graph_offsets, num_graphs, topk_idx,
+                       topk_score, w + split_ws(N, H, d), s);
+  if (st != KMIP_OK) return st;
+  return launch_status(
+      launch_gather_rescore_av(q, k, v, N, H, d, topk, topk_idx, topk_score, out, s));
+}
 
-  st = launch_status(launch_bwd_query(static_cast<const uint16_t*>(k),
-                                      static_cast<const uint16_t*>(v), N, H, d, topk,
-                                      topk_idx, topk_score, dout, dq, pairs, s));
-  if (st != KMIP_OK) return st;
-  st = launch_status(launch_selection_transpose(topk_idx, N, H, topk, &sc, s));
-  if (st != KMIP_OK) return st;
-  return launch_status(launch_bwd_keys(static_cast<const uint16_t*>(q), dout, N, H, d, topk,
-                                       &sc, partials, dk, dv, s));
+kmip_status_t kmip_backward_f32(const float* q, const float* k, const float* v, int64_t N,
+                                int H, int d, int topk, const int32_t* graph_offsets,
+                                int num_graphs, const int32_t* topk_idx,
+                                const float* topk_score, const float* dout, float* dq,
+                                float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                                kmip_stream_t stream) {
+  return backward_impl(q, k, v, true, N, H, d, topk, graph_offsets, num_graphs, topk_idx,
+                       topk_score, dout, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -20,6 +20,7 @@
 //     directly; runs cut by a slice boundary go to per-slice partials, which
 //     a fix-up pass adds in slice order.  Keys selected by no query get exact
 //     zeros.  Every sum has a fixed order, so results are bitwise repeatable.
+#include "kmip_cols.h"
 #include "kmip_internal.h"
 
 namespace kmip {
@@ -256,53 +257,15 @@ __global__ __launch_bounds__(SORT_THREADS) void radix_scatter_kernel(
 }
 
 // ------------------------------------------------------------ segmented reduce
-template <int EPL>
-__device__ __forceinline__ void load_bf16_cols(const uint16_t* p, float* x) {
-  if constexpr (EPL == 2) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    x[0] = __uint_as_float(w << 16);
-    x[1] = __uint_as_float(w & 0xffff0000u);
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    x[0] = __uint_as_float(w.x << 16);
-    x[1] = __uint_as_float(w.x & 0xffff0000u);
-    x[2] = __uint_as_float(w.y << 16);
-    x[3] = __uint_as_float(w.y & 0xffff0000u);
-  }
-}
-
-template <int EPL>
-__device__ __forceinline__ void load_f32_cols(const float* p, float* x) {
-  if constexpr (EPL == 2) {
-    const float2 t = *reinterpret_cast<const float2*>(p);
-    x[0] = t.x;
-    x[1] = t.y;
-  } else {
-    const float4 t = *reinterpret_cast<const float4*>(p);
-    x[0] = t.x;
-    x[1] = t.y;
-    x[2] = t.z;
-    x[3] = t.w;
-  }
-}
-
-template <int EPL>
-__device__ __forceinline__ void store_f32_cols(float* p, const float* x) {
-  if constexpr (EPL == 2) {
-    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
-  } else {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-  }
-}
-
 constexpr int SEG_GROUPS = 16;     // 16-lane groups per 256-thread block
 
 // partials layout: [slice][slot 0|1][dk | dv][D], fp64.  Sums are carried in
 // fp64 (hub keys add thousands of terms of mixed sign) and rounded to fp32
-// once, when the key's total is written.
-template <int D>
+// once, when the key's total is written.  Q rows are bf16 (QT = uint16_t) or
+// fp32.
+template <int D, typename QT>
 __global__ __launch_bounds__(256) void segreduce_kernel(
-    const uint16_t* __restrict__ Q, const float* __restrict__ dout,
+    const QT* __restrict__ Q, const float* __restrict__ dout,
     const float2* __restrict__ spay, const uint32_t* __restrict__ skeys,
     const uint32_t* __restrict__ svals, const int32_t* __restrict__ key_ptr, int64_t N, int H,
     int topk, int64_t nslices, double* __restrict__ partials, float* __restrict__ dk,
@@ -334,8 +297,8 @@ __global__ __launch_bounds__(256) void segreduce_kernel(
         fk[e] = (float)ak[e];
         fv[e] = (float)av[e];
       }
-      store_f32_cols<EPL>(dk + orow * D + l16 * EPL, fk);
-      store_f32_cols<EPL>(dv + orow * D + l16 * EPL, fv);
+      store_cols<EPL>(dk + orow * D + l16 * EPL, fk);
+      store_cols<EPL>(dv + orow * D + l16 * EPL, fv);
       return;
     }
     const int slot = (ra == s0) ? 0 : 1;
@@ -378,8 +341,8 @@ __global__ __launch_bounds__(256) void segreduce_kernel(
       py[u] = __shfl(mpy[i], src, 16);
       if (ip < n) {
         const int64_t row = pid / (uint32_t)topk;
-        load_bf16_cols<EPL>(Q + row * D + l16 * EPL, qx[u]);
-        load_f32_cols<EPL>(dout + row * D + l16 * EPL, gx[u]);
+        load_cols<EPL>(Q + row * D + l16 * EPL, qx[u]);
+        load_cols<EPL>(dout + row * D + l16 * EPL, gx[u]);
       }
     }
 #pragma unroll
@@ -441,8 +404,8 @@ __global__ __launch_bounds__(256) void segfix_kernel(const int32_t* __restrict__
     fk[e] = (float)ak[e];
     fv[e] = (float)av[e];
   }
-  store_f32_cols<EPL>(dk + orow * D + l16 * EPL, fk);
-  store_f32_cols<EPL>(dv + orow * D + l16 * EPL, fv);
+  store_cols<EPL>(dk + orow * D + l16 * EPL, fk);
+  store_cols<EPL>(dv + orow * D + l16 * EPL, fv);
 }
 
 // key_ptr[key] = first position of the sorted keys that is >= key, for
@@ -548,30 +511,34 @@ size_t segreduce_scratch_bytes(int64_t P, int d) {
   return align256((size_t)nslices * 2 * 2 * d * sizeof(double));
 }
 
-hipError_t launch_bwd_keys(const uint16_t* q, const float* dout, int64_t N, int H, int d,
-                           int topk, const SortScratch* sc, double* partials, float* dk,
-                           float* dv, hipStream_t s) {
+namespace {
+template <int D, typename QT>
+void launch_keys_t(const QT* q, const float* dout, int64_t N, int H, int topk,
+                   const SortScratch* sc, double* partials, float* dk, float* dv,
+                   hipStream_t s) {
   const int64_t P = N * H * topk;
   const int64_t HN = N * H;
   const int64_t nslices = ceil_div(P, SEG_SLICE);
   const unsigned b1 = (unsigned)ceil_div(nslices, SEG_GROUPS);
   const unsigned b2 = (unsigned)ceil_div(HN, SEG_GROUPS);
-  const uint32_t* sk = sc->keys[sc->final_buf];
-  const uint32_t* sv = sc->vals[sc->final_buf];
-  const float2* sp = sc->pay[sc->final_buf];
-  if (d == 32) {
-    hipLaunchKernelGGL(segreduce_kernel<32>, dim3(b1), dim3(256), 0, s, q, dout, sp, sk, sv,
-                       sc->key_ptr, N, H, topk, nslices, partials, dk, dv);
-    hipLaunchKernelGGL(segfix_kernel<32>, dim3(b2), dim3(256), 0, s, sc->key_ptr, N, H,
-                       partials, dk, dv);
-  } else if (d == 64) {
-    hipLaunchKernelGGL(segreduce_kernel<64>, dim3(b1), dim3(256), 0, s, q, dout, sp, sk, sv,
-                       sc->key_ptr, N, H, topk, nslices, partials, dk, dv);
-    hipLaunchKernelGGL(segfix_kernel<64>, dim3(b2), dim3(256), 0, s, sc->key_ptr, N, H,
-                       partials, dk, dv);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((segreduce_kernel<D, QT>), dim3(b1), dim3(256), 0, s, q, dout,
+                     sc->pay[sc->final_buf], sc->keys[sc->final_buf], sc->vals[sc->final_buf],
+                     sc->key_ptr, N, H, topk, nslices, partials, dk, dv);
+  hipLaunchKernelGGL(segfix_kernel<D>, dim3(b2), dim3(256), 0, s, sc->key_ptr, N, H, partials,
+                     dk, dv);
+}
+}  // namespace
+
+hipError_t launch_bwd_keys(const void* q, bool q_f32, const float* dout, int64_t N, int H,
+                           int d, int topk, const SortScratch* sc, double* partials, float* dk,
+                           float* dv, hipStream_t s) {
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const float* qf = static_cast<const float*>(q);
+  if (d == 32 && !q_f32) launch_keys_t<32>(qb, dout, N, H, topk, sc, partials, dk, dv, s);
+  else if (d == 32) launch_keys_t<32>(qf, dout, N, H, topk, sc, partials, dk, dv, s);
+  else if (d == 64 && !q_f32) launch_keys_t<64>(qb, dout, N, H, topk, sc, partials, dk, dv, s);
+  else if (d == 64) launch_keys_t<64>(qf, dout, N, H, topk, sc, partials, dk, dv, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

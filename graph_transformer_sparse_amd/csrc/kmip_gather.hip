@@ -9,9 +9,10 @@
 //
 // These kernels are bandwidth bound (a handful of flops per gathered byte).
 // A query row (node, head) is handled by 16 lanes; each lane owns d/16
-// consecutive columns, so one gathered bf16 row is a single 64- or 128-byte
-// coalesced segment.  Index and score rows are read once per row group and
-// broadcast with 16-lane shuffles.
+// consecutive columns, so one gathered row is a single coalesced segment
+// (64 or 128 bytes in bf16, 128 or 256 in fp32).  Index and score rows are
+// read once per row group and broadcast with 16-lane shuffles.
+#include "kmip_cols.h"
 #include "kmip_internal.h"
 
 namespace kmip {
@@ -20,61 +21,10 @@ namespace {
 constexpr int ROWS_PER_BLOCK = 16;          // 256 threads, 16 lanes per row
 constexpr int MAXK = 64;
 
-template <int EPL>
-struct Cols;                                 // EPL bf16 values of one row
-template <>
-struct Cols<2> {
-  static __device__ __forceinline__ void load(const uint16_t* p, float* x) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    x[0] = __uint_as_float(w << 16);
-    x[1] = __uint_as_float(w & 0xffff0000u);
-  }
-};
-template <>
-struct Cols<4> {
-  static __device__ __forceinline__ void load(const uint16_t* p, float* x) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    x[0] = __uint_as_float(w.x << 16);
-    x[1] = __uint_as_float(w.x & 0xffff0000u);
-    x[2] = __uint_as_float(w.y << 16);
-    x[3] = __uint_as_float(w.y & 0xffff0000u);
-  }
-};
-
-template <int EPL>
-__device__ __forceinline__ void load_cols_f32(const float* p, float* x) {
-  if constexpr (EPL == 2) {
-    const float2 t = *reinterpret_cast<const float2*>(p);
-    x[0] = t.x;
-    x[1] = t.y;
-  } else {
-    const float4 t = *reinterpret_cast<const float4*>(p);
-    x[0] = t.x;
-    x[1] = t.y;
-    x[2] = t.z;
-    x[3] = t.w;
-  }
-}
-
-template <int EPL>
-__device__ __forceinline__ void store_cols(float* p, const float* x) {
-  if constexpr (EPL == 2) {
-    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
-  } else {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-  }
-}
-
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) x += __shfl_xor(x, o, 16);
-  return x;
-}
-
-// out[row] = sum_t softmax(score[row])_t * V[idx[row][t]]
-template <int D>
+// out[row] = sum_t softmax(score[row])_t * V[idx[row][t]] (bf16 V rows).
+template <int D, typename T>
 __global__ __launch_bounds__(256) void gather_av_kernel(
-    const uint16_t* __restrict__ V, int64_t NH, int H, int topk,
+    const T* __restrict__ V, int64_t NH, int H, int topk,
     const int32_t* __restrict__ idx, const float* __restrict__ score,
     float* __restrict__ out) {
   constexpr int EPL = D / 16;
@@ -109,12 +59,81 @@ __global__ __launch_bounds__(256) void gather_av_kernel(
       if (j >= 0) {
         const float w = __expf(__shfl(sv[c], u, 16) - m);
         float x[EPL];
-        Cols<EPL>::load(V + ((int64_t)j * H + h) * D + l16 * EPL, x);
+        load_cols<EPL>(V + ((int64_t)j * H + h) * D + l16 * EPL, x);
         z += w;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, x[e], acc[e]);
       }
     }
+  }
+  const float inv = 1.f / z;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] *= inv;
+  store_cols<EPL>(out + row * D + l16 * EPL, acc);
+}
+
+// fp32 entry point: the scan selects on split-precision scores (error up to
+// ~2^-16 |q||k|), and the softmax weights would inherit that error, which the
+// backward's p (dp - D) can amplify where dp is close to D.  This variant
+// recomputes each selected score in fp32 from the fp32 rows, s_t = q . k_t
+// (lane partials of d/16 products, then a 16-lane tree), overwrites the saved
+// score with it and weighs V with it.  The shift m is the best split score,
+// within 2 eps of the best recomputed one, so exp stays bounded.  Selection
+// and order are the scan's.
+template <int D>
+__global__ __launch_bounds__(256) void gather_rescore_av_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    int64_t NH, int H, int topk, const int32_t* __restrict__ idx, float* __restrict__ score,
+    float* __restrict__ out) {
+  constexpr int EPL = D / 16;
+  const int l16 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 4);
+  if (row >= NH) return;
+  const int h = (int)(row % H);
+  const int32_t* ir = idx + row * topk;
+  float* sr = score + row * topk;
+
+  int jv[MAXK / 16];
+  float sv[MAXK / 16];
+#pragma unroll
+  for (int c = 0; c < MAXK / 16; ++c) {
+    const int t = c * 16 + l16;
+    jv[c] = t < topk ? ir[t] : -1;
+    sv[c] = t < topk ? sr[t] : 0.f;
+  }
+  float qx[EPL];
+  load_cols<EPL>(Q + row * D + l16 * EPL, qx);
+  const float m = __shfl(sv[0], 0, 16);
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float z = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXK / 16; ++c) {
+    if (c * 16 >= topk) break;
+    const int tn = topk - c * 16 < 16 ? topk - c * 16 : 16;
+    float snew = sv[c];
+    for (int u = 0; u < tn; ++u) {
+      const int j = __shfl(jv[c], u, 16);
+      if (j >= 0) {                         // uniform across the 16 lanes
+        const int64_t base = ((int64_t)j * H + h) * D + l16 * EPL;
+        float kx[EPL], vx[EPL];
+        load_cols<EPL>(K + base, kx);
+        load_cols<EPL>(V + base, vx);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) part = fmaf(qx[e], kx[e], part);
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) part += __shfl_xor(part, o, 16);
+        const float w = __expf(part - m);
+        z += w;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, vx[e], acc[e]);
+        if (l16 == u) snew = part;
+      }
+    }
+    const int t = c * 16 + l16;
+    if (t < topk && jv[c] >= 0) sr[t] = snew;
   }
   const float inv = 1.f / z;
 #pragma unroll
@@ -128,8 +147,8 @@ __global__ __launch_bounds__(256) void gather_av_kernel(
 //
 // dp_t - D cancels when one weight dominates (p_0 -> 1), so the weights are
 // normalised and dp, D, ds and dq are carried in fp64: the products of fp32
-// dO and bf16 v are exact in fp64, and an fp32 p_0 alone would already carry
-// an absolute error of ~6e-8.  The exponentials stay fp32 (each w_t is
+// dO and bf16 or fp32 v are exact in fp64, and an fp32 p_0 alone would
+// already carry an absolute error of ~6e-8.  The exponentials stay fp32 (each w_t is
 // relatively accurate, which keeps p_0 = 1/Z accurate in fp64).
 __device__ __forceinline__ double sum16d(double x) {
 #pragma unroll
@@ -137,9 +156,9 @@ __device__ __forceinline__ double sum16d(double x) {
   return x;
 }
 
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_query_kernel(
-    const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V, int64_t NH, int H,
+    const T* __restrict__ Kt, const T* __restrict__ V, int64_t NH, int H,
     int topk, const int32_t* __restrict__ idx, const float* __restrict__ score,
     const float* __restrict__ dout, float* __restrict__ dq, float2* __restrict__ pairs) {
   constexpr int EPL = D / 16;
@@ -159,7 +178,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
     sv[c] = t < topk ? sr[t] : 0.f;
   }
   float g[EPL];
-  load_cols_f32<EPL>(dout + row * D + l16 * EPL, g);
+  load_cols<EPL>(dout + row * D + l16 * EPL, g);
   const float m = __shfl(sv[0], 0, 16);
 
   // Pass 1: weights w_t and dp_t; lane (t % 16) keeps entry t.
@@ -176,7 +195,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
         double dp = 0.0, w = 0.0;
         if (j >= 0) {                      // uniform across the 16 lanes
           float x[EPL];
-          Cols<EPL>::load(V + ((int64_t)j * H + h) * D + l16 * EPL, x);
+          load_cols<EPL>(V + ((int64_t)j * H + h) * D + l16 * EPL, x);
           double part = 0.0;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) part = fma((double)g[e], (double)x[e], part);
@@ -212,7 +231,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
         const double dsu = __shfl(ds, u, 16);
         if (j >= 0) {
           float x[EPL];
-          Cols<EPL>::load(Kt + ((int64_t)j * H + h) * D + l16 * EPL, x);
+          load_cols<EPL>(Kt + ((int64_t)j * H + h) * D + l16 * EPL, x);
 #pragma unroll
           for (int e = 0; e < EPL; ++e) acc[e] = fma(dsu, (double)x[e], acc[e]);
         }
@@ -225,37 +244,66 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   store_cols<EPL>(dq + row * D + l16 * EPL, r);
 }
 
+template <int D, typename T>
+void launch_gather_t(const T* v, int64_t NH, int H, int topk, const int32_t* idx,
+                     const float* score, float* out, hipStream_t s) {
+  const unsigned blocks = (unsigned)ceil_div(NH, ROWS_PER_BLOCK);
+  hipLaunchKernelGGL((gather_av_kernel<D, T>), dim3(blocks), dim3(256), 0, s, v, NH, H, topk,
+                     idx, score, out);
+}
+
+template <int D, typename T>
+void launch_bwd_query_t(const T* k, const T* v, int64_t NH, int H, int topk, const int32_t* idx,
+                        const float* score, const float* dout, float* dq, float2* pairs,
+                        hipStream_t s) {
+  const unsigned blocks = (unsigned)ceil_div(NH, ROWS_PER_BLOCK);
+  hipLaunchKernelGGL((bwd_query_kernel<D, T>), dim3(blocks), dim3(256), 0, s, k, v, NH, H,
+                     topk, idx, score, dout, dq, pairs);
+}
+
 }  // namespace
 
-hipError_t launch_gather_av(const uint16_t* v, int64_t N, int H, int d, int topk,
-                            const int32_t* topk_idx, const float* topk_score, float* out,
-                            hipStream_t s) {
+hipError_t launch_gather_rescore_av(const float* q, const float* k, const float* v, int64_t N,
+                                    int H, int d, int topk, const int32_t* topk_idx,
+                                    float* topk_score, float* out, hipStream_t s) {
   const int64_t NH = N * H;
   const unsigned blocks = (unsigned)ceil_div(NH, ROWS_PER_BLOCK);
   if (d == 32)
-    hipLaunchKernelGGL(gather_av_kernel<32>, dim3(blocks), dim3(256), 0, s, v, NH, H, topk,
-                       topk_idx, topk_score, out);
+    hipLaunchKernelGGL(gather_rescore_av_kernel<32>, dim3(blocks), dim3(256), 0, s, q, k, v, NH,
+                       H, topk, topk_idx, topk_score, out);
   else if (d == 64)
-    hipLaunchKernelGGL(gather_av_kernel<64>, dim3(blocks), dim3(256), 0, s, v, NH, H, topk,
-                       topk_idx, topk_score, out);
+    hipLaunchKernelGGL(gather_rescore_av_kernel<64>, dim3(blocks), dim3(256), 0, s, q, k, v, NH,
+                       H, topk, topk_idx, topk_score, out);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_query(const uint16_t* k, const uint16_t* v, int64_t N, int H, int d,
+hipError_t launch_gather_av(const uint16_t* v, int64_t N, int H, int d, int topk,
+                            const int32_t* topk_idx, const float* topk_score, float* out,
+                            hipStream_t s) {
+  const int64_t NH = N * H;
+  if (d == 32) launch_gather_t<32>(v, NH, H, topk, topk_idx, topk_score, out, s);
+  else if (d == 64) launch_gather_t<64>(v, NH, H, topk, topk_idx, topk_score, out, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_query(const void* k, const void* v, bool f32, int64_t N, int H, int d,
                             int topk, const int32_t* topk_idx, const float* topk_score,
                             const float* dout, float* dq, float2* pairs, hipStream_t s) {
   const int64_t NH = N * H;
-  const unsigned blocks = (unsigned)ceil_div(NH, ROWS_PER_BLOCK);
-  if (d == 32)
-    hipLaunchKernelGGL(bwd_query_kernel<32>, dim3(blocks), dim3(256), 0, s, k, v, NH, H, topk,
-                       topk_idx, topk_score, dout, dq, pairs);
+  const uint16_t *kb = static_cast<const uint16_t*>(k), *vb = static_cast<const uint16_t*>(v);
+  const float *kf = static_cast<const float*>(k), *vf = static_cast<const float*>(v);
+  if (d == 32 && !f32)
+    launch_bwd_query_t<32>(kb, vb, NH, H, topk, topk_idx, topk_score, dout, dq, pairs, s);
+  else if (d == 32)
+    launch_bwd_query_t<32>(kf, vf, NH, H, topk, topk_idx, topk_score, dout, dq, pairs, s);
+  else if (d == 64 && !f32)
+    launch_bwd_query_t<64>(kb, vb, NH, H, topk, topk_idx, topk_score, dout, dq, pairs, s);
   else if (d == 64)
-    hipLaunchKernelGGL(bwd_query_kernel<64>, dim3(blocks), dim3(256), 0, s, k, v, NH, H, topk,
-                       topk_idx, topk_score, dout, dq, pairs);
-  else
-    return hipErrorInvalidValue;
+    launch_bwd_query_t<64>(kf, vf, NH, H, topk, topk_idx, topk_score, dout, dq, pairs, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

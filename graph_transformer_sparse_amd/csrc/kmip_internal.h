@@ -83,6 +83,12 @@ struct ScanArgs {
   int cap;
 };
 hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s);
+// Per row width (bf16 elements; 96 and 192 are split-precision rows of 32
+// and 64 fp32 elements), kp = scan_list_len(topk).
+hipError_t launch_scan_d32(int kp, const ScanArgs& a, hipStream_t s);
+hipError_t launch_scan_d64(int kp, const ScanArgs& a, hipStream_t s);
+hipError_t launch_scan_d96(int kp, const ScanArgs& a, hipStream_t s);
+hipError_t launch_scan_d192(int kp, const ScanArgs& a, hipStream_t s);
 
 // Query order for one graph: groups each head's queries by a sign-random-
 // projection code of q.  Workspace: query_order_bytes(N, H); *perm points
@@ -91,13 +97,27 @@ size_t query_order_bytes(int64_t N, int H);
 hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* ws,
                               int32_t** perm, hipStream_t s);
 
-// Gather the selected V rows, softmax over saved scores, weighted sum.
+// Split-precision rows for the fp32 entry points: per (node, head) row of d
+// fp32 elements x = hi + lo + r (hi = bf16(x), lo = bf16(x - hi)),
+// q3 = [q_hi | q_hi | q_lo] and k3 = [k_hi | k_lo | k_hi], bf16 [rows][3d],
+// so that q3 . k3 = q_hi.k_hi + q_hi.k_lo + q_lo.k_hi.
+hipError_t launch_split_rows(const float* q, const float* k, int64_t rows, int d, uint16_t* q3,
+                             uint16_t* k3, hipStream_t s);
+
+// Gather the selected V rows (bf16), softmax over saved scores, weighted sum.
 hipError_t launch_gather_av(const uint16_t* v, int64_t N, int H, int d, int topk,
                             const int32_t* topk_idx, const float* topk_score, float* out,
                             hipStream_t s);
 
-// Backward, query side: dq and the per-pair (p, ds).
-hipError_t launch_bwd_query(const uint16_t* k, const uint16_t* v, int64_t N, int H, int d,
+// fp32 entry point: recompute the selected scores in fp32 from the fp32 rows
+// (overwriting topk_score), then the softmax-weighted sum of fp32 V rows.
+hipError_t launch_gather_rescore_av(const float* q, const float* k, const float* v, int64_t N,
+                                    int H, int d, int topk, const int32_t* topk_idx,
+                                    float* topk_score, float* out, hipStream_t s);
+
+// Backward, query side: dq and the per-pair (p, ds).  K and V are bf16 bits,
+// or fp32 when f32 is set.
+hipError_t launch_bwd_query(const void* k, const void* v, bool f32, int64_t N, int H, int d,
                             int topk, const int32_t* topk_idx, const float* topk_score,
                             const float* dout, float* dq, float2* pairs, hipStream_t s);
 
@@ -119,10 +139,11 @@ void sort_scratch_carve(void* base, float2* pairs, int64_t P, int64_t HN, SortSc
 hipError_t launch_selection_transpose(const int32_t* topk_idx, int64_t N, int H, int topk,
                                       SortScratch* sc, hipStream_t s);
 
-// Backward, key side: dk, dv by segmented reduction over the sorted pairs.
+// Backward, key side: dk, dv by segmented reduction over the sorted pairs
+// (Q bf16 bits, or fp32 when q_f32 is set).
 size_t segreduce_scratch_bytes(int64_t P, int d);
-hipError_t launch_bwd_keys(const uint16_t* q, const float* dout, int64_t N, int H, int d,
-                           int topk, const SortScratch* sc, double* partials, float* dk,
+hipError_t launch_bwd_keys(const void* q, bool q_f32, const float* dout, int64_t N, int H,
+                           int d, int topk, const SortScratch* sc, double* partials, float* dk,
                            float* dv, hipStream_t s);
 
 // Device-wide exclusive scan of int32 (aux: scan_aux_elems(n) ints).

@@ -1,608 +1,10 @@
-// Score scan with the top-k selection (the O(N^2) part of k-MIP attention)
-// and the ragged tile plan.
-//
-// Page "k-Maximum Inner Product Attention for Graph Transformers and the
-// Expressive Power of GraphGPS", Abstract: each query keeps the key nodes with
-// the k largest inner products, found by a top-k operation over scores that
-// are never stored as an N x N matrix.
-//
-// Design (gfx950):
-//  * Work is split into sub-tiles of up to 512 query rows of one head and one
-//    graph: a workgroup of 16 wavefronts, each owning 32 rows.  A wavefront
-//    keeps its Q rows in VGPRs as MFMA B operands for the whole scan.
-//  * The graph's keys stream through an LDS ring of two chunks (64 KB, 1024
-//    keys at d = 32, in the threshold pass; 32 KB in the selection pass, which
-//    also holds candidate buffers), fetched with direct global->LDS loads one
-//    chunk ahead.  A chunk is stored in MFMA operand order (see ScanShape), so
-//    each A operand is one contiguous, conflict-free 1 KB LDS read.
-//  * v_mfma_f32_32x32x16_bf16 scores 32 keys x 32 queries (fp32 accumulation
-//    of exact bf16 products).  Lane l holds query l%32 and 16 of the 32 keys,
-//    so each lane sees a private half of every query's key stream, in
-//    ascending key order.
-//  * Two passes.  The threshold pass scores every fourth chunk only and
-//    keeps, per lane and query, the top-k of the maxima of SCAN_CHUNKS
-//    consecutive ranges of those keys (uniform, lockstep insertions); these
-//    maxima are scores of distinct keys, so the k-th largest over both halves
-//    is a lower bound T of the query's k-th score.
-//    The selection pass then runs the exact running top-k seeded with
-//    next_down(T): a block of scores is rejected with a max tree and one
-//    compare, rare hits go to a per-lane LDS candidate buffer, and buffers
-//    are drained in lockstep into per-lane register lists.  At the end the
-//    two half-lists of a query (lanes l, l^32) are merged by rank with the
-//    tie rule (score descending, id ascending).
-//  * One graph: each head's queries are first grouped by a sign-random-
-//    projection code, so a wavefront's 32 queries tend to share their
-//    candidate keys.  A persistent grid of exactly the co-resident
-//    workgroups, each taking an equal contiguous range of query blocks (no
-//    partial last round), with logical ids permuted so that the workgroups of
-//    one XCD share a head and its keys in that XCD's L2.  Batched graphs: one workgroup per planned
-//    sub-tile; sub-blocks past a graph's last key are skipped.
+// Host side of the score scan: the ragged tile plan for batched graphs, the
+// query order for one graph, and the dispatch to the per-dimension scan
+// kernels (kmip_scan_kernels.h, instantiated in kmip_scan_d*.hip).
 #include "kmip_internal.h"
 
 namespace kmip {
 namespace {
-
-constexpr float kInf = __builtin_inff();
-constexpr int QB = 1;                       // query blocks of 32 per wavefront
-// Per pass: LDS chunk size in 16 KB units (LPW: 1 KB loads per wavefront and
-// chunk), ring depth, and sub-blocks per batch (LDS reads, then MFMAs, then
-// scores).  Large chunks amortise the workgroup barrier of every chunk; the
-// selection pass keeps room for its candidate buffers.  With a ring of two,
-// chunk c + 1 is fetched while chunk c is scored.
-#ifndef KMIP_SCAN_BATCH
-#define KMIP_SCAN_BATCH 2
-#endif
-#ifndef KMIP_PRE_SAMPLE
-#define KMIP_PRE_SAMPLE 4
-#endif
-// Scan modes.  THRESH: per-row lower bound T of the k-th score.  SELECT:
-// exact running top-k in per-lane register lists.  COLLECT (lists longer
-// than 16): every key scoring above next_down(T) is appended to a per-row
-// candidate array, and a second kernel selects the top-k from it; rows whose
-// arrays overflow are then recomputed by SELECT.
-constexpr int M_THRESH = 0, M_SELECT = 1, M_COLLECT = 2;
-template <int MODE> struct PassCfg;
-// SAMPLE: THRESH scores every SAMPLE-th chunk only.  Any subset of a
-// query's keys yields a valid lower bound of its k-th score; a sparser subset
-// gives a looser bound, i.e. more candidates in the later pass.
-template <> struct PassCfg<M_THRESH> {
-  static constexpr int LPW = 4, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = KMIP_PRE_SAMPLE;
-};
-template <> struct PassCfg<M_SELECT> {
-  static constexpr int LPW = 2, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = 1;
-};
-template <> struct PassCfg<M_COLLECT> {
-  static constexpr int LPW = 2, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = 1;
-};
-
-// Chunk layout in LDS ("operand order"): the chunk is a sequence of 1 KB
-// blocks, one per (32-key sub-block st, K-slice m of the MFMA), block index
-// st * NM + m.  Inside a block, lane l's 16 bytes sit at l * 16 and hold the
-// bf16 elements [16m + 8(l/32), 16m + 8(l/32) + 8) of key st*32 + l%32: the
-// A operand of v_mfma_f32_32x32x16_bf16 for that lane.  A wavefront then reads
-// each operand as one contiguous 1 KB ds_read_b128 (no bank conflicts), and
-// the direct global->LDS load that fills a block writes it in the same lane
-// order.
-template <int D, int MODE, int W>
-struct ScanShape {
-  static constexpr int NM = D / 16;                 // K=16 MFMAs per 32x32 block
-  static constexpr int ROWB = 2 * D;                // bytes per key row
-  static constexpr int LPW = PassCfg<MODE>::LPW;     // operand blocks loaded per wave
-  static constexpr int NBUF = PassCfg<MODE>::NBUF;   // LDS ring depth
-  static constexpr int SAMPLE = PassCfg<MODE>::SAMPLE;  // chunk stride
-  static constexpr int CHUNK_BYTES = 1024 * W * LPW;
-  static constexpr int TK = CHUNK_BYTES / ROWB;      // keys per chunk
-  static constexpr int SUBT = TK / 32;               // 32-key sub-blocks per chunk
-  static_assert(SUBT * NM == W * LPW, "LPW operand blocks per wavefront");
-  static_assert(NBUF == 2 || NBUF == 3, "ring depth");
-};
-
-// Insert (s, j) into a descending list.  The caller guarantees s beats the
-// k-th entry.  Keys reach a lane in ascending id order, so on equal scores
-// the entry already present (smaller id) stays first: strict compare.
-template <int KP>
-__device__ __forceinline__ void list_insert(float (&ls)[KP], int (&lj)[KP], float s, int j) {
-  bool b[KP];
-#pragma unroll
-  for (int t = 0; t < KP; ++t) b[t] = s > ls[t];
-#pragma unroll
-  for (int t = KP - 1; t >= 1; --t) {
-    ls[t] = b[t - 1] ? ls[t - 1] : (b[t] ? s : ls[t]);
-    lj[t] = b[t - 1] ? lj[t - 1] : (b[t] ? j : lj[t]);
-  }
-  ls[0] = b[0] ? s : ls[0];
-  lj[0] = b[0] ? j : lj[0];
-}
-
-template <int KP>
-__device__ __forceinline__ void value_insert(float (&ls)[KP], float s) {
-  bool b[KP];
-#pragma unroll
-  for (int t = 0; t < KP; ++t) b[t] = s > ls[t];
-#pragma unroll
-  for (int t = KP - 1; t >= 1; --t) ls[t] = b[t - 1] ? ls[t - 1] : (b[t] ? s : ls[t]);
-  ls[0] = b[0] ? s : ls[0];
-}
-
-// Largest float below x (x finite or -inf; -inf stays -inf).
-__device__ __forceinline__ float next_down(float x) {
-  if (x == -kInf) return x;
-  if (x == 0.f) return __uint_as_float(0x80000001u);
-  const unsigned u = __float_as_uint(x);
-  return __uint_as_float(x > 0.f ? u - 1u : u + 1u);
-}
-
-struct SubTile {
-  int h;
-  int64_t q0, q1;     // query rows [q0, q1)
-  int64_t kb, ke;     // key range of the graph
-};
-
-template <int D, int KP, int MODE>
-struct Scanner {
-  static constexpr bool PRE = MODE == M_THRESH;
-  static constexpr int W = scan_waves(KP);    // wavefronts per workgroup
-  using S = ScanShape<D, MODE, W>;
-  // Chunk stride of this pass.  Long lists take a denser sample: their
-  // candidates must fit the per-row arrays of the collecting pass.
-  static constexpr int SAMPLE = PRE && KP > 16 ? 2 : S::SAMPLE;
-  unsigned char* kbuf;        // S::NBUF chunks (read side)
-  unsigned kbuf_lds;          // LDS byte address of kbuf (direct-load side)
-  uint2* cbuf;                // per-lane candidate buffers (SELECT)
-  int* wg_flag;               // one LDS word (SELECT restricted to flagged rows)
-  const ScanArgs& a;
-  const uint16_t* Q;
-  const uint16_t* K;
-  const int32_t* perm;        // query order per head, [H][N] (one graph), or null
-  int64_t N;
-  int H, topk;
-  float* thr_buf;
-  int32_t* out_idx;
-  float* out_score;
-
-  // Direct global->LDS load of chunk c into ring slot `slot`: wave w fills
-  // operand blocks w + i * W (i < LPW), lane l writing 16 bytes at
-  // l * 16 of the block.  The address is a per-chunk uniform base (SGPRs)
-  // plus a 32-bit lane offset; rows past the graph's last key re-read the
-  // last key.  Written as inline assembly so that the compiler does not treat
-  // ring reads as aliasing the loads in flight: completion is tracked by the
-  // explicit vmcnt waits of the chunk loop.  The instruction writes no VGPR.
-  __device__ __forceinline__ void issue(const SubTile& t, int c, int slot, int wave, int lane) {
-    const int64_t first = t.kb + (int64_t)c * S::TK;
-    const int64_t left = t.ke - first;
-    const int rmax = (int)(left < S::TK ? left : S::TK) - 1;
-    const uint16_t* base = K + (first * H + t.h) * D;
-#pragma unroll
-    for (int i = 0; i < S::LPW; ++i) {
-      const int blk = wave + i * W;
-      const int row = (blk / S::NM) * 32 + (lane & 31);
-      const int piece = 2 * (blk % S::NM) + (lane >> 5);
-      const unsigned off =
-          (unsigned)(row < rmax ? row : rmax) * (unsigned)(H * S::ROWB) + (unsigned)piece * 16u;
-      const unsigned lds =
-          kbuf_lds + (unsigned)(slot * S::CHUNK_BYTES + blk * 1024);
-      asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
-                   "{m0}"(__builtin_amdgcn_readfirstlane(lds))
-                   : "memory");
-    }
-  }
-
-  static __device__ __forceinline__ int64_t uniform64(int64_t v) {
-    const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xffffffff));
-    const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
-    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-  }
-
-  __device__ __forceinline__ void run(const SubTile& tin) {
-    // The sub-tile is the same for the whole workgroup: keep it in SGPRs.
-    const SubTile t{__builtin_amdgcn_readfirstlane(tin.h), uniform64(tin.q0), uniform64(tin.q1),
-                    uniform64(tin.kb), uniform64(tin.ke)};
-    // The wave index is uniform: keep it (and all that derives from it) scalar.
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lrow = lane & 31, lhalf = lane >> 5;
-    const int64_t nkeys = t.ke - t.kb;
-    const int nchunks = (int)((nkeys + S::TK - 1) / S::TK);
-    // Chunks scored by this pass: c = j * SAMPLE for j < nproc.
-    const int nproc = (nchunks + SAMPLE - 1) / SAMPLE;
-
-    // The ring may still be read by slower waves of the previous sub-tile.
-    __syncthreads();
-
-    int64_t qrow[QB];
-    bool qvalid[QB], bact[QB];
-    bf16x8_t qb[QB][S::NM];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const int64_t first = t.q0 + (wave * QB + b) * 32;
-      // Positions [q0, q1) index the head's query order; rows are node ids.
-      const int64_t pos = first + lrow;
-      bact[b] = first < t.q1;
-      qvalid[b] = pos < t.q1;
-      const int64_t pl = qvalid[b] ? pos : t.q1 - 1;
-      qrow[b] = perm ? (int64_t)perm[t.h * N + pl] : pl;
-      const uint16_t* qp = Q + (qrow[b] * H + t.h) * D + 8 * lhalf;
-#pragma unroll
-      for (int m = 0; m < S::NM; ++m) qb[b][m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
-    }
-    // Rows this call writes.  SELECT with candidate counts (after COLLECT)
-    // recomputes only the rows whose candidate arrays overflowed and skips
-    // sub-tiles that have none.
-    bool keep[QB];
-    bool wave_rows = bact[0];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) keep[b] = qvalid[b];
-    if constexpr (MODE == M_SELECT && KP > 16) {
-      if (a.cand_cnt != nullptr) {
-        const int64_t r = qrow[0] * H + t.h;
-        keep[0] = qvalid[0] && (a.cand_cnt[2 * r] > a.cap || a.cand_cnt[2 * r + 1] > a.cap);
-        wave_rows = __ballot(keep[0]) != 0ull;
-        if (tid == 0) *wg_flag = 0;
-        __syncthreads();
-        if (wave_rows && lane == 0) *wg_flag = 1;
-        __syncthreads();
-        if (*wg_flag == 0) return;            // uniform over the workgroup
-      }
-    }
-    const bool wave_active = wave_rows;
-    const int aoff = lane * 16;
-
-    // Lists: slots [0, KP-topk) hold +inf sentinels that nothing displaces, so
-    // the live top-k occupies the tail and its k-th score is ls[.][KP-1].
-    const int nsent = KP - topk;
-    float ls[QB][KP];
-    int lj[QB][KP];
-#pragma unroll
-    for (int b = 0; b < QB; ++b)
-#pragma unroll
-      for (int i = 0; i < KP; ++i) {
-        ls[b][i] = i < nsent ? kInf : -kInf;
-        lj[b][i] = -1;
-      }
-    float thr[QB], cm[QB];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      cm[b] = -kInf;
-      thr[b] = kInf;
-      if constexpr (!PRE) {
-        if (qvalid[b]) thr[b] = next_down(thr_buf[qrow[b] * H + t.h]);
-      }
-    }
-    // Q operands and thresholds have arrived before the first key load is
-    // issued, so the chunk loop waits on key loads only.
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-#pragma unroll
-    for (int j = 0; j < S::NBUF - 1; ++j)
-      if (j < nproc) issue(t, j * SAMPLE, j, wave, lane);
-
-    // Scored sub-blocks: all of the first nproc - 1 scored chunks, plus the
-    // part of the last one that holds keys.
-    const int last_keys = (int)(nkeys - (int64_t)(nproc - 1) * SAMPLE * S::TK);
-    const int nsub = (nproc - 1) * S::SUBT + ((last_keys < S::TK ? last_keys : S::TK) + 31) / 32;
-    // Key ranges per lane half: a query's bound is the k-th largest of
-    // 2 * NCH range maxima, so long lists need proportionally more ranges.
-    constexpr int NCH = KP <= 16 ? SCAN_CHUNKS : 4 * KP;
-    const int spc = (nsub + NCH - 1) / NCH;                   // sub-blocks per range
-    int cleft = spc;                                          // sub-blocks left in chunk
-    int cnt = 0;
-    uint2* cb = cbuf + wave * SCAN_CAP * 64 + lane;           // entry c at cb[c * 64]
-    // COLLECT: candidates of row r, this lane's half, go to
-    // cand[(lhalf * cap + n) * NH + r] for n < cap; ccnt keeps counting past
-    // cap so that overflow is visible.
-    const int64_t NH = N * H;
-    int ccnt[QB];
-    int64_t crow[QB];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      ccnt[b] = 0;
-      crow[b] = qrow[b] * H + t.h;
-    }
-
-    auto drain = [&]() __attribute__((always_inline)) {
-      for (int c = 0; __ballot(c < cnt) != 0ull; ++c) {
-        if (c < cnt) {
-          const uint2 e = cb[c * 64];
-          const float sv = __uint_as_float(e.x);
-          const int key = (int)(e.y & 0x7fffffffu);
-          const int tag = (int)(e.y >> 31);
-#pragma unroll
-          for (int b = 0; b < QB; ++b) {
-            if (tag == b && sv > thr[b]) {
-              list_insert<KP>(ls[b], lj[b], sv, key);
-              thr[b] = fmaxf(thr[b], ls[b][KP - 1]);
-            }
-          }
-        }
-      }
-      cnt = 0;
-    };
-
-    for (int j = 0; j < nproc; ++j) {
-      const int c = j * SAMPLE;
-      // Chunk c's loads (LPW instructions per wavefront) were followed by
-      // those of at most NBUF - 2 later chunks.
-      if constexpr (S::NBUF == 3) {
-        static_assert(S::LPW <= 15, "vmcnt field");
-        if (j + 1 < nproc) __builtin_amdgcn_s_waitcnt(0x0f70 | S::LPW);
-        else __builtin_amdgcn_s_waitcnt(0x0f70);
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0f70);
-      }
-      __syncthreads();
-      if (j + S::NBUF - 1 < nproc)
-        issue(t, (j + S::NBUF - 1) * SAMPLE, (j + S::NBUF - 1) % S::NBUF, wave, lane);
-      if (!wave_active) continue;
-      const unsigned char* kc = kbuf + (j % S::NBUF) * S::CHUNK_BYTES;
-      const int crel = c * S::TK;                 // first key of the chunk, graph-relative
-      const int nk = (int)nkeys;
-      const bool partial = crel + S::TK > nk;
-
-      // Sub-blocks are processed in batches of BS: all LDS reads of the
-      // batch, then all its MFMAs (independent accumulation chains), then the
-      // scores, so a wavefront keeps several MFMAs in flight.
-      constexpr int BS = PassCfg<MODE>::BATCH < S::SUBT ? PassCfg<MODE>::BATCH : S::SUBT;
-      static_assert(S::SUBT % BS == 0, "batches tile the chunk");
-      floatx16_t acc[BS][QB];
-      bf16x8_t areg[BS][S::NM];
-      auto aload = [&](int st, int slot) __attribute__((always_inline)) {
-#pragma unroll
-        for (int m = 0; m < S::NM; ++m)
-          areg[slot][m] =
-              *reinterpret_cast<const bf16x8_t*>(kc + (st * S::NM + m) * 1024 + aoff);
-      };
-      auto mfma = [&](int slot_a, int slot) __attribute__((always_inline)) {
-#pragma unroll
-        for (int b = 0; b < QB; ++b) acc[slot][b] = floatx16_t{};
-#pragma unroll
-        for (int m = 0; m < S::NM; ++m) {
-#pragma unroll
-          for (int b = 0; b < QB; ++b)
-            if (bact[b])
-              acc[slot][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  areg[slot_a][m], qb[b][m], acc[slot][b], 0, 0, 0);
-        }
-      };
-      auto examine = [&](int st, int slot) __attribute__((always_inline)) {
-        // acc[r] = <k_key, q_query>, key = key0 + 8*(r/4) + (r%4), query = lane%32.
-        const int rel0 = crel + st * 32 + 4 * lhalf;
-        const int key0 = (int)t.kb + rel0;
-        floatx16_t(&s)[QB] = acc[slot];
-        if (partial) {
-#pragma unroll
-          for (int b = 0; b < QB; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (rel0 + 8 * (r >> 2) + (r & 3) >= nk) s[b][r] = -kInf;
-        }
-        if constexpr (PRE) {
-#pragma unroll
-          for (int b = 0; b < QB; ++b)
-            cm[b] = fmaxf(fmaxf(fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])),
-                                fmaxf(fmaxf(s[b][4], s[b][5]), fmaxf(s[b][6], s[b][7]))),
-                          fmaxf(fmaxf(fmaxf(s[b][8], s[b][9]), fmaxf(s[b][10], s[b][11])),
-                                fmaxf(fmaxf(s[b][12], s[b][13]),
-                                      fmaxf(fmaxf(s[b][14], s[b][15]), cm[b]))));
-          const int ti = j * S::SUBT + st;            // scored sub-block index, uniform
-          if (--cleft == 0 || ti + 1 == nsub) {
-            cleft = spc;
-#pragma unroll
-            for (int b = 0; b < QB; ++b) {
-              if (cm[b] > ls[b][KP - 1]) value_insert<KP>(ls[b], cm[b]);
-              cm[b] = -kInf;
-            }
-          }
-        } else if constexpr (MODE == M_COLLECT) {
-          float g[QB][4], mx[QB];
-#pragma unroll
-          for (int b = 0; b < QB; ++b) {
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-              g[b][qq] = fmaxf(fmaxf(s[b][4 * qq], s[b][4 * qq + 1]),
-                               fmaxf(s[b][4 * qq + 2], s[b][4 * qq + 3]));
-            mx[b] = fmaxf(fmaxf(g[b][0], g[b][1]), fmaxf(g[b][2], g[b][3]));
-          }
-          bool hit = false;
-#pragma unroll
-          for (int b = 0; b < QB; ++b) hit = hit || (mx[b] > thr[b]);
-          if (__ballot(hit) != 0ull) {
-#pragma unroll
-            for (int b = 0; b < QB; ++b)
-#pragma unroll
-              for (int qq = 0; qq < 4; ++qq) {
-                if (__ballot(g[b][qq] > thr[b]) != 0ull) {
-#pragma unroll
-                  for (int r = 0; r < 4; ++r) {
-                    const float sv = s[b][4 * qq + r];
-                    if (sv > thr[b]) {
-                      if (ccnt[b] < a.cap)
-                        a.cand[(int64_t)(lhalf * a.cap + ccnt[b]) * NH + crow[b]] =
-                            make_uint2(__float_as_uint(sv), (unsigned)(key0 + 8 * qq + r));
-                      ++ccnt[b];
-                    }
-                  }
-                }
-              }
-          }
-        } else {
-          float g[QB][4], mx[QB];
-#pragma unroll
-          for (int b = 0; b < QB; ++b) {
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-              g[b][qq] = fmaxf(fmaxf(s[b][4 * qq], s[b][4 * qq + 1]),
-                               fmaxf(s[b][4 * qq + 2], s[b][4 * qq + 3]));
-            mx[b] = fmaxf(fmaxf(g[b][0], g[b][1]), fmaxf(g[b][2], g[b][3]));
-          }
-          bool hit = false;
-#pragma unroll
-          for (int b = 0; b < QB; ++b) hit = hit || (mx[b] > thr[b]);
-          if (__ballot(hit) != 0ull) {
-            // Appends go in halves of two quarters (at most 8 = SCAN_CAP per
-            // lane): make room first, so each half has a single drain site
-            // and the buffer index stays below SCAN_CAP.
-            static_assert(SCAN_CAP >= 8, "a half sub-block appends up to 8 scores");
-#pragma unroll
-            for (int b = 0; b < QB; ++b)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              int room = cnt;
-#pragma unroll
-              for (int qq = 2 * hf; qq < 2 * hf + 2; ++qq) room += g[b][qq] > thr[b] ? 4 : 0;
-              if (__ballot(room > SCAN_CAP) != 0ull) drain();
-#pragma unroll
-              for (int qq = 2 * hf; qq < 2 * hf + 2; ++qq) {
-                if (__ballot(g[b][qq] > thr[b]) != 0ull) {
-#pragma unroll
-                  for (int r = 0; r < 4; ++r) {
-                    const float sv = s[b][4 * qq + r];
-                    if (sv > thr[b]) {
-                      cb[cnt * 64] = make_uint2(__float_as_uint(sv),
-                                                (unsigned)(key0 + 8 * qq + r) |
-                                                    ((unsigned)b << 31));
-                      ++cnt;
-                    }
-                  }
-                }
-              }
-            }
-          }
-        }
-      };
-#pragma unroll
-      for (int st0 = 0; st0 < S::SUBT; st0 += BS) {
-        if (crel + st0 * 32 >= nk) break;       // only padding left in a last chunk
-#pragma unroll
-        for (int i = 0; i < BS; ++i) aload(st0 + i, i);
-#pragma unroll
-        for (int i = 0; i < BS; ++i) mfma(i, i);
-#pragma unroll
-        for (int i = 0; i < BS; ++i) examine(st0 + i, i);
-      }
-    }
-    if (!wave_active) return;
-
-    if constexpr (PRE) {
-      // k-th largest chunk maximum over both halves of each query.
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        float ps[KP];
-#pragma unroll
-        for (int i = 0; i < KP; ++i) ps[i] = __shfl_xor(ls[b][i], 32);
-#pragma unroll
-        for (int i = 0; i < KP; ++i)
-          if (i >= nsent && ps[i] > ls[b][KP - 1]) value_insert<KP>(ls[b], ps[i]);
-        if (qvalid[b] && lhalf == 0) thr_buf[qrow[b] * H + t.h] = ls[b][KP - 1];
-      }
-    } else if constexpr (MODE == M_COLLECT) {
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-        if (qvalid[b]) a.cand_cnt[2 * crow[b] + lhalf] = ccnt[b];
-    } else {
-      drain();
-      // Merge the two half-lists of each query by rank: live entry i of my
-      // list (slots [nsent, KP)) lands at (i - nsent) + the number of partner
-      // live entries ordered before it.  Lower-half lanes win exact (score,
-      // id) ties, which only padding entries (-inf, -1) can produce.
-      const bool lower = lhalf == 0;
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        float ps[KP];
-        int pj[KP];
-#pragma unroll
-        for (int i = 0; i < KP; ++i) {
-          ps[i] = __shfl_xor(ls[b][i], 32);
-          pj[i] = __shfl_xor(lj[b][i], 32);
-        }
-        if (keep[b]) {
-          int32_t* oi = out_idx + (qrow[b] * H + t.h) * topk;
-          float* os = out_score + (qrow[b] * H + t.h) * topk;
-#pragma unroll
-          for (int i = 0; i < KP; ++i) {
-            if (i >= nsent) {
-              int rank = i - nsent;
-#pragma unroll
-              for (int u = 0; u < KP; ++u) {
-                const bool before =
-                    u >= nsent && (ps[u] > ls[b][i] ||
-                                   (ps[u] == ls[b][i] && (lower ? pj[u] < lj[b][i]
-                                                                : pj[u] <= lj[b][i])));
-                rank += before ? 1 : 0;
-              }
-              if (rank < topk) {
-                oi[rank] = lj[b][i];
-                os[rank] = lj[b][i] < 0 ? -kInf : ls[b][i];
-              }
-            }
-          }
-        }
-      }
-    }
-  }
-};
-
-// Persistent grid for one graph: nwg workgroups split the H * nbph query
-// blocks (32 rows each) into equal contiguous ranges.  Batched graphs: one
-// workgroup per (planned tile, head).
-template <int D, int KP, int MODE>
-__global__ __launch_bounds__(scan_waves(KP) * 64) void score_topk_kernel(ScanArgs a, int nwg) {
-  const int64_t N = a.N;
-  const int H = a.H;
-  const int2* tiles = a.tiles;
-  const int32_t* offsets = a.offsets;
-  constexpr int W = scan_waves(KP);
-  constexpr int SUB_ROWS = W * QB * 32;
-  using S = ScanShape<D, MODE, W>;
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[S::NBUF * S::CHUNK_BYTES];
-  __shared__ __attribute__((aligned(16))) uint2 cbuf[MODE == M_SELECT ? W * SCAN_CAP * 64 : 1];
-  __shared__ int wg_flag;
-  const unsigned kbuf_lds =
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kbuf;
-  Scanner<D, KP, MODE> sc{kbuf, kbuf_lds, cbuf,   &wg_flag, a,     a.q,   a.k,
-                          a.perm, a.N,    a.H,    a.topk,   a.thr, a.idx, a.score};
-  // Query blocks [b, be) of the flattened (head, 32-row block) space for one
-  // graph; a single planned sub-tile for batched graphs.
-  const int64_t nbph = (N + 31) / 32;
-  int64_t b = 0, be = 0;
-  int rh = 0;
-  int64_t rq0 = 0, rq1 = 0, rkb = 0, rke = 0;
-  if (tiles == nullptr) {
-    // Logical id: the 8 XCDs receive workgroups round-robin; give each XCD a
-    // contiguous range so its workgroups share a head (and its keys in L2).
-    const int per = nwg / 8;
-    const int L = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    const int64_t total = nbph * H;
-    b = total * L / nwg;
-    be = total * (L + 1) / nwg;
-  } else {
-    const int2 tl = tiles[blockIdx.x / H];
-    if (tl.x < 0) return;                 // beyond the planned tiles
-    rh = (int)(blockIdx.x % H);
-    rkb = offsets[tl.x];
-    rke = offsets[tl.x + 1];
-    if (tl.y >= rke) return;
-    rq0 = tl.y;
-    rq1 = tl.y + SUB_ROWS < rke ? tl.y + SUB_ROWS : rke;
-    be = 1;
-  }
-  while (b < be) {
-    SubTile st;
-    if (tiles == nullptr) {
-      // Spread the remaining blocks evenly over the sub-tiles still needed.
-      const int h = (int)(b / nbph);
-      const int64_t nb0 = b % nbph;
-      const int64_t rem = be - b;
-      const int64_t nst = (rem + W * QB - 1) / (W * QB);
-      int64_t n = (rem + nst - 1) / nst;
-      n = n < nbph - nb0 ? n : nbph - nb0;
-      st = SubTile{h, nb0 * 32, (nb0 + n) * 32 < N ? (nb0 + n) * 32 : N, 0, N};
-      b += n;
-    } else {
-      st = SubTile{rh, rq0, rq1, rkb, rke};
-      b = be;
-    }
-    sc.run(st);
-  }
-}
 
 // ------------------------------------------------------------------ tile plan
 constexpr int PLAN_THREADS = 1024;
@@ -652,132 +54,6 @@ __global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B, int
   tiles[t] = make_int2(lo, offsets[lo] + (int)(t - tile_start[lo]) * tile_rows);
 }
 
-// Co-resident workgroups of a kernel on this device (one graph: the
-// persistent grid size, a multiple of 8 so each XCD gets an equal share).
-template <typename Kern>
-int resident_workgroups(Kern kern, int threads) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
-                                                   threads, 0) != hipSuccess)
-    return 0;
-  const int n = cus * (per_cu > 0 ? per_cu : 1);
-  return n >= 8 ? n - n % 8 : 8;
-}
-
-template <int D, int KP, int MODE>
-hipError_t launch_pass(const ScanArgs& a, hipStream_t s) {
-  auto kern = score_topk_kernel<D, KP, MODE>;
-  constexpr int threads = scan_waves(KP) * 64;
-  int nwg = 0;
-  dim3 grid;
-  if (a.tiles == nullptr) {
-    nwg = resident_workgroups(kern, threads);
-    if (nwg <= 0) return hipErrorInvalidDevice;
-    grid = dim3((unsigned)nwg);
-  } else {
-    grid = dim3((unsigned)(a.max_tiles * a.H));
-  }
-  hipLaunchKernelGGL(kern, grid, dim3(threads), 0, s, a, nwg);
-  return hipGetLastError();
-}
-
-// Insert (s, j) into a descending list under (score descending, id
-// ascending); candidates may come in any order.
-template <int KP>
-__device__ __forceinline__ void ordered_insert(float (&ls)[KP], int (&lj)[KP], float s, int j) {
-  bool b[KP];
-#pragma unroll
-  for (int t = 0; t < KP; ++t) b[t] = s > ls[t] || (s == ls[t] && (unsigned)j < (unsigned)lj[t]);
-#pragma unroll
-  for (int t = KP - 1; t >= 1; --t) {
-    ls[t] = b[t - 1] ? ls[t - 1] : (b[t] ? s : ls[t]);
-    lj[t] = b[t - 1] ? lj[t - 1] : (b[t] ? j : lj[t]);
-  }
-  ls[0] = b[0] ? s : ls[0];
-  lj[0] = b[0] ? j : lj[0];
-}
-
-// Top-k of each row's collected candidates, one thread per row.  Rows whose
-// arrays overflowed are left to the SELECT pass.  Empty slots hold (-inf, -1)
-// and rank after every candidate ((unsigned)-1 is the largest id); +inf
-// sentinels fill slots [0, KP - topk).
-template <int KP>
-__global__ __launch_bounds__(256) void collect_topk_kernel(ScanArgs a) {
-  const int64_t NH = a.N * a.H;
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= NH) return;
-  const int c0 = a.cand_cnt[2 * r], c1 = a.cand_cnt[2 * r + 1];
-  if (c0 > a.cap || c1 > a.cap) return;
-  const int nsent = KP - a.topk;
-  float ls[KP];
-  int lj[KP];
-#pragma unroll
-  for (int i = 0; i < KP; ++i) {
-    ls[i] = i < nsent ? kInf : -kInf;
-    lj[i] = -1;
-  }
-  for (int hf = 0; hf < 2; ++hf) {
-    const int n = hf ? c1 : c0;
-    const uint2* src = a.cand + (int64_t)hf * a.cap * NH + r;
-    for (int u = 0; u < n; ++u) {
-      const uint2 e = src[(int64_t)u * NH];
-      const float sv = __uint_as_float(e.x);
-      const int j = (int)e.y;
-      if (sv > ls[KP - 1] || (sv == ls[KP - 1] && (unsigned)j < (unsigned)lj[KP - 1]))
-        ordered_insert<KP>(ls, lj, sv, j);
-    }
-  }
-  int32_t* oi = a.idx + r * a.topk;
-  float* os = a.score + r * a.topk;
-#pragma unroll
-  for (int i = 0; i < KP; ++i) {
-    if (i >= nsent) {
-      oi[i - nsent] = lj[i];
-      os[i - nsent] = lj[i] < 0 ? -kInf : ls[i];
-    }
-  }
-}
-
-template <int D, int KP>
-hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
-  hipError_t e = launch_pass<D, KP, M_THRESH>(a, s);
-  if (e != hipSuccess) return e;
-  if constexpr (KP > 16) {
-    // Long lists: collect candidates, select from them, then recompute the
-    // rows whose candidate arrays overflowed (that pass usually only checks
-    // the counts).
-    e = launch_pass<D, KP, M_COLLECT>(a, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(collect_topk_kernel<KP>, dim3((unsigned)ceil_div(a.N * a.H, 256)),
-                       dim3(256), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_pass<D, KP, M_SELECT>(a, s);
-  } else {
-    ScanArgs b = a;
-    b.cand_cnt = nullptr;                      // SELECT writes every row
-    return launch_pass<D, KP, M_SELECT>(b, s);
-  }
-}
-
-template <int D>
-hipError_t launch_scan_d(int kp, const ScanArgs& a, hipStream_t s) {
-  switch (kp) {
-    case 5: return launch_scan_t<D, 5>(a, s);
-    case 8: return launch_scan_t<D, 8>(a, s);
-    case 15: return launch_scan_t<D, 15>(a, s);
-    case 16: return launch_scan_t<D, 16>(a, s);
-    case 32: return launch_scan_t<D, 32>(a, s);
-    case 45: return launch_scan_t<D, 45>(a, s);
-    case 48: return launch_scan_t<D, 48>(a, s);
-    case 64: return launch_scan_t<D, 64>(a, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 // ------------------------------------------------------------ query order
 // Queries of one head are grouped by a 12-bit sign-random-projection code of
 // q (Rademacher directions fixed by the constants below), so that the 32
@@ -809,10 +85,13 @@ __global__ void lsh_code_kernel(const uint16_t* __restrict__ Q, int64_t N, int H
   if (r >= N * H) return;
   const int64_t i = r / H;
   const int h = (int)(r % H);
-  float x[D];
+  // The code uses the first min(D, 64) elements (for split rows: the high
+  // parts).
+  constexpr int DH = D < 64 ? D : 64;
+  float x[DH];
   const uint4* src = reinterpret_cast<const uint4*>(Q + r * D);
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
+  for (int c = 0; c < DH / 8; ++c) {
     const uint4 w = src[c];
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -826,7 +105,7 @@ __global__ void lsh_code_kernel(const uint16_t* __restrict__ Q, int64_t N, int H
   for (int b = 0; b < LSH_BITS; ++b) {
     float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < D; ++c) {
+    for (int c = 0; c < (D < 64 ? D : 64); ++c) {
       const bool neg = (kLshSigns[b][c >> 5] >> (c & 31)) & 1u;
       acc += neg ? -x[c] : x[c];
     }
@@ -888,10 +167,17 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
   const unsigned rows = (unsigned)ceil_div(N * H, 256);
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, s,
                      counts, nb);
-  if (d == 32)
-    hipLaunchKernelGGL(lsh_code_kernel<32>, dim3(rows), dim3(256), 0, s, q, N, H, codes, counts);
-  else
-    hipLaunchKernelGGL(lsh_code_kernel<64>, dim3(rows), dim3(256), 0, s, q, N, H, codes, counts);
+  switch (d) {
+    case 32: hipLaunchKernelGGL(lsh_code_kernel<32>, dim3(rows), dim3(256), 0, s, q, N, H,
+                                codes, counts); break;
+    case 64: hipLaunchKernelGGL(lsh_code_kernel<64>, dim3(rows), dim3(256), 0, s, q, N, H,
+                                codes, counts); break;
+    case 96: hipLaunchKernelGGL(lsh_code_kernel<96>, dim3(rows), dim3(256), 0, s, q, N, H,
+                                codes, counts); break;
+    case 192: hipLaunchKernelGGL(lsh_code_kernel<192>, dim3(rows), dim3(256), 0, s, q, N, H,
+                                 codes, counts); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Exclusive scan over (head, code, copy): head h's positions start at h*N.
@@ -904,9 +190,13 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
 
 hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s) {
   const int kp = scan_list_len(args.topk);
-  if (d == 32) return launch_scan_d<32>(kp, args, s);
-  if (d == 64) return launch_scan_d<64>(kp, args, s);
-  return hipErrorInvalidValue;
+  switch (d) {
+    case 32: return launch_scan_d32(kp, args, s);
+    case 64: return launch_scan_d64(kp, args, s);
+    case 96: return launch_scan_d96(kp, args, s);
+    case 192: return launch_scan_d192(kp, args, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kmip

@@ -1,0 +1,9 @@
+// Score-scan kernels for split-precision rows: 192 bf16 elements standing for
+// 64 fp32 elements (three bf16 terms per product).
+#include "kmip_scan_kernels.h"
+
+namespace kmip {
+hipError_t launch_scan_d192(int kp, const ScanArgs& a, hipStream_t s) {
+  return launch_scan_d<192>(kp, a, s);
+}
+}  // namespace kmip

@@ -1,0 +1,8 @@
+// Score-scan kernels for rows of 32 bf16 elements.
+#include "kmip_scan_kernels.h"
+
+namespace kmip {
+hipError_t launch_scan_d32(int kp, const ScanArgs& a, hipStream_t s) {
+  return launch_scan_d<32>(kp, a, s);
+}
+}  // namespace kmip

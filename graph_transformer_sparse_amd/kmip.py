@@ -53,13 +53,20 @@ def lib() -> ctypes.CDLL:
     L.kmip_score_topk.restype = i32
     L.kmip_gather_softmax_av.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp]
     L.kmip_gather_softmax_av.restype = i32
+    L.kmip_forward_f32_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    L.kmip_forward_f32_workspace_bytes.restype = sz
+    L.kmip_forward_f32.argtypes = L.kmip_forward.argtypes
+    L.kmip_forward_f32.restype = i32
+    L.kmip_backward_f32.argtypes = L.kmip_backward.argtypes
+    L.kmip_backward_f32.restype = i32
     _lib = L
     return L
 
 
 EXPORTED = ["kmip_status_string", "kmip_version", "kmip_forward_workspace_bytes",
             "kmip_backward_workspace_bytes", "kmip_forward", "kmip_backward",
-            "kmip_score_topk", "kmip_gather_softmax_av"]
+            "kmip_score_topk", "kmip_gather_softmax_av", "kmip_forward_f32_workspace_bytes",
+            "kmip_forward_f32", "kmip_backward_f32"]
 
 
 def status_string(status: int) -> str:
@@ -78,6 +85,10 @@ def backward_workspace_bytes(N: int, H: int, d: int, topk: int, num_graphs: int 
     return int(lib().kmip_backward_workspace_bytes(N, H, d, topk, num_graphs))
 
 
+def forward_f32_workspace_bytes(N: int, H: int, d: int, topk: int, num_graphs: int = 0) -> int:
+    return int(lib().kmip_forward_f32_workspace_bytes(N, H, d, topk, num_graphs))
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -88,10 +99,10 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _check_qkv(q, k, v):
+def _check_qkv(q, k, v, dtype=torch.bfloat16):
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor [N, H, d]")
+        if t.dtype != dtype or t.dim() != 3 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor [N, H, d]")
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k, v must have the same shape")
 
@@ -107,8 +118,11 @@ def _graphs(graph_offsets):
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
             graph_offsets: Optional[torch.Tensor] = None, *, out=None, topk_idx=None,
             topk_score=None, workspace=None, stream=None):
-    """k-MIP attention forward.  Returns (out fp32, topk_idx int32, topk_score fp32)."""
-    _check_qkv(q, k, v)
+    """k-MIP attention forward.  q, k, v bfloat16, or all float32 (the
+    split-precision fp32 entry point).  Returns (out fp32, topk_idx int32,
+    topk_score fp32)."""
+    f32 = q.dtype == torch.float32
+    _check_qkv(q, k, v, torch.float32 if f32 else torch.bfloat16)
     N, H, d = q.shape
     go, B = _graphs(graph_offsets)
     dev = q.device
@@ -118,15 +132,15 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
         topk_idx = torch.empty((N, H, topk), dtype=torch.int32, device=dev)
     if topk_score is None:
         topk_score = torch.empty((N, H, topk), dtype=torch.float32, device=dev)
-    need = forward_workspace_bytes(N, H, d, topk, B)
+    need = (forward_f32_workspace_bytes if f32 else forward_workspace_bytes)(N, H, d, topk, B)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    st = lib().kmip_forward(_ptr(q), _ptr(k), _ptr(v), N, H, d, topk, _ptr(go), B, _ptr(out),
-                            _ptr(topk_idx), _ptr(topk_score), _ptr(workspace), ws_bytes,
-                            _stream(stream))
+    fn = lib().kmip_forward_f32 if f32 else lib().kmip_forward
+    st = fn(_ptr(q), _ptr(k), _ptr(v), N, H, d, topk, _ptr(go), B, _ptr(out), _ptr(topk_idx),
+            _ptr(topk_score), _ptr(workspace), ws_bytes, _stream(stream))
     if st != KMIP_OK:
-        raise KmipError(st, "kmip_forward")
+        raise KmipError(st, "kmip_forward_f32" if f32 else "kmip_forward")
     return out, topk_idx, topk_score
 
 
@@ -171,8 +185,10 @@ def gather_softmax_av(v: torch.Tensor, topk_idx: torch.Tensor, topk_score: torch
 def backward(q, k, v, topk: int, topk_idx, topk_score, dout,
              graph_offsets: Optional[torch.Tensor] = None, *, dq=None, dk=None, dv=None,
              workspace=None, stream=None):
-    """k-MIP attention backward with the selection fixed.  Returns (dq, dk, dv) fp32."""
-    _check_qkv(q, k, v)
+    """k-MIP attention backward with the selection fixed.  q, k, v as given to
+    forward (bfloat16, or all float32).  Returns (dq, dk, dv) fp32."""
+    f32 = q.dtype == torch.float32
+    _check_qkv(q, k, v, torch.float32 if f32 else torch.bfloat16)
     N, H, d = q.shape
     go, B = _graphs(graph_offsets)
     dev = q.device
@@ -184,9 +200,10 @@ def backward(q, k, v, topk: int, topk_idx, topk_score, dout,
     need = backward_workspace_bytes(N, H, d, topk, B)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = lib().kmip_backward(_ptr(q), _ptr(k), _ptr(v), N, H, d, topk, _ptr(go), B,
-                             _ptr(topk_idx), _ptr(topk_score), _ptr(dout), _ptr(dq), _ptr(dk),
-                             _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream))
+    fn = lib().kmip_backward_f32 if f32 else lib().kmip_backward
+    st = fn(_ptr(q), _ptr(k), _ptr(v), N, H, d, topk, _ptr(go), B, _ptr(topk_idx),
+            _ptr(topk_score), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+            workspace.numel(), _stream(stream))
     if st != KMIP_OK:
-        raise KmipError(st, "kmip_backward")
+        raise KmipError(st, "kmip_backward_f32" if f32 else "kmip_backward")
     return dq, dk, dv

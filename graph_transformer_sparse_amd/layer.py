@@ -26,9 +26,11 @@ from . import kmip
 class KMIPAttentionFunction(torch.autograd.Function):
     """out = kmip_attention(q, k, v) for q, k, v of shape [N, H, d].
 
-    q, k and v may be fp32 or bf16; the kernels take bf16, so fp32 inputs
-    are rounded to bf16 first, and their gradients are those of the rounded
-    values (the cast passes gradients through unchanged).  The output and the
+    precision="bf16": q, k and v are rounded to bf16 (the bf16 entry points);
+    their gradients are those of the rounded values (the cast passes
+    gradients through unchanged).  precision="fp32": the fp32 entry points,
+    whose scan scores a three-term bf16 split of the fp32 values (fp32-level
+    scores at three times the matrix-core work).  The output and the
     gradients are fp32 (gradients are cast back to the input dtype).  The
     score is the unscaled inner product: fold a temperature such as 1/sqrt(d)
     into q.  The top-k selection is piecewise constant and carries no
@@ -36,8 +38,12 @@ class KMIPAttentionFunction(torch.autograd.Function):
     """
 
     @staticmethod
-    def forward(ctx, q, k, v, topk: int, graph_offsets: Optional[torch.Tensor] = None):
-        qb, kb, vb = (x.detach().to(torch.bfloat16).contiguous() for x in (q, k, v))
+    def forward(ctx, q, k, v, topk: int, graph_offsets: Optional[torch.Tensor] = None,
+                precision: str = "bf16"):
+        if precision not in ("bf16", "fp32"):
+            raise ValueError("precision must be 'bf16' or 'fp32'")
+        dt = torch.float32 if precision == "fp32" else torch.bfloat16
+        qb, kb, vb = (x.detach().to(dt).contiguous() for x in (q, k, v))
         out, idx, score = kmip.forward(qb, kb, vb, topk, graph_offsets)
         ctx.save_for_backward(qb, kb, vb, idx, score)
         ctx.topk = topk
@@ -54,13 +60,14 @@ class KMIPAttentionFunction(torch.autograd.Function):
         dq, dk, dv = kmip.backward(qb, kb, vb, ctx.topk, idx, score,
                                    dout.to(torch.float32).contiguous(), ctx.graph_offsets)
         tq, tk, tv = ctx.dtypes
-        return dq.to(tq), dk.to(tk), dv.to(tv), None, None
+        return dq.to(tq), dk.to(tk), dv.to(tv), None, None, None
 
 
-def kmip_attention(q, k, v, topk: int, graph_offsets: Optional[torch.Tensor] = None):
+def kmip_attention(q, k, v, topk: int, graph_offsets: Optional[torch.Tensor] = None,
+                   precision: str = "bf16"):
     """Differentiable k-MIP attention.  Returns (out [N, H, d] fp32,
     topk_idx [N, H, topk] int32, not differentiable)."""
-    return KMIPAttentionFunction.apply(q, k, v, topk, graph_offsets)
+    return KMIPAttentionFunction.apply(q, k, v, topk, graph_offsets, precision)
 
 
 class KMIPMultiheadAttention(nn.Module):
@@ -70,15 +77,17 @@ class KMIPMultiheadAttention(nn.Module):
     per head, each node attends to the topk nodes of its graph with the
     largest q.k; the heads are concatenated and projected back to C channels.
     The 1/sqrt(d) temperature is folded into the query projection, since the
-    kernels score the unscaled inner product.
+    kernels score the unscaled inner product.  precision selects the bf16 or
+    the fp32 entry points (KMIPAttentionFunction).
     """
 
     def __init__(self, channels: int, heads: int, head_dim: int, topk: int,
-                 bias: bool = True):
+                 bias: bool = True, precision: str = "bf16"):
         super().__init__()
         if head_dim not in (32, 64):
             raise ValueError("head_dim must be 32 or 64")
         self.heads, self.head_dim, self.topk = heads, head_dim, topk
+        self.precision = precision
         inner = heads * head_dim
         self.q_proj = nn.Linear(channels, inner, bias=bias)
         self.k_proj = nn.Linear(channels, inner, bias=bias)
@@ -93,7 +102,7 @@ class KMIPMultiheadAttention(nn.Module):
         q = (self.q_proj(x) * self.scale).view(shape)
         k = self.k_proj(x).view(shape)
         v = self.v_proj(x).view(shape)
-        out, idx = kmip_attention(q, k, v, self.topk, graph_offsets)
+        out, idx = kmip_attention(q, k, v, self.topk, graph_offsets, self.precision)
         self.last_topk_idx = idx
         return self.out_proj(out.reshape(n, self.heads * self.head_dim).to(x.dtype))
 

@@ -14,7 +14,8 @@
  * ---------------------------------------
  *  - Layout: q, k, v, out, dout, dq, dk, dv are row-major [N][H][d] (the
  *    natural x.view(N, H, d) of an [N, H*d] matrix).  q, k, v are bfloat16
- *    bit patterns (uint16); every other floating-point array is fp32.
+ *    bit patterns (uint16), or fp32 for the *_f32 entry points; every other
+ *    floating-point array is fp32.
  *    topk_idx / topk_score are [N][H][topk].
  *  - Ownership: every pointer is device memory owned by the caller.  The
  *    library allocates nothing, keeps no state between calls and is
@@ -144,6 +145,50 @@ kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t
                             const int32_t* topk_idx, const float* topk_score,
                             const float* dout, float* dq, float* dk, float* dv,
                             void* workspace, size_t workspace_bytes, kmip_stream_t stream);
+
+/*
+ * fp32-input variants.  The page's own k-MIP timings (same page, Tables 15
+ * and 16) use fp32 inputs and arithmetic; these entry points take q, k, v as
+ * fp32 [N][H][d] and are otherwise identical to kmip_forward / kmip_backward
+ * (outputs, layouts, ties, padding, errors).
+ *
+ * Scores.  Each element is split as x = hi + lo + r with hi = bf16(x) and
+ * lo = bf16(x - hi) (round to nearest even), and the matrix cores evaluate
+ * q_hi.k_hi + q_hi.k_lo + q_lo.k_hi with fp32 accumulation of exact bf16
+ * products.  The score error is at most about (3 * 2^-18 + 3d * 2^-24) *
+ * sum_c |q_c k_c|, where rounding q and k to bf16 first would cost ~2^-8
+ * relative.  The selection, its order and its tie rule refer to these
+ * scores.  topk_score then holds each selected key's score recomputed in
+ * fp32 from the fp32 rows (d products, fp32 accumulation), and the softmax
+ * and kmip_backward_f32 use those, so the gradients do not inherit the
+ * split's error; consecutive saved scores may therefore be out of order by
+ * up to twice the split error.  The weighted sum reads fp32 v rows.  Every
+ * element of q and k must be finite and below the bf16 maximum (~3.39e38) in
+ * magnitude.
+ *
+ * Workspace: kmip_forward_f32_workspace_bytes(...), which is the
+ * kmip_forward figure plus the split rows (about 12 * N * H * d bytes).
+ */
+size_t kmip_forward_f32_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs);
+
+kmip_status_t kmip_forward_f32(const float* q, const float* k, const float* v, int64_t N, int H,
+                               int d, int topk, const int32_t* graph_offsets, int num_graphs,
+                               float* out, int32_t* topk_idx, float* topk_score,
+                               void* workspace, size_t workspace_bytes, kmip_stream_t stream);
+
+/*
+ * Backward of kmip_forward_f32 (the selection held fixed, as kmip_backward):
+ * q, k, v fp32 [N][H][d], topk_idx / topk_score as written by
+ * kmip_forward_f32, workspace of kmip_backward_workspace_bytes(...) bytes.
+ * The products dout.v and k, q rows enter fp64 sums exactly, as in
+ * kmip_backward.
+ */
+kmip_status_t kmip_backward_f32(const float* q, const float* k, const float* v, int64_t N,
+                                int H, int d, int topk, const int32_t* graph_offsets,
+                                int num_graphs, const int32_t* topk_idx,
+                                const float* topk_score, const float* dout, float* dq,
+                                float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                                kmip_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,12 @@ def bf16_tensor(bits: np.ndarray, device="cuda"):
 
 
 def to_device(w, device="cuda"):
-    t = dict(q=bf16_tensor(w.q, device), k=bf16_tensor(w.k, device), v=bf16_tensor(w.v, device))
+    if getattr(w, "dtype", "bf16") == "f32":
+        t = {n: torch.from_numpy(np.ascontiguousarray(getattr(w, n))).to(device)
+             for n in ("q", "k", "v")}
+    else:
+        t = dict(q=bf16_tensor(w.q, device), k=bf16_tensor(w.k, device),
+                 v=bf16_tensor(w.v, device))
     t["offsets"] = (torch.from_numpy(w.offsets).to(device) if w.num_graphs > 1 else None)
     if w.dout is not None:
         t["dout"] = torch.from_numpy(w.dout).to(device)

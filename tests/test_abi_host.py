@@ -24,7 +24,7 @@ FAKE = ctypes.c_void_p(1 << 20)       # aligned, never dereferenced: validation 
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kmip_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kmip_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_symbols_exported():
@@ -92,3 +92,35 @@ def test_workspace_sizes_are_linear_in_n():
     assert 1.9 < b2 / b1 < 2.1                              # O(N * H * k)
     assert b(500000, 4, 32, 15) < 1.5e9
     assert f(0, 4, 32, 15, 0) == 0 and b(10, 4, 48, 15) == 0   # invalid shapes -> 0
+
+
+def _fwd32(N=128, H=2, d=32, topk=15, offs=None, B=0, v=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return kmip.lib().kmip_forward_f32(FAKE, FAKE, v, N, H, d, topk, offs, B, FAKE, FAKE, FAKE,
+                                       ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(v=None), INVALID), (dict(N=0), INVALID), (dict(B=2, offs=None), INVALID),
+    (dict(v=ctypes.c_void_p((1 << 20) + 4)), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(topk=65), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=4096), WORKSPACE),
+])
+def test_forward_f32_rejects(kw, status):
+    assert _fwd32(**kw) == status
+
+
+def test_backward_f32_rejects():
+    L = kmip.lib()
+    args = [FAKE, FAKE, FAKE, 128, 2, 32, 15, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert L.kmip_backward_f32(*args, FAKE, 100, None) == WORKSPACE
+    assert L.kmip_backward_f32(*args[:5], 16, *args[6:], FAKE, 1 << 40, None) == UNSUPPORTED
+    args[12] = None                                   # dq
+    assert L.kmip_backward_f32(*args, FAKE, 1 << 40, None) == INVALID
+
+
+def test_f32_workspace_adds_split_rows():
+    # The fp32 forward also holds q and k as bf16 rows of 3d elements.
+    for (N, H, d, k, B) in [(1000, 2, 32, 15, 0), (100000, 4, 32, 15, 0), (5000, 4, 64, 45, 7)]:
+        extra = kmip.forward_f32_workspace_bytes(N, H, d, k, B) - kmip.forward_workspace_bytes(
+            N, H, d, k, B)
+        assert 12 * N * H * d <= extra <= 12 * N * H * d + 512
+    assert kmip.forward_f32_workspace_bytes(10, 4, 48, 15, 0) == 0

@@ -124,3 +124,22 @@ def test_gps_layer_trains_one_step():
     lo = np.repeat(offs.cpu().numpy()[:-1], sizes)[:, None, None]
     hi = np.repeat(offs.cpu().numpy()[1:], sizes)[:, None, None]
     assert ((idx >= lo) & (idx < hi)).all()                   # keys stay inside the graph
+
+
+def test_autograd_function_fp32_precision():
+    """precision="fp32": the fp32 entry points, checked against the oracle on
+    the unrounded values."""
+    g = torch.Generator().manual_seed(11)
+    n, heads, d, topk = 600, 2, 64, 15
+    q, k, v, G = (torch.randn((n, heads, d), generator=g) for _ in range(4))
+    qg, kg, vg = (x.cuda().requires_grad_(True) for x in (q, k, v))
+    out, idx = kmip_attention(qg, kg, vg, topk, None, precision="fp32")
+    (out * G.cuda()).sum().backward()
+    qr, kr, vr = (_np(x).astype(np.float64) for x in (q, k, v))
+    sets = _np(idx).astype(np.int64)
+    ref = orc.attend_on_sets(qr, kr, vr, sets)
+    assert_rows_close(_np(out), ref["out"], "out")
+    dq, dk, dv = orc.kmip_backward_on_sets(qr, kr, vr, sets, _np(G).astype(np.float64))
+    assert_rows_close(_np(qg.grad), dq, "dq")
+    assert_rows_close(_np(kg.grad), dk, "dk")
+    assert_rows_close(_np(vg.grad), dv, "dv")

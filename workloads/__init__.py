@@ -6,8 +6,9 @@ that the CPU oracle and the GPU library see identical bytes.
 
 Inputs are drawn in float32 from NumPy's PCG64 generator and rounded to
 bfloat16 (round to nearest, ties to even) on the bit pattern.  Q, K and V are
-returned as uint16 bf16 bit patterns laid out [N][H][d]; the upstream gradient
-is float32 [N][H][d]; graph offsets are int32 [B+1].
+returned as uint16 bf16 bit patterns laid out [N][H][d] (or, with
+dtype="f32", as the float32 draws themselves); the upstream gradient is
+float32 [N][H][d]; graph offsets are int32 [B+1].
 
 The shapes stand in for the workloads of "k-Maximum Inner Product Attention
 for Graph Transformers and the Expressive Power of GraphGPS": the controlled
@@ -42,12 +43,13 @@ class Workload:
     d: int
     topk: int
     offsets: np.ndarray            # int32 [B+1]
-    q: np.ndarray                  # uint16 bf16 bits [N][H][d]
+    q: np.ndarray                  # uint16 bf16 bits [N][H][d] (float32 if dtype == "f32")
     k: np.ndarray
     v: np.ndarray
     dout: Optional[np.ndarray]     # float32 [N][H][d] or None (forward only)
     backward: bool
     meta: dict = field(default_factory=dict)
+    dtype: str = "bf16"
 
     @property
     def num_graphs(self) -> int:
@@ -74,7 +76,8 @@ def _clustered_qk(rng, n, heads, d, clusters, sigma):
 def make_workload(name: str, *, n: Optional[int] = None, heads: int, d: int, topk: int,
                   law: str = "iid", clusters: int = 0, sigma: float = 0.3,
                   graph_sizes: Optional[tuple] = None, num_graphs: int = 1,
-                  backward: bool = False, seed: int = SEED_BASE) -> Workload:
+                  backward: bool = False, seed: int = SEED_BASE,
+                  dtype: str = "bf16") -> Workload:
     """Draw one workload.
 
     Draw order: graph sizes (ragged batches only), cluster assignments,
@@ -82,6 +85,7 @@ def make_workload(name: str, *, n: Optional[int] = None, heads: int, d: int, top
     law="iid": Q, K, V ~ N(0, 1).  law="clustered": a node takes one cluster
     for both its Q and K row; centres ~ N(0, 1) independently per head;
     Q = centre + sigma*noise, K = centre + sigma*independent noise.
+    dtype="f32" keeps Q, K, V as float32 (same draws, no bf16 rounding).
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     if graph_sizes is not None:
@@ -102,11 +106,14 @@ def make_workload(name: str, *, n: Optional[int] = None, heads: int, d: int, top
         raise ValueError(law)
     v = rng.standard_normal((n, heads, d), dtype=np.float32)
     dout = rng.standard_normal((n, heads, d), dtype=np.float32) if backward else None
+    if dtype == "bf16":
+        q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    elif dtype != "f32":
+        raise ValueError(dtype)
     return Workload(name=name, n=n, heads=heads, d=d, topk=topk,
-                    offsets=offsets.astype(np.int32),
-                    q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v),
+                    offsets=offsets.astype(np.int32), q=q, k=k, v=v,
                     dout=dout, backward=backward,
-                    meta=dict(law=law, clusters=clusters, sigma=sigma, seed=seed))
+                    meta=dict(law=law, clusters=clusters, sigma=sigma, seed=seed), dtype=dtype)
 
 
 # The five workload families.  Ids fix the seeds (SEED_BASE + id).
@@ -144,24 +151,24 @@ def get_workload(name: str) -> Workload:
 
 def small_case(n: int, heads: int, d: int, topk: int, *, law: str = "iid", clusters: int = 0,
                graph_sizes=None, num_graphs: int = 1, backward: bool = True,
-               seed: int = 12345) -> Workload:
+               seed: int = 12345, dtype: str = "bf16") -> Workload:
     """A small seeded case for parity tests (sizes chosen by the caller)."""
     if graph_sizes is not None:
         return make_workload(f"small_ragged_{seed}", heads=heads, d=d, topk=topk, law=law,
                              clusters=clusters, graph_sizes=graph_sizes,
-                             num_graphs=num_graphs, backward=backward, seed=seed)
+                             num_graphs=num_graphs, backward=backward, seed=seed, dtype=dtype)
     return make_workload(f"small_{n}_{seed}", n=n, heads=heads, d=d, topk=topk, law=law,
-                         clusters=clusters, backward=backward, seed=seed)
+                         clusters=clusters, backward=backward, seed=seed, dtype=dtype)
 
 
 def with_offsets(name: str, sizes, heads: int, d: int, topk: int, *, law="iid",
-                 clusters=0, backward=True, seed=777) -> Workload:
+                 clusters=0, backward=True, seed=777, dtype: str = "bf16") -> Workload:
     """A case with explicit graph sizes (edge cases: tiny graphs, n_b < k, ...)."""
     sizes = np.asarray(sizes, dtype=np.int64)
     offsets = np.zeros(len(sizes) + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(sizes)
     n = int(offsets[-1])
     w = make_workload(name, n=n, heads=heads, d=d, topk=topk, law=law, clusters=clusters,
-                      backward=backward, seed=seed)
+                      backward=backward, seed=seed, dtype=dtype)
     w.offsets = offsets.astype(np.int32)
     return w

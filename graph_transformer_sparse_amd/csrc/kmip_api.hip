@@ -111,6 +111,24 @@ kmip_status_t score_topk_core(const uint16_t* q, const uint16_t* k, int64_t N, i
   return launch_status(launch_score_topk(a, d_rows, s));
 }
 
+// Argument checks of the selection (kmip_score_topk and kmip_forward).
+kmip_status_t check_topk_args(const void* q, const void* k, int64_t N, int H, int d, int topk,
+                              const int32_t* graph_offsets, int num_graphs,
+                              const int32_t* topk_idx, const float* topk_score,
+                              const void* workspace, size_t workspace_bytes) {
+  if (!q || !k || !topk_idx || !topk_score) return KMIP_ERR_INVALID_VALUE;
+  const kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
+  if (st != KMIP_OK) return st;
+  if (num_graphs > 1 && graph_offsets == nullptr) return KMIP_ERR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(topk_idx, 4) || !aligned(topk_score, 4))
+    return KMIP_ERR_INVALID_VALUE;
+  const bool single = single_graph(graph_offsets, num_graphs);
+  const size_t need = forward_ws(N, H, topk, single ? 0 : num_graphs);
+  if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
+  return KMIP_OK;
+}
+
 kmip_status_t backward_impl(const void* q, const void* k, const void* v, bool f32, int64_t N,
                             int H, int d, int topk, const int32_t* graph_offsets,
                             int num_graphs, const int32_t* topk_idx, const float* topk_score,
@@ -179,16 +197,9 @@ kmip_status_t kmip_score_topk(const void* q, const void* k, int64_t N, int H, in
                               const int32_t* graph_offsets, int num_graphs, int32_t* topk_idx,
                               float* topk_score, void* workspace, size_t workspace_bytes,
                               kmip_stream_t stream) {
-  if (!q || !k || !topk_idx || !topk_score) return KMIP_ERR_INVALID_VALUE;
-  kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
+  const kmip_status_t st = check_topk_args(q, k, N, H, d, topk, graph_offsets, num_graphs,
+                                           topk_idx, topk_score, workspace, workspace_bytes);
   if (st != KMIP_OK) return st;
-  if (num_graphs > 1 && graph_offsets == nullptr) return KMIP_ERR_INVALID_VALUE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(topk_idx, 4) || !aligned(topk_score, 4))
-    return KMIP_ERR_INVALID_VALUE;
-  const bool single = single_graph(graph_offsets, num_graphs);
-  const size_t need = forward_ws(N, H, topk, single ? 0 : num_graphs);
-  if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
-  if (!aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
   return score_topk_core(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), N,
                          H, d, topk, graph_offsets, num_graphs, topk_idx, topk_score,
                          static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
@@ -212,15 +223,19 @@ kmip_status_t kmip_forward(const void* q, const void* k, const void* v, int64_t 
                            float* out, int32_t* topk_idx, float* topk_score, void* workspace,
                            size_t workspace_bytes, kmip_stream_t stream) {
   if (!q || !k || !v || !out || !topk_idx || !topk_score) return KMIP_ERR_INVALID_VALUE;
-  if (!aligned(v, 16) || !aligned(out, 16)) {
-    const kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
-    return st != KMIP_OK ? st : KMIP_ERR_INVALID_VALUE;
-  }
-  const kmip_status_t st = kmip_score_topk(q, k, N, H, d, topk, graph_offsets, num_graphs,
-                                           topk_idx, topk_score, workspace, workspace_bytes,
-                                           stream);
+  kmip_status_t st = check_topk_args(q, k, N, H, d, topk, graph_offsets, num_graphs, topk_idx,
+                                     topk_score, workspace, workspace_bytes);
   if (st != KMIP_OK) return st;
-  return kmip_gather_softmax_av(v, N, H, d, topk, topk_idx, topk_score, out, stream);
+  if (!aligned(v, 16) || !aligned(out, 16)) return KMIP_ERR_INVALID_VALUE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const uint16_t* kb = static_cast<const uint16_t*>(k);
+  const uint16_t* vb = static_cast<const uint16_t*>(v);
+  char* w = static_cast<char*>(workspace);
+  st = score_topk_core(qb, kb, N, H, d, topk, graph_offsets, num_graphs, topk_idx, topk_score,
+                       w, s);
+  if (st != KMIP_OK) return st;
+  return launch_status(launch_gather_av(vb, N, H, d, topk, topk_idx, topk_score, out, s));
 }
 
 kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t N, int H,

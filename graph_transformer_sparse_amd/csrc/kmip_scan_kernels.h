@@ -105,29 +105,40 @@ struct ScanShape {
 
 // Insert (s, j) into a descending list.  The caller guarantees s beats the
 // k-th entry.  Keys reach a lane in ascending id order, so on equal scores
-// the entry already present (smaller id) stays first: strict compare.
+// the entry already present (smaller id) stays first: strict compare.  With
+// p the first slot that s beats, slot t >= 1 becomes ls[t] (t < p), s
+// (t = p) or ls[t-1] (t > p), which for a descending list is the median of
+// (ls[t], ls[t-1], s): one v_med3 per slot; ids follow the compares.
 template <int KP>
 __device__ __forceinline__ void list_insert(float (&ls)[KP], int (&lj)[KP], float s, int j) {
   bool b[KP];
 #pragma unroll
   for (int t = 0; t < KP; ++t) b[t] = s > ls[t];
+  if constexpr (KP <= 16) {
 #pragma unroll
-  for (int t = KP - 1; t >= 1; --t) {
-    ls[t] = b[t - 1] ? ls[t - 1] : (b[t] ? s : ls[t]);
-    lj[t] = b[t - 1] ? lj[t - 1] : (b[t] ? j : lj[t]);
+    for (int t = KP - 1; t >= 1; --t) {
+      lj[t] = b[t] ? (b[t - 1] ? lj[t - 1] : j) : lj[t];
+      ls[t] = __builtin_amdgcn_fmed3f(ls[t], ls[t - 1], s);
+    }
+    lj[0] = b[0] ? j : lj[0];
+    ls[0] = fmaxf(ls[0], s);
+  } else {
+    // Long lists live partly in scratch; this form keeps their spills small.
+#pragma unroll
+    for (int t = KP - 1; t >= 1; --t) {
+      ls[t] = b[t - 1] ? ls[t - 1] : (b[t] ? s : ls[t]);
+      lj[t] = b[t - 1] ? lj[t - 1] : (b[t] ? j : lj[t]);
+    }
+    ls[0] = b[0] ? s : ls[0];
+    lj[0] = b[0] ? j : lj[0];
   }
-  ls[0] = b[0] ? s : ls[0];
-  lj[0] = b[0] ? j : lj[0];
 }
 
 template <int KP>
 __device__ __forceinline__ void value_insert(float (&ls)[KP], float s) {
-  bool b[KP];
 #pragma unroll
-  for (int t = 0; t < KP; ++t) b[t] = s > ls[t];
-#pragma unroll
-  for (int t = KP - 1; t >= 1; --t) ls[t] = b[t - 1] ? ls[t - 1] : (b[t] ? s : ls[t]);
-  ls[0] = b[0] ? s : ls[0];
+  for (int t = KP - 1; t >= 1; --t) ls[t] = __builtin_amdgcn_fmed3f(ls[t], ls[t - 1], s);
+  ls[0] = fmaxf(ls[0], s);
 }
 
 // Largest float below x (x finite or -inf; -inf stays -inf).
@@ -147,6 +158,10 @@ struct SubTile {
 template <int D, int KP, int MODE>
 struct Scanner {
   static constexpr bool PRE = MODE == M_THRESH;
+  // uint2 entries of LDS per wavefront: the candidate buffer (SCAN_CAP per
+  // lane); after the last drain the same space holds the upper lanes' lists
+  // for the merge.
+  static constexpr int CBW = SCAN_CAP * 64;
   static constexpr int W = scan_waves(KP);    // wavefronts per workgroup
   using S = ScanShape<D, MODE, W>;
   // Chunk stride of this pass.  Long lists take a denser sample: their
@@ -295,7 +310,7 @@ struct Scanner {
     const int spc = (nsub + NCH - 1) / NCH;                   // sub-blocks per range
     int cleft = spc;                                          // sub-blocks left in chunk
     int cnt = 0;
-    uint2* cb = cbuf + wave * SCAN_CAP * 64 + lane;           // entry c at cb[c * 64]
+    uint2* cb = cbuf + wave * CBW + lane;                     // entry c at cb[c * 64]
     // COLLECT: candidates of row r, this lane's half, go to
     // cand[(lhalf * cap + n) * NH + r] for n < cap; ccnt keeps counting past
     // cap so that overflow is visible.
@@ -448,8 +463,10 @@ struct Scanner {
           for (int b = 0; b < QB; ++b) hit = hit || (mx[b] > thr[b]);
           if (__ballot(hit) != 0ull) {
             // Appends go in halves of two quarters (at most 8 = SCAN_CAP per
-            // lane): make room first, so each half has a single drain site
-            // and the buffer index stays below SCAN_CAP.
+            // lane): make room first, so each half has a single drain site.
+            // A lane with a hit in a quarter writes all four scores, without
+            // branches, at its next slot, which only advances on a hit (the
+            // room check keeps those slots below SCAN_CAP).
             static_assert(SCAN_CAP >= 8, "a half sub-block appends up to 8 scores");
 #pragma unroll
             for (int b = 0; b < QB; ++b)
@@ -461,16 +478,13 @@ struct Scanner {
               if (__ballot(room > SCAN_CAP) != 0ull) drain();
 #pragma unroll
               for (int qq = 2 * hf; qq < 2 * hf + 2; ++qq) {
-                if (__ballot(g[b][qq] > thr[b]) != 0ull) {
+                if (g[b][qq] > thr[b]) {
 #pragma unroll
                   for (int r = 0; r < 4; ++r) {
                     const float sv = s[b][4 * qq + r];
-                    if (sv > thr[b]) {
-                      cb[cnt * 64] = make_uint2(__float_as_uint(sv),
-                                                (unsigned)(key0 + 8 * qq + r) |
-                                                    ((unsigned)b << 31));
-                      ++cnt;
-                    }
+                    cb[cnt * 64] = make_uint2(__float_as_uint(sv),
+                                              (unsigned)(key0 + 8 * qq + r) | ((unsigned)b << 31));
+                    cnt += sv > thr[b] ? 1 : 0;
                   }
                 }
               }
@@ -509,38 +523,93 @@ struct Scanner {
         if (qvalid[b]) a.cand_cnt[2 * crow[b] + lhalf] = ccnt[b];
     } else {
       drain();
-      // Merge the two half-lists of each query by rank: live entry i of my
-      // list (slots [nsent, KP)) lands at (i - nsent) + the number of partner
-      // live entries ordered before it.  Lower-half lanes win exact (score,
-      // id) ties, which only padding entries (-inf, -1) can produce.
       const bool lower = lhalf == 0;
+      if constexpr (KP <= 16) {
+        static_assert(QB == 1 && SCAN_CAP * 64 >= 32 * 16, "32 rows of 16 entries per region");
+        // Two-pointer merge of the half-lists of each query (lanes l, l ^ 32)
+        // under (score descending, id ascending): the upper lane publishes its
+        // live entries, best first, in the drained candidate buffer; the lower
+        // lane walks them beside its own list and writes the top-k in order.
+        // Only padding entries (-inf, -1) can tie exactly; the lower lane's
+        // go first.
+        uint2* wl = cbuf + wave * CBW;
+        if (!lower) {
 #pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        float ps[KP];
-        int pj[KP];
-#pragma unroll
-        for (int i = 0; i < KP; ++i) {
-          ps[i] = __shfl_xor(ls[b][i], 32);
-          pj[i] = __shfl_xor(lj[b][i], 32);
+          for (int i = 0; i < KP; ++i)
+            if (i >= nsent)
+              wl[lrow * 16 + (i - nsent)] =
+                  make_uint2(__float_as_uint(ls[0][i]), (unsigned)lj[0][i]);
         }
-        if (keep[b]) {
-          int32_t* oi = out_idx + (qrow[b] * H + t.h) * topk;
-          float* os = out_score + (qrow[b] * H + t.h) * topk;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lower && keep[0]) {
+          int32_t* oi = out_idx + (qrow[0] * H + t.h) * topk;
+          float* os = out_score + (qrow[0] * H + t.h) * topk;
+          const uint2* pl = wl + lrow * 16;
+          int u = 0, r = 0;
+          uint2 pu = pl[0];
+          auto emit = [&](float sv, int j) __attribute__((always_inline)) {
+            const float sc = j < 0 ? -kInf : sv;
+            oi[r] = j;
+            os[r] = sc;
+            ++r;
+          };
 #pragma unroll
           for (int i = 0; i < KP; ++i) {
             if (i >= nsent) {
-              int rank = i - nsent;
-#pragma unroll
-              for (int u = 0; u < KP; ++u) {
-                const bool before =
-                    u >= nsent && (ps[u] > ls[b][i] ||
-                                   (ps[u] == ls[b][i] && (lower ? pj[u] < lj[b][i]
-                                                                : pj[u] <= lj[b][i])));
-                rank += before ? 1 : 0;
+              const float sv = ls[0][i];
+              const int j = lj[0][i];
+              while (r < topk && u < topk &&
+                     (__uint_as_float(pu.x) > sv ||
+                      (__uint_as_float(pu.x) == sv && (int)pu.y < j))) {
+                emit(__uint_as_float(pu.x), (int)pu.y);
+                ++u;
+                pu = pl[u < 16 ? u : 15];
               }
-              if (rank < topk) {
-                oi[rank] = lj[b][i];
-                os[rank] = lj[b][i] < 0 ? -kInf : ls[b][i];
+              if (r < topk) emit(sv, j);
+            }
+          }
+          while (r < topk) {                  // r < topk implies u < topk
+            emit(__uint_as_float(pu.x), (int)pu.y);
+            ++u;
+            pu = pl[u < 16 ? u : 15];
+          }
+        }
+      } else {
+        // Merge the two half-lists of each query by rank: live entry i of my
+        // list (slots [nsent, KP)) lands at (i - nsent) + the number of partner
+        // live entries ordered before it.  Lower-half lanes win exact (score,
+        // id) ties, which only padding entries (-inf, -1) can produce.
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          float ps[KP];
+          int pj[KP];
+#pragma unroll
+          for (int i = 0; i < KP; ++i) {
+            ps[i] = __shfl_xor(ls[b][i], 32);
+            pj[i] = __shfl_xor(lj[b][i], 32);
+          }
+          if (keep[b]) {
+            int32_t* oi = out_idx + (qrow[b] * H + t.h) * topk;
+            float* os = out_score + (qrow[b] * H + t.h) * topk;
+#pragma unroll
+            for (int i = 0; i < KP; ++i) {
+              if (i >= nsent) {
+                int rank = i - nsent;
+#pragma unroll
+                for (int u = 0; u < KP; ++u) {
+                  const bool before =
+                      u >= nsent && (ps[u] > ls[b][i] ||
+                                     (ps[u] == ls[b][i] && (lower ? pj[u] < lj[b][i]
+                                                                  : pj[u] <= lj[b][i])));
+                  rank += before ? 1 : 0;
+                }
+                if (rank < topk) {
+                  const float sc = lj[b][i] < 0 ? -kInf : ls[b][i];
+                  oi[rank] = lj[b][i];
+                  os[rank] = sc;
+                }
               }
             }
           }
@@ -562,8 +631,11 @@ __global__ __launch_bounds__(scan_waves(KP) * 64) void score_topk_kernel(ScanArg
   constexpr int W = scan_waves(KP);
   constexpr int SUB_ROWS = W * QB * 32;
   using S = ScanShape<D, MODE, W>;
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[S::NBUF * S::CHUNK_BYTES];
-  __shared__ __attribute__((aligned(16))) uint2 cbuf[MODE == M_SELECT ? W * SCAN_CAP * 64 : 1];
+  // One LDS block: the key ring, then (SELECT) the candidate buffers.
+  constexpr int KB = S::NBUF * S::CHUNK_BYTES;
+  constexpr int CB = MODE == M_SELECT ? W * Scanner<D, KP, MODE>::CBW * 8 : 0;
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[KB + CB];
+  uint2* cbuf = reinterpret_cast<uint2*>(kbuf + KB);
   const unsigned kbuf_lds =
       (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kbuf;
   Scanner<D, KP, MODE> sc{kbuf,   kbuf_lds, cbuf,   a,     a.q,   a.k,

@@ -16,7 +16,13 @@ summary (calibrated against a plain device copy), null once the scan sources
 differ from the ones profiled.  `cpu_baseline` times the fp64 oracle on a
 bounded sample of the same workload on the host cores.
 
+With --precision fp32 the same workload runs through the fp32 entry points
+(fp32 q, k, v; the scan scores three bf16 terms per product, so it does three
+times the bf16 MFMA work); the forward is then timed as one phase and the
+roofline counts the MFMA work of the split.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--precision bf16|fp32]
 """
 from __future__ import annotations
 
@@ -77,7 +83,10 @@ def cpu_baseline(w, nodes: int, seed: int = 7):
     contributions of the same rows) on a seeded sample of query nodes."""
     import numpy as np
     import oracle.kmip_oracle as orc
-    q, k, v = (orc.bf16_bits_to_f64(x) for x in (w.q, w.k, w.v))
+    if getattr(w, "dtype", "bf16") == "f32":
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (w.q, w.k, w.v))
+    else:
+        q, k, v = (orc.bf16_bits_to_f64(x) for x in (w.q, w.k, w.v))
     dout = w.dout.astype(np.float64) if w.dout is not None else None
     rng = np.random.default_rng(seed)
     rows = np.sort(rng.choice(w.n, size=min(nodes, w.n), replace=False))
@@ -106,6 +115,7 @@ def main():
     # The GPU's clocks settle over the first ~100 ms of sustained work.
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--precision", choices=("bf16", "fp32"), default="bf16")
     ap.add_argument("--cpu-nodes", type=int, default=16384,
                     help="query nodes in the CPU oracle sample (0 skips the CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -124,7 +134,8 @@ def main():
     from graph_transformer_sparse_amd import kmip
     from workloads import get_workload
 
-    w = get_workload(args.workload)
+    f32 = args.precision == "fp32"
+    w = get_workload(args.workload, dtype="f32" if f32 else "bf16")
     dev = torch.device("cuda", 0)
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -138,14 +149,18 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
             torch.bfloat16).to(dev)
 
-    q, k, v = bf16(w.q), bf16(w.k), bf16(w.v)
+    if f32:
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (w.q, w.k, w.v))
+    else:
+        q, k, v = bf16(w.q), bf16(w.k), bf16(w.v)
     offs = torch.from_numpy(w.offsets).to(dev) if w.num_graphs > 1 else None
     N, H, d, K = w.n, w.heads, w.d, w.topk
     dout = torch.from_numpy(w.dout).to(dev) if w.backward else None
     out = torch.empty((N, H, d), dtype=torch.float32, device=dev)
     idx = torch.empty((N, H, K), dtype=torch.int32, device=dev)
     score = torch.empty((N, H, K), dtype=torch.float32, device=dev)
-    fws = kmip.forward_workspace_bytes(N, H, d, K, w.num_graphs)
+    fws = (kmip.forward_f32_workspace_bytes if f32 else kmip.forward_workspace_bytes)(
+        N, H, d, K, w.num_graphs)
     fwork = torch.empty(max(fws, 1), dtype=torch.uint8, device=dev)
     if w.backward:
         dq, dk, dv = (torch.empty((N, H, d), dtype=torch.float32, device=dev) for _ in range(3))
@@ -156,11 +171,18 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        kmip.score_topk(q, k, K, offs, topk_idx=idx, topk_score=score, workspace=fwork,
-                        stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        kmip.gather_softmax_av(v, idx, score, out=out, stream=stream)
+        if f32:
+            # split rows, scan, fp32 rescoring and weighted sum: one call
+            kmip.forward(q, k, v, K, offs, out=out, topk_idx=idx, topk_score=score,
+                         workspace=fwork, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        else:
+            kmip.score_topk(q, k, K, offs, topk_idx=idx, topk_score=score, workspace=fwork,
+                            stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            kmip.gather_softmax_av(v, idx, score, out=out, stream=stream)
         if ev is not None:
             ev[2].record(stream)
         if w.backward:
@@ -184,7 +206,7 @@ def main():
     gather_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
     ms_per_step = wall * 1e3 / args.steps
-    flops = 2.0 * d * H * w.sum_nb2()
+    flops = 2.0 * d * H * w.sum_nb2() * (3 if f32 else 1)   # MFMA work of the scan
     scan_tflops = flops / (scan_ms.mean() * 1e-3) / 1e12
     rows = N * H
     g_bytes = rows * gather_bytes_per_row(d, K)
@@ -205,7 +227,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp32 (3-term bf16 split scan)" if f32 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "N": N, "H": H, "d": d, "k": K,
                    "graphs": w.num_graphs, "law": w.meta["law"],
@@ -213,15 +235,18 @@ def main():
                    if w.backward else "forward"},
         "roofline": {"bound": "mfma", "achieved": scan_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": scan_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": scan_traffic(w.name), "kernel": "score_topk_kernel",
+                     "traffic": None if f32 else scan_traffic(w.name),
+                     "kernel": "kmip_forward_f32 (split + scan + rescoring gather)" if f32
+                     else "score_topk_kernel",
                      "algorithmic_flop_per_launch": flops,
                      "avg_launch_ms": float(scan_ms.mean())},
-        "phases_ms": {"score_topk": float(scan_ms.mean()),
-                      "gather_softmax_av": float(gather_ms.mean()),
+        "phases_ms": {("forward_f32" if f32 else "score_topk"): float(scan_ms.mean()),
+                      "gather_softmax_av": None if f32 else float(gather_ms.mean()),
                       "backward": float(bwd_ms.mean()) if w.backward else None},
         "hbm_model": {
-            "gather_GBps": g_bytes / (gather_ms.mean() * 1e-3) / 1e9,
-            "gather_frac": g_bytes / (gather_ms.mean() * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "gather_GBps": None if f32 else g_bytes / (gather_ms.mean() * 1e-3) / 1e9,
+            "gather_frac": None if f32 else
+            g_bytes / (gather_ms.mean() * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "backward_GBps": (b_bytes / (bwd_ms.mean() * 1e-3) / 1e9) if w.backward else None,
             "backward_frac": (b_bytes / (bwd_ms.mean() * 1e-3) / 1e9 / PEAK_HBM_GBS)
             if w.backward else None,

@@ -143,10 +143,10 @@ WORKLOADS = {
 }
 
 
-def get_workload(name: str) -> Workload:
+def get_workload(name: str, dtype: str = "bf16") -> Workload:
     spec = dict(WORKLOADS[name])
     wid = spec.pop("id")
-    return make_workload(name, seed=SEED_BASE + wid, **spec)
+    return make_workload(name, seed=SEED_BASE + wid, dtype=dtype, **spec)
 
 
 def small_case(n: int, heads: int, d: int, topk: int, *, law: str = "iid", clusters: int = 0,

@@ -89,7 +89,7 @@ kmip_status_t score_topk_core(const uint16_t* q, const uint16_t* k, int64_t N, i
     int32_t* tile_start = reinterpret_cast<int32_t*>(w);
     int2* tiles = reinterpret_cast<int2*>(w + align256((size_t)(num_graphs + 1) * 4));
     w += align256((size_t)(num_graphs + 1) * 4) + align256((size_t)max_tiles * sizeof(int2));
-    const int tile_rows = scan_waves(scan_list_len(topk)) * SCAN_QPW;
+    const int tile_rows = scan_waves(scan_list_len(topk), true) * SCAN_QPW;
     st = launch_status(launch_tile_plan(graph_offsets, num_graphs, max_tiles, tile_rows,
                                         tile_start, tiles, s));
     if (st != KMIP_OK) return st;

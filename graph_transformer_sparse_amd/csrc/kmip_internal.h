@@ -43,8 +43,13 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int scan_list_len(int topk);
 
 // Wavefronts per scan workgroup for a list length: long register lists need
-// the VGPR budget of two wavefronts per SIMD.
-constexpr int scan_waves(int kp) { return kp <= 16 ? SCAN_WAVES : SCAN_WAVES_LONG; }
+// the VGPR budget of two wavefronts per SIMD.  Batched graphs use 8-wavefront
+// workgroups for short lists too: tiles of 256 rows waste less on each
+// graph's partial last tile, and two such workgroups share a CU, so one's
+// barrier stalls are covered by the other's work.
+constexpr int scan_waves(int kp, bool batched = false) {
+  return kp <= 16 && !batched ? SCAN_WAVES : SCAN_WAVES_LONG;
+}
 
 // Maximum number of query tiles for N nodes in num_graphs graphs (for the
 // smallest tile).

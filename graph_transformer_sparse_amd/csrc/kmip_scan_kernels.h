@@ -155,14 +155,13 @@ struct SubTile {
   int64_t kb, ke;     // key range of the graph
 };
 
-template <int D, int KP, int MODE>
+template <int D, int KP, int MODE, int W>
 struct Scanner {
   static constexpr bool PRE = MODE == M_THRESH;
   // uint2 entries of LDS per wavefront: the candidate buffer (SCAN_CAP per
   // lane); after the last drain the same space holds the upper lanes' lists
   // for the merge.
   static constexpr int CBW = SCAN_CAP * 64;
-  static constexpr int W = scan_waves(KP);    // wavefronts per workgroup
   using S = ScanShape<D, MODE, W>;
   // Chunk stride of this pass.  Long lists take a denser sample: their
   // candidates must fit the per-row arrays of the collecting pass.
@@ -622,24 +621,27 @@ struct Scanner {
 // Persistent grid for one graph: nwg workgroups split the H * nbph query
 // blocks (32 rows each) into equal contiguous ranges.  Batched graphs: one
 // workgroup per (planned tile, head).
-template <int D, int KP, int MODE>
-__global__ __launch_bounds__(scan_waves(KP) * 64) void score_topk_kernel(ScanArgs a, int nwg) {
+// W wavefronts per workgroup; short lists keep 128 VGPRs (four wavefronts
+// per SIMD: one 16-wavefront or two 8-wavefront workgroups per CU).
+template <int D, int KP, int MODE, int W>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64),
+                          amdgpu_waves_per_eu(KP <= 16 ? 4 : 2)))
+void score_topk_kernel(ScanArgs a, int nwg) {
   const int64_t N = a.N;
   const int H = a.H;
   const int2* tiles = a.tiles;
   const int32_t* offsets = a.offsets;
-  constexpr int W = scan_waves(KP);
   constexpr int SUB_ROWS = W * QB * 32;
   using S = ScanShape<D, MODE, W>;
   // One LDS block: the key ring, then (SELECT) the candidate buffers.
   constexpr int KB = S::NBUF * S::CHUNK_BYTES;
-  constexpr int CB = MODE == M_SELECT ? W * Scanner<D, KP, MODE>::CBW * 8 : 0;
+  constexpr int CB = MODE == M_SELECT ? W * Scanner<D, KP, MODE, W>::CBW * 8 : 0;
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[KB + CB];
   uint2* cbuf = reinterpret_cast<uint2*>(kbuf + KB);
   const unsigned kbuf_lds =
       (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kbuf;
-  Scanner<D, KP, MODE> sc{kbuf,   kbuf_lds, cbuf,   a,     a.q,   a.k,
-                          a.perm, a.N,      a.H,    a.topk, a.thr, a.idx, a.score};
+  Scanner<D, KP, MODE, W> sc{kbuf,   kbuf_lds, cbuf,   a,      a.q,   a.k,
+                             a.perm, a.N,      a.H,    a.topk, a.thr, a.idx, a.score};
   // Query blocks [b, be) of the flattened (head, 32-row block) space for one
   // graph; a single planned sub-tile for batched graphs.
   const int64_t nbph = (N + 31) / 32;
@@ -702,18 +704,17 @@ int resident_workgroups(Kern kern, int threads) {
 
 template <int D, int KP, int MODE>
 hipError_t launch_pass(const ScanArgs& a, hipStream_t s) {
-  auto kern = score_topk_kernel<D, KP, MODE>;
-  constexpr int threads = scan_waves(KP) * 64;
-  int nwg = 0;
-  dim3 grid;
   if (a.tiles == nullptr) {
-    nwg = resident_workgroups(kern, threads);
+    constexpr int W = scan_waves(KP, false);
+    auto kern = score_topk_kernel<D, KP, MODE, W>;
+    const int nwg = resident_workgroups(kern, W * 64);
     if (nwg <= 0) return hipErrorInvalidDevice;
-    grid = dim3((unsigned)nwg);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(W * 64), 0, s, a, nwg);
   } else {
-    grid = dim3((unsigned)(a.max_tiles * a.H));
+    constexpr int W = scan_waves(KP, true);
+    hipLaunchKernelGGL((score_topk_kernel<D, KP, MODE, W>), dim3((unsigned)(a.max_tiles * a.H)),
+                       dim3(W * 64), 0, s, a, 0);
   }
-  hipLaunchKernelGGL(kern, grid, dim3(threads), 0, s, a, nwg);
   return hipGetLastError();
 }
 

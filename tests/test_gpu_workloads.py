@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle.kmip_oracle as orc
-from tests.parity import assert_rows_close, check_selection, decode
+from tests.parity import BAND_REL, assert_rows_close, check_selection, decode
 from workloads import get_workload
 
 pytestmark = pytest.mark.gpu
@@ -29,16 +29,19 @@ def _sample_rows(n, m, seed):
     return np.unique(np.concatenate([[0, n - 1], rows]))
 
 
-def _forward(name, nrows):
+def _forward(name, nrows, dtype="bf16"):
     from tests.gpu_util import np_, run_forward
-    w = get_workload(name)
+    w = get_workload(name, dtype=dtype)
     print(f"[workload] {name} n={w.n} H={w.heads} d={w.d} k={w.topk} B={w.num_graphs}",
           flush=True)
     t, out, idx, score = run_forward(w)
     q, k, v = decode(w)
     rows = np.arange(w.n) if nrows is None else _sample_rows(w.n, nrows, w.meta["seed"])
     idx_n, score_n = np_(idx), np_(score)
-    st = check_selection(idx_n, score_n, q, k, w.offsets, w.topk, rows)
+    # fp32 inputs: the selection is checked at the split scores' own accuracy
+    f32 = dtype == "f32"
+    st = check_selection(idx_n, score_n, q, k, w.offsets, w.topk, rows,
+                         band_rel=0.0 if f32 else BAND_REL, split=f32)
     ref = orc.attend_on_sets(q, k, v, idx_n[rows].astype(np.int64), rows=rows)
     assert_rows_close(np_(out)[rows], ref["out"], "out")
     print(f"[workload] {name} selection {st}", flush=True)
@@ -88,6 +91,15 @@ def test_train_clustered_n100000():
 
 def test_ragged64():
     w, t, out, idx, score, qkv, rows = _forward("ragged64_h4_d32_k15", 1024)
+    _backward(w, t, idx, score, qkv, rows)
+
+
+@pytest.mark.parametrize("name,nrows", [("train_clustered_n100000_h4_d32_k15", 192),
+                                        ("ragged64_h4_d32_k15", 512)])
+def test_f32_entry_points_full_size(name, nrows):
+    """The fp32 entry points on the float32 draws of the training and batched
+    workloads (the bench's --precision fp32 runs)."""
+    w, t, out, idx, score, qkv, rows = _forward(name, nrows, dtype="f32")
     _backward(w, t, idx, score, qkv, rows)
 
 

@@ -55,22 +55,23 @@ __global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B, int
 }
 
 // ------------------------------------------------------------ query order
-// Queries of one head are grouped by a 12-bit sign-random-projection code of
+// Queries of one head are grouped by a 14-bit sign-random-projection code of
 // q (Rademacher directions fixed by the constants below), so that the 32
 // queries of a wavefront tend to point the same way and share their few
 // high-scoring keys: the selection pass then meets far fewer 32-key blocks
 // holding a candidate for any of its queries.  The order only changes which
 // queries share a wavefront; every query's result is independent of it.
-constexpr int LSH_BITS = 12;
+constexpr int LSH_BITS = 14;
 constexpr int LSH_BINS = 1 << LSH_BITS;
 // Each (head, code) count is split over LSH_COPIES counters picked by the
 // node id, which keeps atomic contention low when many queries share a code.
-constexpr int LSH_COPIES = 16;
+constexpr int LSH_COPIES = 4;
 __constant__ uint32_t kLshSigns[LSH_BITS][2] = {
     {0x9e3779b9u, 0x7f4a7c15u}, {0xf39cc060u, 0x5ced1d6bu}, {0xbf58476du, 0x1ce4e5b9u},
     {0x94d049bbu, 0x133111ebu}, {0x2545f491u, 0x4f6cdd1du}, {0xd6e8feb8u, 0x6658e9a5u},
     {0x85ebca6bu, 0xc2b2ae35u}, {0x27d4eb2fu, 0x165667b1u}, {0xa0761d64u, 0xe7037ed1u},
-    {0x8ebc6af0u, 0x589965ccu}, {0x1d8e4e27u, 0xc5ed3a8bu}, {0x6a09e667u, 0xbb67ae85u}};
+    {0x8ebc6af0u, 0x589965ccu}, {0x1d8e4e27u, 0xc5ed3a8bu}, {0x6a09e667u, 0xbb67ae85u},
+    {0x3c6ef372u, 0xa54ff53au}, {0x510e527fu, 0x9b05688cu}};
 
 __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -156,6 +156,26 @@ __device__ __forceinline__ double sum16d(double x) {
   return x;
 }
 
+// Reduce-scatter over a 16-lane group: each lane holds 16 partial sums v[u];
+// lane l returns the total of v[l] over the group.  Round o (8, 4, 2, 1)
+// keeps the half of the live values whose index bit matches the lane's bit o
+// and adds the partner's copy of it: 15 shuffles for 16 sums.
+__device__ __forceinline__ double reduce_scatter16(const double (&v)[16], int l16) {
+  double a8[8], a4[4], a2[2];
+  const bool b8 = (l16 & 8) != 0, b4 = (l16 & 4) != 0, b2 = (l16 & 2) != 0,
+             b1 = (l16 & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    a8[i] = (b8 ? v[i + 8] : v[i]) + __shfl_xor(b8 ? v[i] : v[i + 8], 8, 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    a4[i] = (b4 ? a8[i + 4] : a8[i]) + __shfl_xor(b4 ? a8[i] : a8[i + 4], 4, 16);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    a2[i] = (b2 ? a4[i + 2] : a4[i]) + __shfl_xor(b2 ? a4[i] : a4[i + 2], 2, 16);
+  return (b1 ? a2[1] : a2[0]) + __shfl_xor(b1 ? a2[0] : a2[1], 1, 16);
+}
+
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_query_kernel(
     const T* __restrict__ Kt, const T* __restrict__ V, int64_t NH, int H,
@@ -181,38 +201,40 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   load_cols<EPL>(dout + row * D + l16 * EPL, g);
   const float m = __shfl(sv[0], 0, 16);
 
-  // Pass 1: weights w_t and dp_t; lane (t % 16) keeps entry t.
+  // Pass 1: weights w_t and dp_t; lane (t % 16) keeps entry t.  The 16 V
+  // rows of a chunk are requested together (unused slots read the query's
+  // own row and count zero), and their partial dot products are reduced in
+  // one butterfly that leaves entry t's dp in lane t % 16.
+  const int64_t self = row / H;
   double wv[MAXK / 16], dpv[MAXK / 16];
-  double z = 0.0, dsum = 0.0;
+  double zl = 0.0, dl = 0.0;               // this lane's share of Z and sum w dp
 #pragma unroll
   for (int c = 0; c < MAXK / 16; ++c) {
     wv[c] = 0.0;
     dpv[c] = 0.0;
     if (c * 16 < topk) {
-      const int tn = topk - c * 16 < 16 ? topk - c * 16 : 16;
-      for (int u = 0; u < tn; ++u) {
-        const int j = __shfl(jv[c], u, 16);
-        double dp = 0.0, w = 0.0;
-        if (j >= 0) {                      // uniform across the 16 lanes
-          float x[EPL];
-          load_cols<EPL>(V + ((int64_t)j * H + h) * D + l16 * EPL, x);
-          double part = 0.0;
+      double part[16];
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) part = fma((double)g[e], (double)x[e], part);
-          dp = sum16d(part);
-          w = (double)__expf(__shfl(sv[c], u, 16) - m);
-        }
-        z += w;
-        dsum = fma(w, dp, dsum);
-        if (l16 == u) {
-          wv[c] = w;
-          dpv[c] = dp;
-        }
+      for (int u = 0; u < 16; ++u) {
+        const int j = __shfl(jv[c], u, 16);
+        float x[EPL];
+        load_cols<EPL>(V + ((j >= 0 ? (int64_t)j : self) * H + h) * D + l16 * EPL, x);
+        double pp = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) pp = fma((double)g[e], (double)x[e], pp);
+        part[u] = j >= 0 ? pp : 0.0;
       }
+      const double dp = reduce_scatter16(part, l16);
+      const bool live = jv[c] >= 0;        // slot c*16 + l16 holds a key
+      const double w = live ? (double)__expf(sv[c] - m) : 0.0;
+      wv[c] = w;
+      dpv[c] = live ? dp : 0.0;
+      zl += w;
+      dl = fma(w, dpv[c], dl);
     }
   }
-  const double inv = 1.0 / z;
-  const double Dm = dsum * inv;
+  const double inv = 1.0 / sum16d(zl);
+  const double Dm = sum16d(dl) * inv;
 
   // Pass 2: ds_t and dq = sum ds_t k_t.
   double acc[EPL];
@@ -225,16 +247,14 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
       const double p = wv[c] * inv;
       const double ds = p * (dpv[c] - Dm);
       if (t < topk) pairs[row * topk + t] = make_float2((float)p, (float)ds);
-      const int tn = topk - c * 16 < 16 ? topk - c * 16 : 16;
-      for (int u = 0; u < tn; ++u) {
-        const int j = __shfl(jv[c], u, 16);
-        const double dsu = __shfl(ds, u, 16);
-        if (j >= 0) {
-          float x[EPL];
-          load_cols<EPL>(Kt + ((int64_t)j * H + h) * D + l16 * EPL, x);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[e] = fma(dsu, (double)x[e], acc[e]);
-        }
+      for (int u = 0; u < 16; ++u) {
+        const int j = __shfl(jv[c], u, 16);
+        const double dsu = __shfl(ds, u, 16);   // 0 on unused slots
+        float x[EPL];
+        load_cols<EPL>(Kt + ((j >= 0 ? (int64_t)j : self) * H + h) * D + l16 * EPL, x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fma(dsu, (double)x[e], acc[e]);
       }
     }
   }

@@ -13,10 +13,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- tiling
-// Score scan: a workgroup of SCAN_WAVES wavefronts, each owning 32 query rows
-// of one head (one 32x32 MFMA output block: keys x queries).
-constexpr int SCAN_WAVES = 16;                    // lists of up to 16 entries
-constexpr int SCAN_WAVES_LONG = 8;                // longer lists: 2 waves per SIMD
+// Score scan: a workgroup of scan_waves(...) wavefronts, each owning 32 query
+// rows of one head (one 32x32 MFMA output block: keys x queries).
+constexpr int SCAN_WAVES = 16;                    // one graph, lists of up to 16
+constexpr int SCAN_WAVES_LONG = 8;                // longer lists; batched graphs
 constexpr int SCAN_QPW = 32;
 constexpr int SCAN_QT_MIN = SCAN_WAVES_LONG * SCAN_QPW;   // smallest planned tile
 constexpr int SCAN_CAP = 8;                       // per-lane candidate buffer entries

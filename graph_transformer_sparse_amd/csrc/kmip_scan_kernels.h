@@ -8,9 +8,11 @@
 // are never stored as an N x N matrix.
 //
 // Design (gfx950):
-//  * Work is split into sub-tiles of up to 512 query rows of one head and one
-//    graph: a workgroup of 16 wavefronts, each owning 32 rows.  A wavefront
-//    keeps its Q rows in VGPRs as MFMA B operands for the whole scan.
+//  * Work is split into sub-tiles of query rows of one head and one graph: a
+//    workgroup of W wavefronts, each owning 32 rows (W = 16 for one graph
+//    and lists of at most 16; W = 8 for longer lists and for batched
+//    graphs).  A wavefront keeps its Q rows in VGPRs as MFMA B operands for
+//    the whole scan.
 //  * The graph's keys stream through an LDS ring of two chunks (64 KB, 1024
 //    keys at d = 32, in the threshold pass; 32 KB in the selection pass, which
 //    also holds candidate buffers), fetched with direct global->LDS loads one
@@ -29,15 +31,17 @@
 //    next_down(T): a block of scores is rejected with a max tree and one
 //    compare, rare hits go to a per-lane LDS candidate buffer, and buffers
 //    are drained in lockstep into per-lane register lists.  At the end the
-//    two half-lists of a query (lanes l, l^32) are merged by rank with the
-//    tie rule (score descending, id ascending).
+//    two half-lists of a query (lanes l, l^32) are merged under the tie rule
+//    (score descending, id ascending).  Lists longer than 16 collect their
+//    candidates in per-row arrays instead (COLLECT below).
 //  * One graph: each head's queries are first grouped by a sign-random-
 //    projection code, so a wavefront's 32 queries tend to share their
 //    candidate keys.  A persistent grid of exactly the co-resident
 //    workgroups, each taking an equal contiguous range of query blocks (no
 //    partial last round), with logical ids permuted so that the workgroups of
 //    one XCD share a head and its keys in that XCD's L2.  Batched graphs: one
-//    workgroup per planned sub-tile; sub-blocks past a graph's last key are skipped.
+//    workgroup per planned sub-tile; sub-blocks past a graph's last key are
+//    skipped.
 #pragma once
 #include "kmip_internal.h"
 

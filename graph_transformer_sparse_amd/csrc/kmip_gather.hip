@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void gather_av_kernel(
     sv[c] = t < topk ? sr[t] : 0.f;
   }
   const float m = __shfl(sv[0], 0, 16);     // best score: entries are sorted
+  const int64_t self = row / H;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
@@ -52,18 +53,21 @@ __global__ __launch_bounds__(256) void gather_av_kernel(
 #pragma unroll
   for (int c = 0; c < MAXK / 16; ++c) {
     if (c * 16 >= topk) break;
-    const int tn = topk - c * 16 < 16 ? topk - c * 16 : 16;
-
-    for (int u = 0; u < tn; ++u) {
-      const int j = __shfl(jv[c], u, 16);
-      if (j >= 0) {
-        const float w = __expf(__shfl(sv[c], u, 16) - m);
-        float x[EPL];
-        load_cols<EPL>(V + ((int64_t)j * H + h) * D + l16 * EPL, x);
-        z += w;
+    // The chunk's 16 rows are requested together; unused slots read the
+    // query's own row with weight 0 (adding 0 leaves the sums unchanged).
+    const float wl = jv[c] >= 0 ? __expf(sv[c] - m) : 0.f;   // this lane's entry
+    float x[16][EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, x[e], acc[e]);
-      }
+    for (int u = 0; u < 16; ++u) {
+      const int j = __shfl(jv[c], u, 16);
+      load_cols<EPL>(V + ((j >= 0 ? (int64_t)j : self) * H + h) * D + l16 * EPL, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float w = __shfl(wl, u, 16);
+      z += w;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, x[u][e], acc[e]);
     }
   }
   const float inv = 1.f / z;

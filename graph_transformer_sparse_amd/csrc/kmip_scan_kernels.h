@@ -22,8 +22,9 @@
 //    of exact bf16 products).  Lane l holds query l%32 and 16 of the 32 keys,
 //    so each lane sees a private half of every query's key stream, in
 //    ascending key order.
-//  * Two passes.  The threshold pass scores every fourth chunk only and
-//    keeps, per lane and query, the top-k of the maxima of SCAN_CHUNKS
+//  * Two passes.  The threshold pass scores every fourth chunk only (every
+//    eighth on graphs of 2^16 keys or more with lists of at most 16, every
+//    second for longer lists) and keeps, per lane and query, the top-k of the maxima of SCAN_CHUNKS
 //    consecutive ranges of those keys (uniform, lockstep insertions); these
 //    maxima are scores of distinct keys, so the k-th largest over both halves
 //    is a lower bound T of the query's k-th score.

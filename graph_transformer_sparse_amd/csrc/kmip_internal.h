@@ -95,8 +95,8 @@ hipError_t launch_scan_d64(int kp, const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_d96(int kp, const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_d192(int kp, const ScanArgs& a, hipStream_t s);
 
-// Query order for one graph: groups each head's queries by a sign-random-
-// projection code of q.  Workspace: query_order_bytes(N, H); *perm points
+// Query order for one graph: groups each head's queries by their nearest
+// pivot query (largest inner product).  Workspace: query_order_bytes(N, H); *perm points
 // into it ([H][N] node ids).
 size_t query_order_bytes(int64_t N, int H);
 hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* ws,

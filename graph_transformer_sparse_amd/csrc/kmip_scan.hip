@@ -55,77 +55,111 @@ __global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B, int
 }
 
 // ------------------------------------------------------------ query order
-// Queries of one head are grouped by a 14-bit sign-random-projection code of
-// q (Rademacher directions fixed by the constants below), so that the 32
-// queries of a wavefront tend to point the same way and share their few
-// high-scoring keys: the selection pass then meets far fewer 32-key blocks
+// Queries of one head are grouped by their nearest pivot: npiv query rows of
+// the head, at evenly spaced node ids (about one per 32 nodes, a multiple of
+// 32, at most ORDER_PIVOTS), and a query's group is the pivot with the
+// largest inner product (the lowest pivot index on ties).  The
+// 32 queries of a wavefront then tend to point the same way and share their
+// few high-scoring keys, so the selection pass meets far fewer 32-key blocks
 // holding a candidate for any of its queries.  The order only changes which
 // queries share a wavefront; every query's result is independent of it.
-constexpr int LSH_BITS = 14;
-constexpr int LSH_BINS = 1 << LSH_BITS;
-// Each (head, code) count is split over LSH_COPIES counters picked by the
-// node id, which keeps atomic contention low when many queries share a code.
-constexpr int LSH_COPIES = 4;
-__constant__ uint32_t kLshSigns[LSH_BITS][2] = {
-    {0x9e3779b9u, 0x7f4a7c15u}, {0xf39cc060u, 0x5ced1d6bu}, {0xbf58476du, 0x1ce4e5b9u},
-    {0x94d049bbu, 0x133111ebu}, {0x2545f491u, 0x4f6cdd1du}, {0xd6e8feb8u, 0x6658e9a5u},
-    {0x85ebca6bu, 0xc2b2ae35u}, {0x27d4eb2fu, 0x165667b1u}, {0xa0761d64u, 0xe7037ed1u},
-    {0x8ebc6af0u, 0x589965ccu}, {0x1d8e4e27u, 0xc5ed3a8bu}, {0x6a09e667u, 0xbb67ae85u},
-    {0x3c6ef372u, 0xa54ff53au}, {0x510e527fu, 0x9b05688cu}};
+constexpr int ORDER_PIVOTS = 1024;
+int order_pivots(int64_t N) {
+  const int64_t p = (N / 32) & ~int64_t(31);
+  return (int)(p < 32 ? 32 : p > ORDER_PIVOTS ? ORDER_PIVOTS : p);
+}
+constexpr int ORDER_WAVES = 8;                    // wavefronts per workgroup
+// Each (head, pivot) count is split over ORDER_COPIES counters picked by the
+// node id, which keeps atomic contention low when many queries share a pivot.
+constexpr int ORDER_COPIES = 4;
 
 __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
 }
 
-// codes[h*N + i] and per-(head, code) counts.
-template <int D>
-__global__ void lsh_code_kernel(const uint16_t* __restrict__ Q, int64_t N, int H,
-                                uint16_t* __restrict__ codes, int32_t* __restrict__ counts) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // r = i*H + h
-  if (r >= N * H) return;
-  const int64_t i = r / H;
-  const int h = (int)(r % H);
-  // The code uses the first min(D, 64) elements (for split rows: the high
-  // parts).
-  constexpr int DH = D < 64 ? D : 64;
-  float x[DH];
-  const uint4* src = reinterpret_cast<const uint4*>(Q + r * D);
+// codes[h*N + i] = nearest pivot of query i of head h, and per-(head, pivot)
+// counts.  Rows hold D bf16 elements; the inner products use the first DP
+// (for split-precision rows, the high parts).  The workgroup stages the
+// head's npiv pivots in LDS in MFMA operand order (block j*NM + m: pivots
+// [32j, 32j + 32), elements [16m, 16m + 16)); each wavefront scores its 32
+// queries against all of them with 32x32x16 MFMAs, keys' role taken by the
+// pivots.  npiv is a multiple of 32 and at most ORDER_PIVOTS.
+template <int D, int DP>
+__global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
+    const uint16_t* __restrict__ Q, int64_t N, int H, int npiv, uint16_t* __restrict__ codes,
+    int32_t* __restrict__ counts) {
+  constexpr int NM = DP / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char piv[ORDER_PIVOTS * DP * 2];
+  const int h = blockIdx.y;
+  const int64_t stride = N / npiv > 0 ? N / npiv : 1;
+  const int pieces = npiv * DP / 8;               // 16-byte operand pieces
+  for (int t = threadIdx.x; t < pieces; t += ORDER_WAVES * 64) {
+    const int blk = t >> 6, l = t & 63;
+    const int p = (blk / NM) * 32 + (l & 31);
+    const int64_t pr = (int64_t)p * stride;
+    const int64_t row = pr < N ? pr : N - 1;
+    *reinterpret_cast<uint4*>(piv + (size_t)t * 16) = *reinterpret_cast<const uint4*>(
+        Q + (row * H + h) * D + 16 * (blk % NM) + 8 * (l >> 5));
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, lrow = lane & 31, lhalf = lane >> 5;
+  const int64_t i0 = ((int64_t)blockIdx.x * ORDER_WAVES + (threadIdx.x >> 6)) * 32;
+  if (i0 >= N) return;                            // uniform per wavefront
+  const int64_t i = i0 + lrow;
+  const uint16_t* qp = Q + ((i < N ? i : N - 1) * H + h) * D + 8 * lhalf;
+  bf16x8_t qb[NM];
 #pragma unroll
-  for (int c = 0; c < DH / 8; ++c) {
-    const uint4 w = src[c];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  for (int m = 0; m < NM; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
+  // Per lane: the best of its pivots (acc[r] of block j is pivot
+  // 32j + 4*lhalf + 8*(r/4) + r%4, increasing in r and j, so a strict
+  // compare keeps the lowest index among equal scores).
+  float best = -__builtin_inff();
+  int bp = 0;
+  const int nblk = npiv / 32;
+#pragma unroll 4
+  for (int j = 0; j < nblk; ++j) {
+    floatx16_t acc{};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[8 * c + 2 * e] = __uint_as_float(ws[e] << 16);
-      x[8 * c + 2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
+    for (int m = 0; m < NM; ++m)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8_t*>(piv + (j * NM + m) * 1024 + lane * 16), qb[m], acc,
+          0, 0, 0);
+    const float mx =
+        fmaxf(fmaxf(fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])),
+                    fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7]))),
+              fmaxf(fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11])),
+                    fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15]))));
+    if (mx > best) {
+      int r0 = 15;
+#pragma unroll
+      for (int r = 14; r >= 0; --r) r0 = acc[r] == mx ? r : r0;
+      best = mx;
+      bp = 32 * j + 4 * lhalf + 8 * (r0 >> 2) + (r0 & 3);
     }
   }
-  uint32_t code = 0;
-#pragma unroll
-  for (int b = 0; b < LSH_BITS; ++b) {
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < (D < 64 ? D : 64); ++c) {
-      const bool neg = (kLshSigns[b][c >> 5] >> (c & 31)) & 1u;
-      acc += neg ? -x[c] : x[c];
-    }
-    code |= (acc > 0.f ? 1u : 0u) << b;
+  const float ob = __shfl_xor(best, 32);
+  const int op = __shfl_xor(bp, 32);
+  if (ob > best || (ob == best && op < bp)) bp = op;
+  if (lhalf == 0 && i < N) {
+    codes[h * N + i] = (uint16_t)bp;
+    atomicAdd(&counts[((int64_t)h * ORDER_PIVOTS + bp) * ORDER_COPIES + (i & (ORDER_COPIES - 1))],
+              1);
   }
-  codes[h * N + i] = (uint16_t)code;
-  atomicAdd(&counts[((int64_t)h * LSH_BINS + code) * LSH_COPIES + (i & (LSH_COPIES - 1))], 1);
 }
 
-// perm[h*N + pos] = i, positions handed out per (head, code) from the
-// scanned counts.  The order inside a code group is immaterial.
-__global__ void lsh_place_kernel(const uint16_t* __restrict__ codes, int64_t N, int H,
-                                 int32_t* __restrict__ cursor, int32_t* __restrict__ perm) {
+// perm[h*N + pos] = i, positions handed out per (head, pivot) from the
+// scanned counts.  The order inside a pivot group is immaterial.
+__global__ void order_place_kernel(const uint16_t* __restrict__ codes, int64_t N, int H,
+                                   int32_t* __restrict__ cursor, int32_t* __restrict__ perm) {
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // r = h*N + i
   if (r >= N * H) return;
   const int h = (int)(r / N);
   const int64_t i = r % N;
   const int pos = atomicAdd(
-      &cursor[((int64_t)h * LSH_BINS + codes[r]) * LSH_COPIES + (i & (LSH_COPIES - 1))], 1);
+      &cursor[((int64_t)h * ORDER_PIVOTS + codes[r]) * ORDER_COPIES + (i & (ORDER_COPIES - 1))],
+      1);
   perm[pos] = (int32_t)i;
 }
 
@@ -151,40 +185,41 @@ hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_
 }
 
 size_t query_order_bytes(int64_t N, int H) {
-  const int64_t nb = (int64_t)H * LSH_BINS * LSH_COPIES;
+  const int64_t nb = (int64_t)H * ORDER_PIVOTS * ORDER_COPIES;
   return align256((size_t)N * H * 4) + align256((size_t)N * H * 2) + 2 * align256((size_t)nb * 4) +
          align256((size_t)scan_aux_elems(nb) * 4);
 }
 
 hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* ws,
                               int32_t** perm_out, hipStream_t s) {
-  const int64_t nb = (int64_t)H * LSH_BINS * LSH_COPIES;
+  const int64_t nb = (int64_t)H * ORDER_PIVOTS * ORDER_COPIES;
   char* p = static_cast<char*>(ws);
   int32_t* perm = reinterpret_cast<int32_t*>(p); p += align256((size_t)N * H * 4);
   uint16_t* codes = reinterpret_cast<uint16_t*>(p); p += align256((size_t)N * H * 2);
   int32_t* counts = reinterpret_cast<int32_t*>(p); p += align256((size_t)nb * 4);
   int32_t* cursor = reinterpret_cast<int32_t*>(p); p += align256((size_t)nb * 4);
   int32_t* aux = reinterpret_cast<int32_t*>(p);
-  const unsigned rows = (unsigned)ceil_div(N * H, 256);
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, s,
                      counts, nb);
-  switch (d) {
-    case 32: hipLaunchKernelGGL(lsh_code_kernel<32>, dim3(rows), dim3(256), 0, s, q, N, H,
-                                codes, counts); break;
-    case 64: hipLaunchKernelGGL(lsh_code_kernel<64>, dim3(rows), dim3(256), 0, s, q, N, H,
-                                codes, counts); break;
-    case 96: hipLaunchKernelGGL(lsh_code_kernel<96>, dim3(rows), dim3(256), 0, s, q, N, H,
-                                codes, counts); break;
-    case 192: hipLaunchKernelGGL(lsh_code_kernel<192>, dim3(rows), dim3(256), 0, s, q, N, H,
-                                 codes, counts); break;
+  const dim3 grid((unsigned)ceil_div(N, ORDER_WAVES * 32), (unsigned)H);
+  const dim3 block(ORDER_WAVES * 64);
+  const int npiv = order_pivots(N);
+  void (*code_kernel)(const uint16_t*, int64_t, int, int, uint16_t*, int32_t*);
+  switch (d) {      // split-precision rows (3d) are grouped by their high parts
+    case 32: code_kernel = pivot_code_kernel<32, 32>; break;
+    case 64: code_kernel = pivot_code_kernel<64, 64>; break;
+    case 96: code_kernel = pivot_code_kernel<96, 32>; break;
+    case 192: code_kernel = pivot_code_kernel<192, 64>; break;
     default: return hipErrorInvalidValue;
   }
+  hipLaunchKernelGGL(code_kernel, grid, block, 0, s, q, N, H, npiv, codes, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Exclusive scan over (head, code, copy): head h's positions start at h*N.
+  // Exclusive scan over (head, pivot, copy): head h's positions start at h*N.
   e = launch_exclusive_scan(counts, cursor, nb, aux, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lsh_place_kernel, dim3(rows), dim3(256), 0, s, codes, N, H, cursor, perm);
+  const unsigned rows = (unsigned)ceil_div(N * H, 256);
+  hipLaunchKernelGGL(order_place_kernel, dim3(rows), dim3(256), 0, s, codes, N, H, cursor, perm);
   *perm_out = perm;
   return hipGetLastError();
 }

@@ -24,8 +24,9 @@
 //    ascending key order.
 //  * Two passes.  The threshold pass scores every fourth chunk only (every
 //    eighth on graphs of 2^16 keys or more with lists of at most 16, every
-//    second for longer lists) and keeps, per lane and query, the top-k of the maxima of SCAN_CHUNKS
-//    consecutive ranges of those keys (uniform, lockstep insertions); these
+//    second for longer lists) and keeps, per lane and query, the top-k of
+//    the maxima of SCAN_CHUNKS consecutive ranges of those keys (uniform,
+//    lockstep insertions); these
 //    maxima are scores of distinct keys, so the k-th largest over both halves
 //    is a lower bound T of the query's k-th score.
 //    The selection pass then runs the exact running top-k seeded with
@@ -35,9 +36,9 @@
 //    two half-lists of a query (lanes l, l^32) are merged under the tie rule
 //    (score descending, id ascending).  Lists longer than 16 collect their
 //    candidates in per-row arrays instead (COLLECT below).
-//  * One graph: each head's queries are first grouped by a sign-random-
-//    projection code, so a wavefront's 32 queries tend to share their
-//    candidate keys.  A persistent grid of exactly the co-resident
+//  * One graph: each head's queries are first grouped by their nearest of
+//    1024 pivot queries (largest inner product), so a wavefront's 32 queries
+//    tend to share their candidate keys.  A persistent grid of exactly the co-resident
 //    workgroups, each taking an equal contiguous range of query blocks (no
 //    partial last round), with logical ids permuted so that the workgroups of
 //    one XCD share a head and its keys in that XCD's L2.  Batched graphs: one

@@ -56,17 +56,19 @@ __global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B, int
 
 // ------------------------------------------------------------ query order
 // Queries of one head are grouped by their nearest pivot: npiv query rows of
-// the head, at evenly spaced node ids (about one per 32 nodes, a multiple of
-// 32, at most ORDER_PIVOTS), and a query's group is the pivot with the
-// largest inner product (the lowest pivot index on ties).  The
+// the head, at evenly spaced node ids (about one per 96 nodes, so a group
+// fills about three wavefronts; a multiple of 32, at least 32), and a query's
+// group is the pivot with the largest inner product (the lowest pivot index
+// on ties).  The
 // 32 queries of a wavefront then tend to point the same way and share their
 // few high-scoring keys, so the selection pass meets far fewer 32-key blocks
 // holding a candidate for any of its queries.  The order only changes which
 // queries share a wavefront; every query's result is independent of it.
-constexpr int ORDER_PIVOTS = 1024;
+constexpr int ORDER_PIVOTS = 1024;                // pivots staged in LDS at a time
+constexpr int ORDER_MAX_PIVOTS = 16384;           // codes are 16-bit
 int order_pivots(int64_t N) {
-  const int64_t p = (N / 32) & ~int64_t(31);
-  return (int)(p < 32 ? 32 : p > ORDER_PIVOTS ? ORDER_PIVOTS : p);
+  const int64_t p = (N / 96) & ~int64_t(31);
+  return (int)(p < 32 ? 32 : p > ORDER_MAX_PIVOTS ? ORDER_MAX_PIVOTS : p);
 }
 constexpr int ORDER_WAVES = 8;                    // wavefronts per workgroup
 // Each (head, pivot) count is split over ORDER_COPIES counters picked by the
@@ -81,10 +83,11 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
 // codes[h*N + i] = nearest pivot of query i of head h, and per-(head, pivot)
 // counts.  Rows hold D bf16 elements; the inner products use the first DP
 // (for split-precision rows, the high parts).  The workgroup stages the
-// head's npiv pivots in LDS in MFMA operand order (block j*NM + m: pivots
-// [32j, 32j + 32), elements [16m, 16m + 16)); each wavefront scores its 32
-// queries against all of them with 32x32x16 MFMAs, keys' role taken by the
-// pivots.  npiv is a multiple of 32 and at most ORDER_PIVOTS.
+// head's pivots in LDS, ORDER_PIVOTS at a time, in MFMA operand order
+// (block j*NM + m: pivots [32j, 32j + 32) of the batch, elements
+// [16m, 16m + 16)); each wavefront scores its 32 queries against all of them
+// with 32x32x16 MFMAs, keys' role taken by the pivots.  npiv is a multiple
+// of 32.
 template <int D, int DP>
 __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
     const uint16_t* __restrict__ Q, int64_t N, int H, int npiv, uint16_t* __restrict__ codes,
@@ -93,73 +96,75 @@ __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char piv[ORDER_PIVOTS * DP * 2];
   const int h = blockIdx.y;
   const int64_t stride = N / npiv > 0 ? N / npiv : 1;
-  const int pieces = npiv * DP / 8;               // 16-byte operand pieces
-  for (int t = threadIdx.x; t < pieces; t += ORDER_WAVES * 64) {
-    const int blk = t >> 6, l = t & 63;
-    const int p = (blk / NM) * 32 + (l & 31);
-    const int64_t pr = (int64_t)p * stride;
-    const int64_t row = pr < N ? pr : N - 1;
-    *reinterpret_cast<uint4*>(piv + (size_t)t * 16) = *reinterpret_cast<const uint4*>(
-        Q + (row * H + h) * D + 16 * (blk % NM) + 8 * (l >> 5));
-  }
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, lrow = lane & 31, lhalf = lane >> 5;
   const int64_t i0 = ((int64_t)blockIdx.x * ORDER_WAVES + (threadIdx.x >> 6)) * 32;
-  if (i0 >= N) return;                            // uniform per wavefront
+  const bool active = i0 < N;                     // uniform per wavefront
   const int64_t i = i0 + lrow;
   const uint16_t* qp = Q + ((i < N ? i : N - 1) * H + h) * D + 8 * lhalf;
   bf16x8_t qb[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
   // Per lane: the best of its pivots (acc[r] of block j is pivot
-  // 32j + 4*lhalf + 8*(r/4) + r%4, increasing in r and j, so a strict
-  // compare keeps the lowest index among equal scores).
+  // base + 32j + 4*lhalf + 8*(r/4) + r%4, increasing in r, j and the batch,
+  // so a strict compare keeps the lowest index among equal scores).
   float best = -__builtin_inff();
   int bp = 0;
-  const int nblk = npiv / 32;
+  for (int base = 0; base < npiv; base += ORDER_PIVOTS) {
+    const int nb = npiv - base < ORDER_PIVOTS ? npiv - base : ORDER_PIVOTS;
+    if (base > 0) __syncthreads();                // the previous batch has been read
+    const int pieces = nb * DP / 8;               // 16-byte operand pieces
+    for (int t = threadIdx.x; t < pieces; t += ORDER_WAVES * 64) {
+      const int blk = t >> 6, l = t & 63;
+      const int64_t pr = (int64_t)(base + (blk / NM) * 32 + (l & 31)) * stride;
+      const int64_t row = pr < N ? pr : N - 1;
+      *reinterpret_cast<uint4*>(piv + (size_t)t * 16) = *reinterpret_cast<const uint4*>(
+          Q + (row * H + h) * D + 16 * (blk % NM) + 8 * (l >> 5));
+    }
+    __syncthreads();
+    if (!active) continue;
 #pragma unroll 4
-  for (int j = 0; j < nblk; ++j) {
-    floatx16_t acc{};
+    for (int j = 0; j < nb / 32; ++j) {
+      floatx16_t acc{};
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8_t*>(piv + (j * NM + m) * 1024 + lane * 16), qb[m], acc,
-          0, 0, 0);
-    const float mx =
-        fmaxf(fmaxf(fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])),
-                    fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7]))),
-              fmaxf(fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11])),
-                    fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15]))));
-    if (mx > best) {
-      int r0 = 15;
+      for (int m = 0; m < NM; ++m)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8_t*>(piv + (j * NM + m) * 1024 + lane * 16), qb[m],
+            acc, 0, 0, 0);
+      const float mx =
+          fmaxf(fmaxf(fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])),
+                      fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7]))),
+                fmaxf(fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11])),
+                      fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15]))));
+      if (mx > best) {
+        int r0 = 15;
 #pragma unroll
-      for (int r = 14; r >= 0; --r) r0 = acc[r] == mx ? r : r0;
-      best = mx;
-      bp = 32 * j + 4 * lhalf + 8 * (r0 >> 2) + (r0 & 3);
+        for (int r = 14; r >= 0; --r) r0 = acc[r] == mx ? r : r0;
+        best = mx;
+        bp = base + 32 * j + 4 * lhalf + 8 * (r0 >> 2) + (r0 & 3);
+      }
     }
   }
+  if (!active) return;
   const float ob = __shfl_xor(best, 32);
   const int op = __shfl_xor(bp, 32);
   if (ob > best || (ob == best && op < bp)) bp = op;
   if (lhalf == 0 && i < N) {
     codes[h * N + i] = (uint16_t)bp;
-    atomicAdd(&counts[((int64_t)h * ORDER_PIVOTS + bp) * ORDER_COPIES + (i & (ORDER_COPIES - 1))],
-              1);
+    atomicAdd(&counts[((int64_t)h * npiv + bp) * ORDER_COPIES + (i & (ORDER_COPIES - 1))], 1);
   }
 }
 
 // perm[h*N + pos] = i, positions handed out per (head, pivot) from the
 // scanned counts.  The order inside a pivot group is immaterial.
 __global__ void order_place_kernel(const uint16_t* __restrict__ codes, int64_t N, int H,
-                                   int32_t* __restrict__ cursor, int32_t* __restrict__ perm) {
+                                   int npiv, int32_t* __restrict__ cursor,
+                                   int32_t* __restrict__ perm) {
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // r = h*N + i
   if (r >= N * H) return;
   const int h = (int)(r / N);
   const int64_t i = r % N;
   const int pos = atomicAdd(
-      &cursor[((int64_t)h * ORDER_PIVOTS + codes[r]) * ORDER_COPIES + (i & (ORDER_COPIES - 1))],
-      1);
+      &cursor[((int64_t)h * npiv + codes[r]) * ORDER_COPIES + (i & (ORDER_COPIES - 1))], 1);
   perm[pos] = (int32_t)i;
 }
 
@@ -185,14 +190,15 @@ hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_
 }
 
 size_t query_order_bytes(int64_t N, int H) {
-  const int64_t nb = (int64_t)H * ORDER_PIVOTS * ORDER_COPIES;
+  const int64_t nb = (int64_t)H * order_pivots(N) * ORDER_COPIES;
   return align256((size_t)N * H * 4) + align256((size_t)N * H * 2) + 2 * align256((size_t)nb * 4) +
          align256((size_t)scan_aux_elems(nb) * 4);
 }
 
 hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* ws,
                               int32_t** perm_out, hipStream_t s) {
-  const int64_t nb = (int64_t)H * ORDER_PIVOTS * ORDER_COPIES;
+  const int npiv = order_pivots(N);
+  const int64_t nb = (int64_t)H * npiv * ORDER_COPIES;
   char* p = static_cast<char*>(ws);
   int32_t* perm = reinterpret_cast<int32_t*>(p); p += align256((size_t)N * H * 4);
   uint16_t* codes = reinterpret_cast<uint16_t*>(p); p += align256((size_t)N * H * 2);
@@ -203,7 +209,6 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
                      counts, nb);
   const dim3 grid((unsigned)ceil_div(N, ORDER_WAVES * 32), (unsigned)H);
   const dim3 block(ORDER_WAVES * 64);
-  const int npiv = order_pivots(N);
   void (*code_kernel)(const uint16_t*, int64_t, int, int, uint16_t*, int32_t*);
   switch (d) {      // split-precision rows (3d) are grouped by their high parts
     case 32: code_kernel = pivot_code_kernel<32, 32>; break;
@@ -219,7 +224,8 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
   e = launch_exclusive_scan(counts, cursor, nb, aux, s);
   if (e != hipSuccess) return e;
   const unsigned rows = (unsigned)ceil_div(N * H, 256);
-  hipLaunchKernelGGL(order_place_kernel, dim3(rows), dim3(256), 0, s, codes, N, H, cursor, perm);
+  hipLaunchKernelGGL(order_place_kernel, dim3(rows), dim3(256), 0, s, codes, N, H, npiv,
+                     cursor, perm);
   *perm_out = perm;
   return hipGetLastError();
 }

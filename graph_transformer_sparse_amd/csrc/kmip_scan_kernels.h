@@ -23,8 +23,8 @@
 //    so each lane sees a private half of every query's key stream, in
 //    ascending key order.
 //  * Two passes.  The threshold pass scores every fourth chunk only (every
-//    eighth on graphs of 2^16 keys or more with lists of at most 16, every
-//    second for longer lists) and keeps, per lane and query, the top-k of
+//    sixteenth on graphs of 2^16 keys or more with lists of at most 16,
+//    every second for longer lists) and keeps, per lane and query, the top-k of
 //    the maxima of SCAN_CHUNKS consecutive ranges of those keys (uniform,
 //    lockstep insertions); these
 //    maxima are scores of distinct keys, so the k-th largest over both halves
@@ -229,10 +229,11 @@ struct Scanner {
     const int64_t nkeys = t.ke - t.kb;
     const int nchunks = (int)((nkeys + S::TK - 1) / S::TK);
     // Chunks scored by this pass: c = j * sample for j < nproc.  Graphs of
-    // 2^16 keys or more sample the threshold pass twice as sparsely (short
-    // lists): at N = 10^5 that measured 2 % faster, at N = 31623 and on
-    // graphs of a few thousand keys 3-10 % slower.
-    const int sample = PRE && KP <= 16 && nkeys >= (int64_t)1 << 16 ? 2 * SAMPLE : SAMPLE;
+    // 2^16 keys or more sample the threshold pass four times as sparsely
+    // (short lists): at N = 10^5 and 5 * 10^5 that measured 1-2 % faster,
+    // while a sparser sample at N = 31623 and on graphs of a few thousand
+    // keys was 3-10 % slower.
+    const int sample = PRE && KP <= 16 && nkeys >= (int64_t)1 << 16 ? 4 * SAMPLE : SAMPLE;
     const int nproc = (nchunks + sample - 1) / sample;
 
     // The ring may still be read by slower waves of the previous sub-tile.

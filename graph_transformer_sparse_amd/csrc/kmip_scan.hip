@@ -73,7 +73,7 @@ int order_pivots(int64_t N) {
 constexpr int ORDER_WAVES = 8;                    // wavefronts per workgroup
 // Each (head, pivot) count is split over ORDER_COPIES counters picked by the
 // node id, which keeps atomic contention low when many queries share a pivot.
-constexpr int ORDER_COPIES = 4;
+constexpr int ORDER_COPIES = 16;
 
 __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -93,6 +93,8 @@ __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
     const uint16_t* __restrict__ Q, int64_t N, int H, int npiv, uint16_t* __restrict__ codes,
     int32_t* __restrict__ counts) {
   constexpr int NM = DP / 16;
+  constexpr int PER_THREAD = ORDER_PIVOTS * DP / 8 / (ORDER_WAVES * 64);
+  static_assert(PER_THREAD * ORDER_WAVES * 64 * 8 == ORDER_PIVOTS * DP, "fill covers a batch");
   __shared__ __attribute__((aligned(16))) unsigned char piv[ORDER_PIVOTS * DP * 2];
   const int h = blockIdx.y;
   const int64_t stride = N / npiv > 0 ? N / npiv : 1;
@@ -104,21 +106,36 @@ __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
   bf16x8_t qb[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
-  // Per lane: the best of its pivots (acc[r] of block j is pivot
+  // Per lane: the best of its pivots.  acc[r] of block j is pivot
   // base + 32j + 4*lhalf + 8*(r/4) + r%4, increasing in r, j and the batch,
-  // so a strict compare keeps the lowest index among equal scores).
+  // so strict compares keep the lowest index among equal scores.  The loop
+  // keeps the best block's index and scores (sv); the position inside it is
+  // found once at the end.
   float best = -__builtin_inff();
-  int bp = 0;
+  int bblk = 0;
+  float sv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sv[r] = best;
   for (int base = 0; base < npiv; base += ORDER_PIVOTS) {
     const int nb = npiv - base < ORDER_PIVOTS ? npiv - base : ORDER_PIVOTS;
     if (base > 0) __syncthreads();                // the previous batch has been read
+    // All of a thread's pieces are requested before any is stored.
     const int pieces = nb * DP / 8;               // 16-byte operand pieces
-    for (int t = threadIdx.x; t < pieces; t += ORDER_WAVES * 64) {
+    uint4 pv[PER_THREAD];
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int tu = threadIdx.x + u * ORDER_WAVES * 64;
+      const int t = tu < pieces ? tu : pieces - 1;   // loads stay in range; stores are skipped
       const int blk = t >> 6, l = t & 63;
       const int64_t pr = (int64_t)(base + (blk / NM) * 32 + (l & 31)) * stride;
       const int64_t row = pr < N ? pr : N - 1;
-      *reinterpret_cast<uint4*>(piv + (size_t)t * 16) = *reinterpret_cast<const uint4*>(
-          Q + (row * H + h) * D + 16 * (blk % NM) + 8 * (l >> 5));
+      pv[u] = *reinterpret_cast<const uint4*>(Q + (row * H + h) * D + 16 * (blk % NM) +
+                                              8 * (l >> 5));
+    }
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int t = threadIdx.x + u * ORDER_WAVES * 64;
+      if (t < pieces) *reinterpret_cast<uint4*>(piv + (size_t)t * 16) = pv[u];
     }
     __syncthreads();
     if (!active) continue;
@@ -135,16 +152,18 @@ __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
                       fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7]))),
                 fmaxf(fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11])),
                       fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15]))));
-      if (mx > best) {
-        int r0 = 15;
+      const bool up = mx > best;
+      best = up ? mx : best;
+      bblk = up ? base / 32 + j : bblk;
 #pragma unroll
-        for (int r = 14; r >= 0; --r) r0 = acc[r] == mx ? r : r0;
-        best = mx;
-        bp = base + 32 * j + 4 * lhalf + 8 * (r0 >> 2) + (r0 & 3);
-      }
+      for (int r = 0; r < 16; ++r) sv[r] = up ? acc[r] : sv[r];
     }
   }
   if (!active) return;
+  int r0 = 15;
+#pragma unroll
+  for (int r = 14; r >= 0; --r) r0 = sv[r] == best ? r : r0;
+  int bp = 32 * bblk + 4 * lhalf + 8 * (r0 >> 2) + (r0 & 3);
   const float ob = __shfl_xor(best, 32);
   const int op = __shfl_xor(bp, 32);
   if (ob > best || (ob == best && op < bp)) bp = op;

@@ -71,6 +71,7 @@ int order_pivots(int64_t N) {
   return (int)(p < 32 ? 32 : p > ORDER_MAX_PIVOTS ? ORDER_MAX_PIVOTS : p);
 }
 constexpr int ORDER_WAVES = 8;                    // wavefronts per workgroup
+constexpr int ORDER_QB = 2;                       // blocks of 32 queries per wavefront
 // Each (head, pivot) count is split over ORDER_COPIES counters picked by the
 // node id, which keeps atomic contention low when many queries share a pivot.
 constexpr int ORDER_COPIES = 16;
@@ -85,8 +86,8 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
 // (for split-precision rows, the high parts).  The workgroup stages the
 // head's pivots in LDS, ORDER_PIVOTS at a time, in MFMA operand order
 // (block j*NM + m: pivots [32j, 32j + 32) of the batch, elements
-// [16m, 16m + 16)); each wavefront scores its 32 queries against all of them
-// with 32x32x16 MFMAs, keys' role taken by the pivots.  npiv is a multiple
+// [16m, 16m + 16)); each wavefront scores its ORDER_QB blocks of 32 queries
+// against all of them with 32x32x16 MFMAs, keys' role taken by the pivots.  npiv is a multiple
 // of 32.
 template <int D, int DP>
 __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
@@ -99,23 +100,30 @@ __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
   const int h = blockIdx.y;
   const int64_t stride = N / npiv > 0 ? N / npiv : 1;
   const int lane = threadIdx.x & 63, lrow = lane & 31, lhalf = lane >> 5;
-  const int64_t i0 = ((int64_t)blockIdx.x * ORDER_WAVES + (threadIdx.x >> 6)) * 32;
+  const int64_t i0 = ((int64_t)blockIdx.x * ORDER_WAVES + (threadIdx.x >> 6)) * (32 * ORDER_QB);
   const bool active = i0 < N;                     // uniform per wavefront
-  const int64_t i = i0 + lrow;
-  const uint16_t* qp = Q + ((i < N ? i : N - 1) * H + h) * D + 8 * lhalf;
-  bf16x8_t qb[NM];
+  bf16x8_t qb[ORDER_QB][NM];
 #pragma unroll
-  for (int m = 0; m < NM; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
-  // Per lane: the best of its pivots.  acc[r] of block j is pivot
-  // base + 32j + 4*lhalf + 8*(r/4) + r%4, increasing in r, j and the batch,
-  // so strict compares keep the lowest index among equal scores.  The loop
-  // keeps the best block's index and scores (sv); the position inside it is
-  // found once at the end.
-  float best = -__builtin_inff();
-  int bblk = 0;
-  float sv[16];
+  for (int b = 0; b < ORDER_QB; ++b) {
+    const int64_t i = i0 + 32 * b + lrow;
+    const uint16_t* qp = Q + ((i < N ? i : N - 1) * H + h) * D + 8 * lhalf;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sv[r] = best;
+    for (int m = 0; m < NM; ++m) qb[b][m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
+  }
+  // Per lane and query block: the best of its pivots.  acc[r] of block j is
+  // pivot base + 32j + 4*lhalf + 8*(r/4) + r%4, increasing in r, j and the
+  // batch, so strict compares keep the lowest index among equal scores.  The
+  // loop keeps the best block's index and scores (sv); the position inside
+  // it is found once at the end.
+  float best[ORDER_QB], sv[ORDER_QB][16];
+  int bblk[ORDER_QB];
+#pragma unroll
+  for (int b = 0; b < ORDER_QB; ++b) {
+    best[b] = -__builtin_inff();
+    bblk[b] = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[b][r] = best[b];
+  }
   for (int base = 0; base < npiv; base += ORDER_PIVOTS) {
     const int nb = npiv - base < ORDER_PIVOTS ? npiv - base : ORDER_PIVOTS;
     if (base > 0) __syncthreads();                // the previous batch has been read
@@ -139,37 +147,49 @@ __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
     }
     __syncthreads();
     if (!active) continue;
-#pragma unroll 4
+#pragma unroll 2
     for (int j = 0; j < nb / 32; ++j) {
-      floatx16_t acc{};
+      floatx16_t acc[ORDER_QB];
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8_t*>(piv + (j * NM + m) * 1024 + lane * 16), qb[m],
-            acc, 0, 0, 0);
-      const float mx =
-          fmaxf(fmaxf(fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])),
-                      fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7]))),
-                fmaxf(fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11])),
-                      fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15]))));
-      const bool up = mx > best;
-      best = up ? mx : best;
-      bblk = up ? base / 32 + j : bblk;
+      for (int b = 0; b < ORDER_QB; ++b) acc[b] = floatx16_t{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] = up ? acc[r] : sv[r];
+      for (int m = 0; m < NM; ++m) {
+        const bf16x8_t pa =
+            *reinterpret_cast<const bf16x8_t*>(piv + (j * NM + m) * 1024 + lane * 16);
+#pragma unroll
+        for (int b = 0; b < ORDER_QB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, qb[b][m], acc[b], 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < ORDER_QB; ++b) {
+        const floatx16_t& x = acc[b];
+        const float mx = fmaxf(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))),
+                               fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])),
+                                     fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]))));
+        const bool up = mx > best[b];
+        best[b] = up ? mx : best[b];
+        bblk[b] = up ? base / 32 + j : bblk[b];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[b][r] = up ? x[r] : sv[b][r];
+      }
     }
   }
   if (!active) return;
-  int r0 = 15;
 #pragma unroll
-  for (int r = 14; r >= 0; --r) r0 = sv[r] == best ? r : r0;
-  int bp = 32 * bblk + 4 * lhalf + 8 * (r0 >> 2) + (r0 & 3);
-  const float ob = __shfl_xor(best, 32);
-  const int op = __shfl_xor(bp, 32);
-  if (ob > best || (ob == best && op < bp)) bp = op;
-  if (lhalf == 0 && i < N) {
-    codes[h * N + i] = (uint16_t)bp;
-    atomicAdd(&counts[((int64_t)h * npiv + bp) * ORDER_COPIES + (i & (ORDER_COPIES - 1))], 1);
+  for (int b = 0; b < ORDER_QB; ++b) {
+    int r0 = 15;
+#pragma unroll
+    for (int r = 14; r >= 0; --r) r0 = sv[b][r] == best[b] ? r : r0;
+    int bp = 32 * bblk[b] + 4 * lhalf + 8 * (r0 >> 2) + (r0 & 3);
+    const float ob = __shfl_xor(best[b], 32);
+    const int op = __shfl_xor(bp, 32);
+    if (ob > best[b] || (ob == best[b] && op < bp)) bp = op;
+    const int64_t i = i0 + 32 * b + lrow;
+    if (lhalf == 0 && i < N) {
+      codes[h * N + i] = (uint16_t)bp;
+      atomicAdd(&counts[((int64_t)h * npiv + bp) * ORDER_COPIES + (i & (ORDER_COPIES - 1))], 1);
+    }
   }
 }
 
@@ -226,7 +246,7 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
   int32_t* aux = reinterpret_cast<int32_t*>(p);
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, s,
                      counts, nb);
-  const dim3 grid((unsigned)ceil_div(N, ORDER_WAVES * 32), (unsigned)H);
+  const dim3 grid((unsigned)ceil_div(N, ORDER_WAVES * 32 * ORDER_QB), (unsigned)H);
   const dim3 block(ORDER_WAVES * 64);
   void (*code_kernel)(const uint16_t*, int64_t, int, int, uint16_t*, int32_t*);
   switch (d) {      // split-precision rows (3d) are grouped by their high parts

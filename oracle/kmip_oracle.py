@@ -165,8 +165,12 @@ def query_grads(q_i, k_sel, v_sel, dout_i, scale: float):
     s = k_sel @ q_i
     p = softmax_selected(s, scale)
     dp = v_sel @ dout_i
-    D = float(p @ dp)
-    ds = p * (dp - D)
+    # dp_j - D evaluated as (dp_j - dp_m) - sum_u p_u (dp_u - dp_m), m the
+    # largest weight: the same value, without the cancellation that drops
+    # the small terms of p . dp when the softmax is nearly one-hot.
+    m = int(np.argmax(p))
+    rel = dp - dp[m]
+    ds = p * (rel - float(p @ rel))
     return p, ds, scale * (ds @ k_sel)
 
 

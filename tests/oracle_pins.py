@@ -335,6 +335,40 @@ def pin_finite_difference(orc, seed=20):
             assert abs(fd - g[i, 0, c]) <= 1e-6 * max(1.0, abs(fd)), (which, i, c, fd, g[i, 0, c])
 
 
+def pin_peaked_softmax_grads(orc, seed=23):
+    """A selection whose best score leads the rest by ~30 (softmax one-hot to
+    ~1e-14): dq against the definition evaluated in 60-digit decimal
+    arithmetic, per-row relative 1e-9.  The gradient is ~1e-14 of its
+    inputs here, so an evaluation that cancels in fp64 fails this pin."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    rng = _rng(seed)
+    for gap in (30.0, 36.0):
+        kk, d = 6, 4
+        q = rng.standard_normal((kk + 1, 1, d))
+        k = rng.standard_normal((kk + 1, 1, d))
+        v = rng.standard_normal((kk + 1, 1, d))
+        do = rng.standard_normal((kk + 1, 1, d))
+        # key 0 scores gap above the others for query 0
+        k[0, 0] = q[0, 0] * (gap / float(q[0, 0] @ q[0, 0]))
+        idx = np.full((kk + 1, 1, kk), -1, dtype=np.int64)
+        idx[0, 0] = np.arange(kk)
+        dq, _, _ = orc.kmip_backward_on_sets(q, k, v, idx, do)
+        D = lambda x: Decimal(repr(float(x)))
+        s = [sum(D(k[j, 0, c]) * D(q[0, 0, c]) for c in range(d)) for j in range(kk)]
+        smax = max(s)
+        e = [(x - smax).exp() for x in s]
+        z = sum(e)
+        p = [x / z for x in e]
+        dp = [sum(D(v[j, 0, c]) * D(do[0, 0, c]) for c in range(d)) for j in range(kk)]
+        Dm = sum(pj * dpj for pj, dpj in zip(p, dp))
+        ds = [pj * (dpj - Dm) for pj, dpj in zip(p, dp)]
+        ref = np.array([float(sum(ds[j] * D(k[j, 0, c]) for j in range(kk))) for c in range(d)])
+        assert np.max(np.abs(ref)) < 1e-9                       # the row is one-hot to ~1e-13
+        err = np.max(np.abs(dq[0, 0] - ref)) / np.max(np.abs(ref))
+        assert err <= 1e-9, (gap, err, dq[0, 0], ref)
+
+
 # ------------------------------------------------------------------ linearity, batching
 def pin_linearity(orc, seed=21):
     rng = _rng(seed)
@@ -365,4 +399,5 @@ def pin_block_diagonal(orc, seed=22):
 
 ALL_PINS = [pin_golden, pin_bruteforce, pin_full_attention, pin_k1, pin_permutation,
             pin_softmax_rows, pin_key_shift, pin_score_exact, pin_grad_identities,
-            pin_backward_autograd, pin_finite_difference, pin_linearity, pin_block_diagonal]
+            pin_backward_autograd, pin_finite_difference, pin_peaked_softmax_grads,
+            pin_linearity, pin_block_diagonal]

@@ -209,9 +209,14 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   // rows of a chunk are requested together (unused slots read the query's
   // own row and count zero), and their partial dot products are reduced in
   // one butterfly that leaves entry t's dp in lane t % 16.
+  // dp_t - D is evaluated as (dp_t - dp_0) - sum_u p_u (dp_u - dp_0), with
+  // entry 0 the best score (the largest weight): the same value, without the
+  // cancellation that loses the small terms of sum_u p_u dp_u when the
+  // softmax is nearly one-hot.
   const int64_t self = row / H;
   double wv[MAXK / 16], dpv[MAXK / 16];
-  double zl = 0.0, dl = 0.0;               // this lane's share of Z and sum w dp
+  double zl = 0.0, dl = 0.0;    // this lane's share of Z and sum w (dp - dp_0)
+  double dp0 = 0.0;
 #pragma unroll
   for (int c = 0; c < MAXK / 16; ++c) {
     wv[c] = 0.0;
@@ -229,10 +234,11 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
         part[u] = j >= 0 ? pp : 0.0;
       }
       const double dp = reduce_scatter16(part, l16);
+      if (c == 0) dp0 = __shfl(dp, 0, 16);
       const bool live = jv[c] >= 0;        // slot c*16 + l16 holds a key
       const double w = live ? (double)__expf(sv[c] - m) : 0.0;
       wv[c] = w;
-      dpv[c] = live ? dp : 0.0;
+      dpv[c] = live ? dp - dp0 : 0.0;
       zl += w;
       dl = fma(w, dpv[c], dl);
     }

@@ -58,14 +58,15 @@ def test_single_graph_forward_backward(n, heads, d, topk):
     _backward_check(w, t, idx, score)
 
 
-@pytest.mark.parametrize("n,heads,law", [(300, 128, "clustered"), (20, 1664, "iid")])
+@pytest.mark.parametrize("n,heads,law", [(300, 128, "clustered"), (20, 1664, "clustered"),
+                                         (20, 1664, "iid")])
 def test_query_order_with_few_nodes_per_head(n, heads, law):
     """N*H >= 32768 groups each head's queries by nearest pivot even when the
     head has few nodes: 32 pivots at node stride N/32 (300 nodes), or pivots
-    clamped to the last node when N < 32 (20 nodes, repeated pivots).  The
-    20-node case draws iid rows: 8 clusters over 20 nodes leave nodes alone
-    in their cluster, whose self score leads by ~30 and whose gradients are
-    ~1e-14, below what a row-relative tolerance can resolve."""
+    clamped to the last node when N < 32 (20 nodes, repeated pivots).  With 8
+    clusters over 20 nodes, nodes alone in their cluster have a self score
+    ~30 above the rest: a softmax one-hot to ~1e-14 and gradients of that
+    size, which the backward must still get to the row tolerance."""
     w = small_case(n, heads, 32, 15, law=law, clusters=8 if law == "clustered" else 0,
                    seed=77 + n)
     t, out, idx, score, st = _forward_check(w)

@@ -124,8 +124,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by query rows across GPUs by design, but this build runs "
-              "on a single MI355X)", file=sys.stderr)
+              "(the path would shard by query rows across GPUs; this benchmark times "
+              "one MI355X)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -59,11 +59,11 @@ __global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B, int
 // the head, at evenly spaced node ids (about one per 96 nodes, so a group
 // fills about three wavefronts; a multiple of 32, at least 32), and a query's
 // group is the pivot with the largest inner product (the lowest pivot index
-// on ties).  The
-// 32 queries of a wavefront then tend to point the same way and share their
-// few high-scoring keys, so the selection pass meets far fewer 32-key blocks
-// holding a candidate for any of its queries.  The order only changes which
-// queries share a wavefront; every query's result is independent of it.
+// on ties).  The 32 queries of a wavefront then tend to point the same way
+// and share their few high-scoring keys, so the selection pass meets far
+// fewer 32-key blocks holding a candidate for any of its queries.  The order
+// only changes which queries share a wavefront; every query's result is
+// independent of it.
 constexpr int ORDER_PIVOTS = 1024;                // pivots staged in LDS at a time
 constexpr int ORDER_MAX_PIVOTS = 16384;           // codes are 16-bit
 int order_pivots(int64_t N) {
@@ -87,8 +87,8 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
 // head's pivots in LDS, ORDER_PIVOTS at a time, in MFMA operand order
 // (block j*NM + m: pivots [32j, 32j + 32) of the batch, elements
 // [16m, 16m + 16)); each wavefront scores its ORDER_QB blocks of 32 queries
-// against all of them with 32x32x16 MFMAs, keys' role taken by the pivots.  npiv is a multiple
-// of 32.
+// against all of them with 32x32x16 MFMAs, keys' role taken by the pivots.
+// npiv is a multiple of 32.
 template <int D, int DP>
 __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
     const uint16_t* __restrict__ Q, int64_t N, int H, int npiv, uint16_t* __restrict__ codes,

@@ -74,6 +74,28 @@ def test_query_order_with_few_nodes_per_head(n, heads, law):
     _backward_check(w, t, idx, score)
 
 
+@pytest.mark.parametrize("n,heads,d,topk", [(8192, 4, 64, 15), (16384, 2, 32, 8),
+                                          (12000, 3, 64, 45)])
+def test_query_order_path_sampled_rows(n, heads, d, topk):
+    """One graph with N*H >= 32768 (pivot query order) for bf16 rows of both
+    widths and a long list: 500 sampled query rows against the oracle, then
+    the backward's dq on those rows and dk, dv on 100 sampled key rows."""
+    from tests.gpu_util import np_, run_backward
+    w = small_case(n, heads, d, topk, law="clustered", clusters=48, seed=n + d + topk)
+    rng = np.random.default_rng(7)
+    rows = rng.choice(n, size=500, replace=False)
+    t, out, idx, score, st = _forward_check(w, rows=rows)
+    assert st["rows"] == 500 * heads
+    dq, dk, dv = run_backward(w, t, idx, score)
+    q, k, v = decode(w)
+    idx_n, do = np_(idx).astype(np.int64), w.dout.astype(np.float64)
+    assert_rows_close(np_(dq)[rows], orc.dq_rows_on_sets(q, k, v, idx_n, do, rows), "dq")
+    keys = rng.choice(n, size=100, replace=False)
+    rk, rv = orc.dkv_keys_on_sets(q, k, v, idx_n, do, keys)
+    assert_rows_close(np_(dk)[keys], rk, "dk")
+    assert_rows_close(np_(dv)[keys], rv, "dv")
+
+
 @pytest.mark.parametrize("topk", [1, 2, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 45, 48, 63, 64])
 def test_every_list_length(topk):
     w = small_case(400, 2, 32, topk, seed=2000 + topk)

@@ -22,11 +22,11 @@
 //    of exact bf16 products).  Lane l holds query l%32 and 16 of the 32 keys,
 //    so each lane sees a private half of every query's key stream, in
 //    ascending key order.
-//  * Two passes.  The threshold pass scores every fourth chunk only (every
-//    sixteenth on graphs of 2^16 keys or more with lists of at most 16,
-//    every second for longer lists) and keeps, per lane and query, the top-k of
-//    the maxima of SCAN_CHUNKS consecutive ranges of those keys (uniform,
-//    lockstep insertions); these
+//  * Two passes.  The threshold pass scores a sample of the chunks (with
+//    lists of at most 16: every chunk below 2^14 keys, every fourth up to
+//    2^16 keys, every sixteenth beyond; every second for longer lists) and
+//    keeps, per lane and query, the top-k of the maxima of SCAN_CHUNKS
+//    consecutive ranges of those keys (uniform, lockstep insertions).  These
 //    maxima are scores of distinct keys, so the k-th largest over both halves
 //    is a lower bound T of the query's k-th score.
 //    The selection pass then runs the exact running top-k seeded with
@@ -228,12 +228,17 @@ struct Scanner {
     const int lrow = lane & 31, lhalf = lane >> 5;
     const int64_t nkeys = t.ke - t.kb;
     const int nchunks = (int)((nkeys + S::TK - 1) / S::TK);
-    // Chunks scored by this pass: c = j * sample for j < nproc.  Graphs of
-    // 2^16 keys or more sample the threshold pass four times as sparsely
-    // (short lists): at N = 10^5 and 5 * 10^5 that measured 1-2 % faster,
-    // while a sparser sample at N = 31623 and on graphs of a few thousand
-    // keys was 3-10 % slower.
-    const int sample = PRE && KP <= 16 && nkeys >= (int64_t)1 << 16 ? 4 * SAMPLE : SAMPLE;
+    // Chunks scored by this pass: c = j * sample for j < nproc.  With short
+    // lists the stride follows the graph's size: every chunk below 2^14 keys
+    // (there the bound from a sample is so loose that the selection pass
+    // spends most of its time on candidates: the 64-graph batch of 500-5000
+    // nodes and N = 8192 measured 9-15 % faster than at stride 4), SAMPLE up
+    // to 2^16 keys (stride 2 at N = 31623 was 5 % slower), 4 * SAMPLE from
+    // 2^16 keys on (1-2 % faster than 2 * SAMPLE at N = 10^5 and 5 * 10^5).
+    const int sample = !(PRE && KP <= 16)       ? SAMPLE
+                       : nkeys >= (int64_t)1 << 16 ? 4 * SAMPLE
+                       : nkeys >= (int64_t)1 << 14 ? SAMPLE
+                                                   : 1;
     const int nproc = (nchunks + sample - 1) / sample;
 
     // The ring may still be read by slower waves of the previous sub-tile.

@@ -116,8 +116,14 @@ def check_selection(gpu_idx, gpu_score, q, k, offsets, topk, rows, heads=None, *
             gs = np.asarray(gpu_score[i, h, :kk], dtype=np.float64)
             seps = saved_coef * float(np.linalg.norm(q[i, h])) * kmax_of[b]
             assert np.all(np.abs(gs - inside) <= seps + 1e-30), (i, h, "score", gs - inside, seps)
-            eq = np.nonzero(np.diff(gs) == 0)[0]
-            assert np.all(g[eq] < g[eq + 1]), (i, h, "tie order", g, gs)
+            if not split:
+                # Equal saved scores are equal scan scores: ascending ids.
+                # The fp32 entry point orders by its split-precision scan
+                # scores but saves rescored fp32 values, which may tie where
+                # the scan's did not; its tie rule is checked on inputs with
+                # duplicate keys instead (tests/test_gpu_f32.py).
+                eq = np.nonzero(np.diff(gs) == 0)[0]
+                assert np.all(g[eq] < g[eq + 1]), (i, h, "tie order", g, gs)
             stats["rows"] += 1
     return stats
 

@@ -158,8 +158,8 @@ kmip_status_t backward_impl(const void* q, const void* k, const void* v, bool f3
   w += sort_scratch_bytes(P, HN);
   double* partials = reinterpret_cast<double*>(w);
 
-  st = launch_status(launch_bwd_query(k, v, f32, N, H, d, topk, topk_idx, topk_score, dout, dq,
-                                      pairs, s));
+  st = launch_status(launch_bwd_query(q, k, v, f32, N, H, d, topk, topk_idx, dout, dq, pairs,
+                                      s));
   if (st != KMIP_OK) return st;
   st = launch_status(launch_selection_transpose(topk_idx, N, H, topk, &sc, s));
   if (st != KMIP_OK) return st;

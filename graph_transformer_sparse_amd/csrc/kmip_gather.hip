@@ -182,33 +182,34 @@ __device__ __forceinline__ double reduce_scatter16(const double (&v)[16], int l1
 
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_query_kernel(
-    const T* __restrict__ Kt, const T* __restrict__ V, int64_t NH, int H,
-    int topk, const int32_t* __restrict__ idx, const float* __restrict__ score,
-    const float* __restrict__ dout, float* __restrict__ dq, float2* __restrict__ pairs) {
+    const T* __restrict__ Q, const T* __restrict__ Kt, const T* __restrict__ V, int64_t NH,
+    int H, int topk, const int32_t* __restrict__ idx, const float* __restrict__ dout,
+    float* __restrict__ dq, float2* __restrict__ pairs) {
   constexpr int EPL = D / 16;
   const int l16 = threadIdx.x & 15;
   const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 4);
   if (row >= NH) return;
   const int h = (int)(row % H);
   const int32_t* ir = idx + row * topk;
-  const float* sr = score + row * topk;
 
   int jv[MAXK / 16];
-  float sv[MAXK / 16];
 #pragma unroll
   for (int c = 0; c < MAXK / 16; ++c) {
     const int t = c * 16 + l16;
     jv[c] = t < topk ? ir[t] : -1;
-    sv[c] = t < topk ? sr[t] : 0.f;
   }
-  float g[EPL];
+  float g[EPL], qx[EPL];
   load_cols<EPL>(dout + row * D + l16 * EPL, g);
-  const float m = __shfl(sv[0], 0, 16);
+  load_cols<EPL>(Q + row * D + l16 * EPL, qx);
 
-  // Pass 1: weights w_t and dp_t; lane (t % 16) keeps entry t.  The 16 V
-  // rows of a chunk are requested together (unused slots read the query's
-  // own row and count zero), and their partial dot products are reduced in
-  // one butterfly that leaves entry t's dp in lane t % 16.
+  // Pass 1: weights w_t and dp_t; lane (t % 16) keeps entry t.  The 16 K
+  // and V rows of a chunk are requested together (unused slots read the
+  // query's own row and count zero), and their partial dot products with q
+  // and dO are reduced in butterflies that leave entry t's score and dp in
+  // lane t % 16.  The scores are recomputed here in fp64 from the input
+  // rows (exact products), not taken from the forward's fp32 scores: where
+  // the gradient is a cancelling sum of small softmax terms, the fp32
+  // accumulation error of the scores (a few ulps) would be amplified.
   // dp_t - D is evaluated as (dp_t - dp_0) - sum_u p_u (dp_u - dp_0), with
   // entry 0 the best score (the largest weight): the same value, without the
   // cancellation that loses the small terms of sum_u p_u dp_u when the
@@ -216,27 +217,39 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   const int64_t self = row / H;
   double wv[MAXK / 16], dpv[MAXK / 16];
   double zl = 0.0, dl = 0.0;    // this lane's share of Z and sum w (dp - dp_0)
-  double dp0 = 0.0;
+  double dp0 = 0.0, m = 0.0;    // entry 0's dp and score (the forward's best)
 #pragma unroll
   for (int c = 0; c < MAXK / 16; ++c) {
     wv[c] = 0.0;
     dpv[c] = 0.0;
     if (c * 16 < topk) {
-      double part[16];
+      double part[16], spart[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int j = __shfl(jv[c], u, 16);
-        float x[EPL];
-        load_cols<EPL>(V + ((j >= 0 ? (int64_t)j : self) * H + h) * D + l16 * EPL, x);
-        double pp = 0.0;
+        const int64_t jr = ((j >= 0 ? (int64_t)j : self) * H + h) * D + l16 * EPL;
+        float x[EPL], y[EPL];
+        load_cols<EPL>(V + jr, x);
+        load_cols<EPL>(Kt + jr, y);
+        double pp = 0.0, ss = 0.0;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) pp = fma((double)g[e], (double)x[e], pp);
+        for (int e = 0; e < EPL; ++e) {
+          pp = fma((double)g[e], (double)x[e], pp);
+          ss = fma((double)qx[e], (double)y[e], ss);
+        }
         part[u] = j >= 0 ? pp : 0.0;
+        spart[u] = j >= 0 ? ss : 0.0;
       }
       const double dp = reduce_scatter16(part, l16);
-      if (c == 0) dp0 = __shfl(dp, 0, 16);
+      const double sc = reduce_scatter16(spart, l16);
+      if (c == 0) {
+        dp0 = __shfl(dp, 0, 16);
+        m = __shfl(sc, 0, 16);
+      }
       const bool live = jv[c] >= 0;        // slot c*16 + l16 holds a key
-      const double w = live ? (double)__expf(sv[c] - m) : 0.0;
+      // fp64 exp: weights far below the best (e^-87 and less) stay normal
+      // numbers instead of underflowing in fp32.
+      const double w = live ? exp(sc - m) : 0.0;
       wv[c] = w;
       dpv[c] = live ? dp - dp0 : 0.0;
       zl += w;
@@ -283,12 +296,12 @@ void launch_gather_t(const T* v, int64_t NH, int H, int topk, const int32_t* idx
 }
 
 template <int D, typename T>
-void launch_bwd_query_t(const T* k, const T* v, int64_t NH, int H, int topk, const int32_t* idx,
-                        const float* score, const float* dout, float* dq, float2* pairs,
+void launch_bwd_query_t(const T* q, const T* k, const T* v, int64_t NH, int H, int topk,
+                        const int32_t* idx, const float* dout, float* dq, float2* pairs,
                         hipStream_t s) {
   const unsigned blocks = (unsigned)ceil_div(NH, ROWS_PER_BLOCK);
-  hipLaunchKernelGGL((bwd_query_kernel<D, T>), dim3(blocks), dim3(256), 0, s, k, v, NH, H,
-                     topk, idx, score, dout, dq, pairs);
+  hipLaunchKernelGGL((bwd_query_kernel<D, T>), dim3(blocks), dim3(256), 0, s, q, k, v, NH, H,
+                     topk, idx, dout, dq, pairs);
 }
 
 }  // namespace
@@ -319,20 +332,22 @@ hipError_t launch_gather_av(const uint16_t* v, int64_t N, int H, int d, int topk
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_query(const void* k, const void* v, bool f32, int64_t N, int H, int d,
-                            int topk, const int32_t* topk_idx, const float* topk_score,
-                            const float* dout, float* dq, float2* pairs, hipStream_t s) {
+hipError_t launch_bwd_query(const void* q, const void* k, const void* v, bool f32, int64_t N,
+                            int H, int d, int topk, const int32_t* topk_idx, const float* dout,
+                            float* dq, float2* pairs, hipStream_t s) {
   const int64_t NH = N * H;
-  const uint16_t *kb = static_cast<const uint16_t*>(k), *vb = static_cast<const uint16_t*>(v);
-  const float *kf = static_cast<const float*>(k), *vf = static_cast<const float*>(v);
+  const uint16_t *qb = static_cast<const uint16_t*>(q), *kb = static_cast<const uint16_t*>(k),
+                 *vb = static_cast<const uint16_t*>(v);
+  const float *qf = static_cast<const float*>(q), *kf = static_cast<const float*>(k),
+              *vf = static_cast<const float*>(v);
   if (d == 32 && !f32)
-    launch_bwd_query_t<32>(kb, vb, NH, H, topk, topk_idx, topk_score, dout, dq, pairs, s);
+    launch_bwd_query_t<32>(qb, kb, vb, NH, H, topk, topk_idx, dout, dq, pairs, s);
   else if (d == 32)
-    launch_bwd_query_t<32>(kf, vf, NH, H, topk, topk_idx, topk_score, dout, dq, pairs, s);
+    launch_bwd_query_t<32>(qf, kf, vf, NH, H, topk, topk_idx, dout, dq, pairs, s);
   else if (d == 64 && !f32)
-    launch_bwd_query_t<64>(kb, vb, NH, H, topk, topk_idx, topk_score, dout, dq, pairs, s);
+    launch_bwd_query_t<64>(qb, kb, vb, NH, H, topk, topk_idx, dout, dq, pairs, s);
   else if (d == 64)
-    launch_bwd_query_t<64>(kf, vf, NH, H, topk, topk_idx, topk_score, dout, dq, pairs, s);
+    launch_bwd_query_t<64>(qf, kf, vf, NH, H, topk, topk_idx, dout, dq, pairs, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -120,11 +120,12 @@ hipError_t launch_gather_rescore_av(const float* q, const float* k, const float*
                                     int H, int d, int topk, const int32_t* topk_idx,
                                     float* topk_score, float* out, hipStream_t s);
 
-// Backward, query side: dq and the per-pair (p, ds).  K and V are bf16 bits,
-// or fp32 when f32 is set.
-hipError_t launch_bwd_query(const void* k, const void* v, bool f32, int64_t N, int H, int d,
-                            int topk, const int32_t* topk_idx, const float* topk_score,
-                            const float* dout, float* dq, float2* pairs, hipStream_t s);
+// Backward, query side: dq and the per-pair (p, ds), with the selected
+// scores recomputed from q and k.  Q, K and V are bf16 bits, or fp32 when
+// f32 is set.
+hipError_t launch_bwd_query(const void* q, const void* k, const void* v, bool f32, int64_t N,
+                            int H, int d, int topk, const int32_t* topk_idx, const float* dout,
+                            float* dq, float2* pairs, hipStream_t s);
 
 // Backward, selection transpose: stable sort of the pairs by key h*N + j
 // (padding slots: H*N), carrying each pair's id and its (p, ds); key segment

@@ -127,15 +127,20 @@ kmip_status_t kmip_gather_softmax_av(const void* v, int64_t N, int H, int d, int
 /*
  * k-MIP attention backward with the forward selection held fixed: gradients
  * of L = sum(dout * out) flow through the selected entries only.  With
- * p = softmax of the saved scores, dp_ij = dout_i . v_j,
+ * p = softmax of the selected scores q_i . k_j, dp_ij = dout_i . v_j,
  * D_i = sum_j p_ij dp_ij and ds_ij = p_ij (dp_ij - D_i):
  *   dq_i = sum_j ds_ij k_j,  dk_j = sum_i ds_ij q_i,  dv_j = sum_i p_ij dout_i.
  * Every row of dq, dk and dv is written; keys no query selected get exact
  * zeros.  The key-side sums run in a fixed order (no atomics), so the result
- * is bitwise repeatable.
+ * is bitwise repeatable.  The selected scores are recomputed from q and k
+ * with fp64 sums of the exact products (not read from topk_score), and
+ * dp_ij - D_i is evaluated relative to entry 0's dp, so rows whose softmax
+ * is nearly one-hot lose no accuracy to cancellation.
  *
  *  q, k, v                 in   bf16 [N][H][d] (as given to kmip_forward)
- *  topk_idx, topk_score    in   as written by kmip_forward
+ *  topk_idx                in   as written by kmip_forward
+ *  topk_score              in   as written by kmip_forward (checked for
+ *                               non-null; the scores are recomputed)
  *  dout                    in   fp32 [N][H][d]
  *  dq, dk, dv              out  fp32 [N][H][d]
  *  workspace               scratch of at least kmip_backward_workspace_bytes(...)
@@ -160,8 +165,8 @@ kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t
  * relative.  The selection, its order and its tie rule refer to these
  * scores.  topk_score then holds each selected key's score recomputed in
  * fp32 from the fp32 rows (d products, fp32 accumulation), and the softmax
- * and kmip_backward_f32 use those, so the gradients do not inherit the
- * split's error; consecutive saved scores may therefore be out of order by
+ * uses those (kmip_backward_f32 recomputes them in fp64), so neither the
+ * output nor the gradients inherit the split's error; consecutive saved scores may therefore be out of order by
  * up to twice the split error.  The weighted sum reads fp32 v rows.  Every
  * element of q and k must be finite and below the bf16 maximum (~3.39e38) in
  * magnitude.
@@ -180,7 +185,7 @@ kmip_status_t kmip_forward_f32(const float* q, const float* k, const float* v, i
  * Backward of kmip_forward_f32 (the selection held fixed, as kmip_backward):
  * q, k, v fp32 [N][H][d], topk_idx / topk_score as written by
  * kmip_forward_f32, workspace of kmip_backward_workspace_bytes(...) bytes.
- * The products dout.v and k, q rows enter fp64 sums exactly, as in
+ * The scores q.k and the products dout.v enter fp64 sums exactly, as in
  * kmip_backward.
  */
 kmip_status_t kmip_backward_f32(const float* q, const float* k, const float* v, int64_t N,

@@ -96,6 +96,28 @@ def test_query_order_path_sampled_rows(n, heads, d, topk):
     assert_rows_close(np_(dv)[keys], rv, "dv")
 
 
+@pytest.mark.parametrize("seed", [4242, 4243])
+def test_extreme_softmax_ranges(seed):
+    """Tight clusters in 64 dimensions: a node's own key scores ~80 above the
+    rest of its selection, so those weights are ~e^-80 (below fp32's normal
+    range) and some gradient rows are ~1e-36, or cancelling sums of tiny
+    terms.  The backward recomputes the selected scores and their weights in
+    fp64, which keeps such rows to 1e-4: the fp32 rounding of the per-pair
+    (p, ds) carried to the key side.  Weights from the forward's fp32 scores
+    measured 2e-4 on dk here."""
+    from tests.gpu_util import np_, run_backward
+    w = with_offsets(f"extreme_{seed}", list(np.random.default_rng(seed).integers(147, 276, 9)),
+                     heads=3, d=64, topk=17, law="clustered", clusters=64, sigma=0.05,
+                     seed=seed)
+    t, out, idx, score, st = _forward_check(w)
+    dq, dk, dv = run_backward(w, t, idx, score)
+    q, k, v = decode(w)
+    rq, rk, rv = orc.kmip_backward_on_sets(q, k, v, np_(idx).astype(np.int64),
+                                           w.dout.astype(np.float64))
+    for name, x, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        assert_rows_close(np_(x), ref, name, tol=1e-4)
+
+
 @pytest.mark.parametrize("topk", [1, 2, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 45, 48, 63, 64])
 def test_every_list_length(topk):
     w = small_case(400, 2, 32, topk, seed=2000 + topk)

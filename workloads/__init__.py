@@ -162,13 +162,14 @@ def small_case(n: int, heads: int, d: int, topk: int, *, law: str = "iid", clust
 
 
 def with_offsets(name: str, sizes, heads: int, d: int, topk: int, *, law="iid",
-                 clusters=0, backward=True, seed=777, dtype: str = "bf16") -> Workload:
+                 clusters=0, sigma: float = 0.3, backward=True, seed=777,
+                 dtype: str = "bf16") -> Workload:
     """A case with explicit graph sizes (edge cases: tiny graphs, n_b < k, ...)."""
     sizes = np.asarray(sizes, dtype=np.int64)
     offsets = np.zeros(len(sizes) + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(sizes)
     n = int(offsets[-1])
     w = make_workload(name, n=n, heads=heads, d=d, topk=topk, law=law, clusters=clusters,
-                      backward=backward, seed=seed, dtype=dtype)
+                      sigma=sigma, backward=backward, seed=seed, dtype=dtype)
     w.offsets = offsets.astype(np.int32)
     return w

@@ -215,6 +215,10 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   // cancellation that loses the small terms of sum_u p_u dp_u when the
   // softmax is nearly one-hot.
   const int64_t self = row / H;
+  // The first chunk's K rows (this lane's columns) are kept in LDS for pass
+  // 2, lane-major so that the accesses are conflict-free.
+  __shared__ float kl[16 * EPL * 256];
+  float* kmine = kl + threadIdx.x;
   double wv[MAXK / 16], dpv[MAXK / 16];
   double zl = 0.0, dl = 0.0;    // this lane's share of Z and sum w (dp - dp_0)
   double dp0 = 0.0, m = 0.0;    // entry 0's dp and score (the forward's best)
@@ -239,6 +243,10 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
         }
         part[u] = j >= 0 ? pp : 0.0;
         spart[u] = j >= 0 ? ss : 0.0;
+        if (c == 0) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) kmine[(u * EPL + e) * 256] = y[e];
+        }
       }
       const double dp = reduce_scatter16(part, l16);
       const double sc = reduce_scatter16(spart, l16);
@@ -275,7 +283,12 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
         const int j = __shfl(jv[c], u, 16);
         const double dsu = __shfl(ds, u, 16);   // 0 on unused slots
         float x[EPL];
-        load_cols<EPL>(Kt + ((j >= 0 ? (int64_t)j : self) * H + h) * D + l16 * EPL, x);
+        if (c == 0) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) x[e] = kmine[(u * EPL + e) * 256];
+        } else {
+          load_cols<EPL>(Kt + ((j >= 0 ? (int64_t)j : self) * H + h) * D + l16 * EPL, x);
+        }
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] = fma(dsu, (double)x[e], acc[e]);
       }

@@ -91,9 +91,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_aux_kernel(int32_t* __restr
 }
 
 // One block scans up to SCAN_SINGLE_TILES tiles in order, carrying the sum.
+// in and out may be the same array (each element is read before it is
+// written, by the same thread), so neither is declared __restrict__.
 constexpr int SCAN_SINGLE_TILES = 4;
 __global__ __launch_bounds__(SCAN_THREADS) void scan_single_kernel(
-    const int32_t* __restrict__ in, int32_t* __restrict__ out, int64_t n) {
+    const int32_t* in, int32_t* out, int64_t n) {
   __shared__ int32_t sh[SCAN_THREADS / 64];
   int32_t carry = 0;
   for (int64_t tile = 0; tile < n; tile += SCAN_TILE_ELEMS) {
@@ -116,9 +118,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_single_kernel(
   }
 }
 
+// in and out may be the same array (see scan_single_kernel).
 __global__ __launch_bounds__(SCAN_THREADS) void scan_down_kernel(
-    const int32_t* __restrict__ in, int32_t* __restrict__ out, int64_t n,
-    const int32_t* __restrict__ aux) {
+    const int32_t* in, int32_t* out, int64_t n, const int32_t* __restrict__ aux) {
   __shared__ int32_t sh[SCAN_THREADS / 64];
   const int64_t base = (int64_t)blockIdx.x * SCAN_TILE_ELEMS + (int64_t)threadIdx.x * SCAN_ITEMS;
   int32_t v[SCAN_ITEMS];

@@ -125,8 +125,12 @@ kmip_status_t kmip_gather_softmax_av(const void* v, int64_t N, int H, int d, int
                                      float* out, kmip_stream_t stream);
 
 /*
- * k-MIP attention backward with the forward selection held fixed: gradients
- * of L = sum(dout * out) flow through the selected entries only.  With
+ * k-MIP attention backward with the forward selection held fixed (page
+ * "k-Maximum Inner Product Attention for Graph Transformers ...", Appendix J,
+ * Table 10: the training setting, whose forward and backward passes the page
+ * times separately; the gradient is that of the Abstract's operation, which
+ * is piecewise constant in the selection).  Gradients of
+ * L = sum(dout * out) flow through the selected entries only.  With
  * p = softmax of the selected scores q_i . k_j, dp_ij = dout_i . v_j,
  * D_i = sum_j p_ij dp_ij and ds_ij = p_ij (dp_ij - D_i):
  *   dq_i = sum_j ds_ij k_j,  dk_j = sum_i ds_ij q_i,  dv_j = sum_i p_ij dout_i.

@@ -72,12 +72,17 @@ def select_topk_row(s: np.ndarray, topk: int) -> np.ndarray:
 
 
 def softmax_selected(s_sel: np.ndarray, scale: float) -> np.ndarray:
-    """Softmax over the selected scores (a 1-D array, best first)."""
+    """Softmax of scale * s over the last axis.  Entries of -inf are slots
+    that hold no key: they get weight 0, and a row with no key at all gets
+    all zeros."""
+    s_sel = np.asarray(s_sel, dtype=np.float64)
     if s_sel.size == 0:
         return s_sel.copy()
-    m = s_sel.max()
-    w = np.exp(scale * (s_sel - m))
-    return w / w.sum()
+    m = s_sel.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    w = np.where(np.isneginf(s_sel), 0.0, np.exp(scale * (s_sel - m)))
+    z = w.sum(axis=-1, keepdims=True)
+    return np.divide(w, z, out=np.zeros_like(w), where=z > 0)
 
 
 # ---------------------------------------------------------------- forward
@@ -125,7 +130,13 @@ def kmip_forward(q, k, v, offsets, topk: int, scale: float = 1.0, rows=None,
 
 
 # ---------------------------------------------------------------- fixed sets
-def attend_on_sets(q, k, v, idx, rows=None, scale: float = 1.0):
+def _gather_selected(x, js, h):
+    """Rows x[j, h] for a block of index rows js [R][K] (-1 slots give a
+    placeholder row that the caller masks out)."""
+    return x[np.where(js >= 0, js, 0), h, :]
+
+
+def attend_on_sets(q, k, v, idx, rows=None, scale: float = 1.0, block: int = 8192):
     """Softmax-AV on given index sets (idx [R][H][topk], -1 = unused slot).
 
     Used to re-evaluate a selection produced elsewhere.  Returns dict with
@@ -139,142 +150,70 @@ def attend_on_sets(q, k, v, idx, rows=None, scale: float = 1.0):
     score = np.full((R, heads, K), NEG_INF)
     p = np.zeros((R, heads, K))
     out = np.zeros((R, heads, d))
-    for r in range(R):
-        i = rows[r]
-        for h in range(heads):
-            sel = idx[r, h]
-            valid = sel >= 0
-            js = sel[valid]
-            if js.size == 0:
-                continue
-            s = k[js, h, :] @ q[i, h, :]
+    for h in range(heads):
+        for a in range(0, R, block):
+            js = idx[a:a + block, h, :]
+            valid = js >= 0
+            ks = _gather_selected(k, js, h)                          # [r][K][d]
+            s = np.einsum("rkc,rc->rk", ks, q[rows[a:a + block], h, :])
+            s = np.where(valid, s, NEG_INF)
             w = softmax_selected(s, scale)
-            score[r, h, valid] = s
-            p[r, h, valid] = w
-            out[r, h, :] = w @ v[js, h, :]
+            score[a:a + block, h] = s
+            p[a:a + block, h] = w
+            out[a:a + block, h] = np.einsum("rk,rkc->rc", w, _gather_selected(v, js, h))
     return dict(score=score, p=p, out=out)
 
 
-def query_grads(q_i, k_sel, v_sel, dout_i, scale: float):
-    """Per-query backward with the selection fixed.
+def query_grads(q_rows, k_sel, v_sel, dout_rows, valid, scale: float):
+    """Backward of a block of query rows with their selections fixed.
 
-    k_sel, v_sel: the selected key / value rows (best first).  Returns
-    (p, ds, dq_i):  p = softmax(scale s), dp_j = dO_i . v_j,
-    D = sum_j p_j dp_j, ds_j = p_j (dp_j - D), dq_i = scale sum_j ds_j k_j.
+    q_rows, dout_rows [R][d]; k_sel, v_sel [R][K][d], the selected key and
+    value rows (slots with valid == False hold no key).  Per row:
+    s_j = q . k_j, p = softmax(scale s), dp_j = dO . v_j, D = sum_j p_j dp_j,
+    ds_j = p_j (dp_j - D), dq = scale sum_j ds_j k_j.  Returns (p, ds, dq);
+    p and ds are 0 on slots without a key.
     """
-    s = k_sel @ q_i
+    s = np.where(valid, np.einsum("rkc,rc->rk", k_sel, q_rows), NEG_INF)
     p = softmax_selected(s, scale)
-    dp = v_sel @ dout_i
+    dp = np.where(valid, np.einsum("rkc,rc->rk", v_sel, dout_rows), 0.0)
     # dp_j - D evaluated as (dp_j - dp_m) - sum_u p_u (dp_u - dp_m), m the
-    # largest weight: the same value, without the cancellation that drops
-    # the small terms of p . dp when the softmax is nearly one-hot.
-    m = int(np.argmax(p))
-    rel = dp - dp[m]
-    ds = p * (rel - float(p @ rel))
-    return p, ds, scale * (ds @ k_sel)
+    # largest weight of the row: the same value, without the cancellation
+    # that drops the small terms of p . dp when the softmax is nearly one-hot.
+    m = np.argmax(p, axis=1)
+    rel = np.where(valid, dp - np.take_along_axis(dp, m[:, None], axis=1), 0.0)
+    ds = p * (rel - np.einsum("rk,rk->r", p, rel)[:, None])
+    return p, ds, scale * np.einsum("rk,rkc->rc", ds, k_sel)
 
 
-def kmip_backward_on_sets(q, k, v, idx, dout, scale: float = 1.0):
+def kmip_backward_on_sets(q, k, v, idx, dout, scale: float = 1.0, rows=None,
+                          block: int = 8192):
     """Gradients of L = sum(dout * out) with the selection idx held fixed.
 
-    idx: int [N][H][topk] (every node is a query row).  Returns dq, dk, dv,
-    float64 [N][H][d].  Keys selected by no query get exactly zero.
+    idx: int [R][H][topk] for the query nodes `rows` (every node when None).
+    Returns dq [R][H][d] of those rows and the dk, dv contributions they make,
+    [N][H][d] (with rows=None: the full gradients).  Keys selected by no
+    query get exactly zero.
       dp_ij = dO_i . v_j,  D_i = sum_j p_ij dp_ij,  ds_ij = p_ij (dp_ij - D_i)
       dQ_i = scale sum_j ds_ij k_j,  dK_j = scale sum_i ds_ij q_i,
       dV_j = sum_i p_ij dO_i
     """
     n, heads, d = q.shape
     idx = np.asarray(idx, dtype=np.int64)
-    dq = np.zeros((n, heads, d))
+    rows = np.arange(idx.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    dq = np.zeros((R, heads, d))
     dk = np.zeros((n, heads, d))
     dv = np.zeros((n, heads, d))
     for h in range(heads):
-        for i in range(n):
-            sel = idx[i, h]
-            js = sel[sel >= 0]
-            if js.size == 0:
-                continue
-            p, ds, dq[i, h, :] = query_grads(q[i, h, :], k[js, h, :], v[js, h, :],
-                                             dout[i, h, :], scale)
-            np.add.at(dk[:, h, :], js, scale * ds[:, None] * q[i, h, :][None, :])
-            np.add.at(dv[:, h, :], js, p[:, None] * dout[i, h, :][None, :])
+        for a in range(0, R, block):
+            js = idx[a:a + block, h, :]
+            valid = js >= 0
+            qr = q[rows[a:a + block], h, :]
+            gr = dout[rows[a:a + block], h, :]
+            p, ds, dq[a:a + block, h] = query_grads(qr, _gather_selected(k, js, h),
+                                                    _gather_selected(v, js, h), gr, valid,
+                                                    scale)
+            r_of, t_of = np.nonzero(valid)
+            np.add.at(dk[:, h, :], js[r_of, t_of], scale * ds[r_of, t_of, None] * qr[r_of])
+            np.add.at(dv[:, h, :], js[r_of, t_of], p[r_of, t_of, None] * gr[r_of])
     return dq, dk, dv
-
-
-def kmip_backward_rows(q, k, v, rows, idx_rows, dout, scale: float = 1.0):
-    """Backward contributions of a subset of query rows (selection fixed).
-
-    idx_rows: int [R][H][topk] for the node ids in rows.  Returns dq of those
-    rows [R][H][d] and the dk, dv contributions they make ([N][H][d]); the
-    full gradients are the sums of such contributions over all rows.
-    """
-    n, heads, d = q.shape
-    rows = np.asarray(rows, dtype=np.int64)
-    dq = np.zeros((rows.size, heads, d))
-    dk = np.zeros((n, heads, d))
-    dv = np.zeros((n, heads, d))
-    for r, i in enumerate(rows):
-        for h in range(heads):
-            sel = idx_rows[r, h]
-            js = sel[sel >= 0]
-            if js.size == 0:
-                continue
-            p, ds, dq[r, h, :] = query_grads(q[i, h, :], k[js, h, :], v[js, h, :],
-                                             dout[i, h, :], scale)
-            np.add.at(dk[:, h, :], js, scale * ds[:, None] * q[i, h, :][None, :])
-            np.add.at(dv[:, h, :], js, p[:, None] * dout[i, h, :][None, :])
-    return dq, dk, dv
-
-
-def kmip_backward(q, k, v, offsets, topk: int, dout, scale: float = 1.0):
-    """Forward selection, then the fixed-selection gradients."""
-    fw = kmip_forward(q, k, v, offsets, topk, scale=scale)
-    return kmip_backward_on_sets(q, k, v, fw["idx"], dout, scale=scale)
-
-
-# ---------------------------------------------------------------- sampled rows
-def row_scores(q, k, offsets, i: int, h: int):
-    """Full fp64 score row of query (i, h) over its graph, with the graph start."""
-    n = q.shape[0]
-    for lo, hi in graph_ranges(offsets, n):
-        if lo <= i < hi:
-            return k[lo:hi, h, :] @ q[i, h, :], lo
-    raise IndexError(i)
-
-
-def dq_rows_on_sets(q, k, v, idx, dout, rows, scale: float = 1.0):
-    """dQ for the given node rows (idx [N][H][topk] over all nodes)."""
-    heads, d = q.shape[1], q.shape[2]
-    rows = np.asarray(rows, dtype=np.int64)
-    res = np.zeros((rows.size, heads, d))
-    for r, i in enumerate(rows):
-        for h in range(heads):
-            sel = idx[i, h]
-            js = sel[sel >= 0]
-            if js.size == 0:
-                continue
-            res[r, h, :] = query_grads(q[i, h, :], k[js, h, :], v[js, h, :],
-                                       dout[i, h, :], scale)[2]
-    return res
-
-
-def dkv_keys_on_sets(q, k, v, idx, dout, keys, scale: float = 1.0):
-    """dK and dV for the given key nodes, summing over every query that
-    selected them in idx [N][H][topk]."""
-    heads, d = q.shape[1], q.shape[2]
-    keys = np.asarray(keys, dtype=np.int64)
-    dk = np.zeros((keys.size, heads, d))
-    dv = np.zeros((keys.size, heads, d))
-    for h in range(heads):
-        idx_h = idx[:, h, :]
-        for r, j in enumerate(keys):
-            qi, slot = np.nonzero(idx_h == j)
-            for i, t in zip(qi, slot):
-                sel = idx_h[i]
-                js = sel[sel >= 0]
-                p, ds, _ = query_grads(q[i, h, :], k[js, h, :], v[js, h, :],
-                                       dout[i, h, :], scale)
-                pos = int(np.nonzero(js == j)[0][0])
-                dk[r, h, :] += scale * ds[pos] * q[i, h, :]
-                dv[r, h, :] += p[pos] * dout[i, h, :]
-    return dk, dv

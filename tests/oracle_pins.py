@@ -295,20 +295,15 @@ def pin_backward_autograd(orc, seed=19):
         assert np.allclose(dq, gq, atol=1e-12, rtol=0)
         assert np.allclose(dk, gk, atol=1e-12, rtol=0)
         assert np.allclose(dv, gv, atol=1e-12, rtol=0)
-        # the sampled-row helpers agree with the full backward
-        rows = np.array([0, n // 2, n - 1])
-        assert np.allclose(orc.dq_rows_on_sets(q, k, v, fw["idx"], do, rows, scale=scale),
-                           dq[rows], atol=1e-13, rtol=0)
-        sk, sv = orc.dkv_keys_on_sets(q, k, v, fw["idx"], do, rows, scale=scale)
-        assert np.allclose(sk, dk[rows], atol=1e-13, rtol=0)
-        assert np.allclose(sv, dv[rows], atol=1e-13, rtol=0)
         # row-subset contributions add up to the full backward
         half = np.arange(n) % 2 == 0
-        parts = [orc.kmip_backward_rows(q, k, v, np.nonzero(m)[0], fw["idx"][m], do, scale)
+        parts = [orc.kmip_backward_on_sets(q, k, v, fw["idx"][m], do, scale=scale,
+                                           rows=np.nonzero(m)[0])
                  for m in (half, ~half)]
         assert np.allclose(parts[0][1] + parts[1][1], dk, atol=1e-13, rtol=0)
         assert np.allclose(parts[0][2] + parts[1][2], dv, atol=1e-13, rtol=0)
         assert np.allclose(parts[0][0], dq[half], atol=1e-13, rtol=0)
+        assert np.allclose(parts[1][0], dq[~half], atol=1e-13, rtol=0)
 
 
 def pin_finite_difference(orc, seed=20):

@@ -1,5 +1,6 @@
-"""A captured k-MIP forward + backward replays bit-identically to eager calls,
-with new inputs copied in and eager work in between the replays."""
+"""A captured k-MIP forward + backward (HIP-graph replay) against the fp64
+oracle, and bit-identical to eager calls, with new inputs copied in and eager
+work in between the replays."""
 from __future__ import annotations
 
 import numpy as np
@@ -12,7 +13,9 @@ torch = pytest.importorskip("torch")
 
 from graph_transformer_sparse_amd import kmip  # noqa: E402
 from graph_transformer_sparse_amd.captured import CapturedKmip  # noqa: E402
-from tests.gpu_util import bf16_tensor  # noqa: E402
+import oracle.kmip_oracle as orc  # noqa: E402
+from tests.gpu_util import bf16_tensor, np_  # noqa: E402
+from tests.parity import assert_rows_close, check_selection, decode  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -21,7 +24,8 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("sizes,topk", [([300], 15), ([100, 50, 200], 8), ([400], 32)])
+@pytest.mark.parametrize("sizes,topk", [([300], 15), ([100, 50, 200], 8), ([400], 32),
+                                        ([16400], 15)])
 def test_replays_match_eager(sizes, topk):
     heads, d = 2, 32
     base = with_offsets(f"cap_{len(sizes)}_{topk}", sizes, heads=heads, d=d, topk=topk,
@@ -42,3 +46,12 @@ def test_replays_match_eager(sizes, topk):
         for a, b in ((cap.out, out), (cap.topk_idx, idx), (cap.topk_score, score),
                      (cap.dq, dq), (cap.dk, dk), (cap.dv, dv)):
             assert torch.equal(a, b), r
+        # the replay's own results against the oracle
+        qf, kf, vf = decode(w)
+        ci = np_(cap.topk_idx)
+        check_selection(ci, np_(cap.topk_score), qf, kf, w.offsets, topk, range(w.n))
+        sets = ci.astype(np.int64)
+        assert_rows_close(np_(cap.out), orc.attend_on_sets(qf, kf, vf, sets)["out"], "out")
+        rq, rk, rv = orc.kmip_backward_on_sets(qf, kf, vf, sets, w.dout.astype(np.float64))
+        for name, x, ref in (("dq", cap.dq, rq), ("dk", cap.dk, rk), ("dv", cap.dv, rv)):
+            assert_rows_close(np_(x), ref, name)

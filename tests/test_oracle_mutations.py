@@ -41,12 +41,16 @@ def _select_strict_candidates(s, topk):
 
 
 def _softmax_unnormalised(s, scale):
-    return np.exp(scale * (s - s.max()))
+    s = np.asarray(s, dtype=np.float64)
+    m = s.max(axis=-1, keepdims=True)
+    return np.where(np.isneginf(s), 0.0, np.exp(scale * (s - m)))
 
 
 def _softmax_sign(s, scale):
-    w = np.exp(-scale * (s - s.max()))
-    return w / w.sum()
+    s = np.asarray(s, dtype=np.float64)
+    m = s.max(axis=-1, keepdims=True)
+    w = np.where(np.isneginf(s), 0.0, np.exp(-scale * (s - m)))
+    return w / w.sum(axis=-1, keepdims=True)
 
 
 def _softmax_noscale(s, scale):
@@ -58,26 +62,42 @@ def _ranges_drop_last(offsets, n):
             for lo, hi in _real["ranges"](offsets, n)]
 
 
-def _grads_no_D(q_i, k_sel, v_sel, dout_i, scale):
-    s = k_sel @ q_i
+def _grads_no_D(q_rows, k_sel, v_sel, dout_rows, valid, scale):
+    s = np.where(valid, np.einsum("rkc,rc->rk", k_sel, q_rows), -np.inf)
     p = orc.softmax_selected(s, scale)
-    ds = p * (v_sel @ dout_i)
-    return p, ds, scale * (ds @ k_sel)
+    ds = p * np.where(valid, np.einsum("rkc,rc->rk", v_sel, dout_rows), 0.0)
+    return p, ds, scale * np.einsum("rk,rkc->rc", ds, k_sel)
 
 
-def _grads_wrong_operand(q_i, k_sel, v_sel, dout_i, scale):
-    p, ds, _ = _real["grads"](q_i, k_sel, v_sel, dout_i, scale)
-    return p, ds, scale * (ds @ v_sel)
+def _grads_wrong_operand(q_rows, k_sel, v_sel, dout_rows, valid, scale):
+    p, ds, _ = _real["grads"](q_rows, k_sel, v_sel, dout_rows, valid, scale)
+    return p, ds, scale * np.einsum("rk,rkc->rc", ds, v_sel)
 
 
-def _grads_sign(q_i, k_sel, v_sel, dout_i, scale):
-    p, ds, dq = _real["grads"](q_i, k_sel, v_sel, dout_i, scale)
+def _grads_sign(q_rows, k_sel, v_sel, dout_rows, valid, scale):
+    p, ds, dq = _real["grads"](q_rows, k_sel, v_sel, dout_rows, valid, scale)
     return p, -ds, -dq
 
 
-def _grads_no_scale(q_i, k_sel, v_sel, dout_i, scale):
-    p, ds, dq = _real["grads"](q_i, k_sel, v_sel, dout_i, scale)
+def _grads_no_scale(q_rows, k_sel, v_sel, dout_rows, valid, scale):
+    p, ds, dq = _real["grads"](q_rows, k_sel, v_sel, dout_rows, valid, scale)
     return p, ds, dq / scale
+
+
+def _grads_no_max_shift(q_rows, k_sel, v_sel, dout_rows, valid, scale):
+    # D taken as the plain p . dp without the relative form: same value in
+    # exact arithmetic, cancels on peaked rows
+    s = np.where(valid, np.einsum("rkc,rc->rk", k_sel, q_rows), -np.inf)
+    p = orc.softmax_selected(s, scale)
+    dp = np.where(valid, np.einsum("rkc,rc->rk", v_sel, dout_rows), 0.0)
+    ds = p * (dp - np.einsum("rk,rk->r", p, dp)[:, None])
+    return p, ds, scale * np.einsum("rk,rkc->rc", ds, k_sel)
+
+
+def _grads_dk_transposed(q_rows, k_sel, v_sel, dout_rows, valid, scale):
+    # p and ds of the wrong slot order (reversed within each row)
+    p, ds, dq = _real["grads"](q_rows, k_sel, v_sel, dout_rows, valid, scale)
+    return p, ds[:, ::-1], dq
 
 
 def _scores_reversed_keys(q_rows, k_graph):
@@ -101,6 +121,8 @@ MUTATIONS = {
     "grad_dq_uses_v": ("query_grads", _grads_wrong_operand),
     "grad_sign": ("query_grads", _grads_sign),
     "grad_dq_unscaled": ("query_grads", _grads_no_scale),
+    "grad_cancelling_D": ("query_grads", _grads_no_max_shift),
+    "grad_ds_slot_order": ("query_grads", _grads_dk_transposed),
     "scores_reversed_keys": ("scores_block", _scores_reversed_keys),
     "decode_shift15": ("bf16_bits_to_f64", _decode_shift15),
 }

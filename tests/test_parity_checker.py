@@ -68,3 +68,49 @@ def test_small_case_generator_is_deterministic():
     a = small_case(100, 2, 32, 5, seed=3)
     b = small_case(100, 2, 32, 5, seed=3)
     assert np.array_equal(a.q, b.q) and np.array_equal(a.dout, b.dout)
+
+
+def test_accepts_swap_inside_tie_band():
+    """A set that trades the k-th key for the (k+1)-th when their scores are
+    within the band is accepted and counted as in-band; the same trade with
+    the band closed is rejected."""
+    w, q, k, v, idx, score = _case()
+    idx, score = idx.copy(), score.copy()
+    i, h = 5, 1
+    s = k[0:40, h] @ q[i, h]
+    order = np.lexsort((np.arange(40), -s))
+    kth, nxt = order[8], order[9]
+    k2 = k.copy()
+    k2[nxt, h] = k[kth, h] + 1e-7 * (k[nxt, h] - k[kth, h])   # (k+1)-th just below k-th
+    s2 = k2[0:40, h] @ q[i, h]
+    assert 0 < s2[kth] - s2[nxt] < 1e-5
+    idx[i, h, 8] = nxt
+    score[i, h, 8] = s2[nxt]
+    st = check_selection(idx, score, q, k2, w.offsets, w.topk, [i], heads=[h])
+    assert st["in_band"] == 1
+    with pytest.raises(AssertionError):
+        _closed_band(idx, score, q, k2, w, i, h)
+
+
+def _closed_band(idx, score, q, k, w, i, h):
+    # zero relative band and a per-score error bound scaled to nothing
+    import tests.parity as par
+    saved = par.eps_coef
+    par.eps_coef = lambda d, split=False: 0.0
+    try:
+        par.check_selection(idx, score, q, k, w.offsets, w.topk, [i], heads=[h], band_rel=0.0)
+    finally:
+        par.eps_coef = saved
+
+
+def test_pool_matches_in_process_oracle():
+    """The worker pool runs the same oracle function over row blocks."""
+    from oracle.pool import forward_rows
+    w = with_offsets("pool", [300, 5, 1, 420], heads=3, d=32, topk=7, law="clustered",
+                     clusters=6, seed=8)
+    q, k, v = (orc.bf16_bits_to_f64(x) for x in (w.q, w.k, w.v))
+    rows = np.array([0, 3, 299, 300, 305, 306, 500, 725])
+    a = orc.kmip_forward(q, k, v, w.offsets, w.topk, rows=rows)
+    b = forward_rows(q, k, v, w.offsets, w.topk, rows, workers=2, block=3)
+    for key in ("idx", "score", "out"):
+        assert np.array_equal(a[key], b[key]), key

@@ -1,8 +1,16 @@
 // libkmip C ABI: argument checks, workspace layout and kernel launches.
 // The contract of every entry point is documented in include/kmip.h.
+#include <mutex>
+
 #include "kmip_internal.h"
 
 using namespace kmip;
+
+// Scratch of kmip_forward_no_workspace: one copy per GPU, held until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol); the device address of each
+// GPU's copy comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[KMIP_NO_WORKSPACE_BYTES];
 
 namespace {
 
@@ -166,6 +174,26 @@ kmip_status_t backward_impl(const void* q, const void* k, const void* v, bool f3
   return launch_status(launch_bwd_keys(q, f32, dout, N, H, d, topk, &sc, partials, dk, dv, s));
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+kmip_status_t static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KMIP_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return KMIP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return KMIP_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KMIP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,6 +264,32 @@ kmip_status_t kmip_forward(const void* q, const void* k, const void* v, int64_t 
                        w, s);
   if (st != KMIP_OK) return st;
   return launch_status(launch_gather_av(vb, N, H, d, topk, topk_idx, topk_score, out, s));
+}
+
+kmip_status_t kmip_forward_no_workspace(const void* q, const void* k, const void* v, int64_t N,
+                                        int H, int d, int topk, const int32_t* graph_offsets,
+                                        int num_graphs, float* out, int32_t* topk_idx,
+                                        float* topk_score, kmip_stream_t stream) {
+  if (!q || !k || !v || !out || !topk_idx || !topk_score) return KMIP_ERR_INVALID_VALUE;
+  kmip_status_t st = check_shape(N, H, d, topk, num_graphs);
+  if (st != KMIP_OK) return st;
+  if (num_graphs > 1 && graph_offsets == nullptr) return KMIP_ERR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(topk_idx, 4) || !aligned(topk_score, 4))
+    return KMIP_ERR_INVALID_VALUE;
+  const bool single = single_graph(graph_offsets, num_graphs);
+  if (forward_ws(N, H, topk, single ? 0 : num_graphs) > (size_t)KMIP_NO_WORKSPACE_BYTES)
+    return KMIP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != KMIP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = score_topk_core(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), N, H,
+                       d, topk, graph_offsets, num_graphs, topk_idx, topk_score,
+                       static_cast<char*>(ws), s);
+  if (st != KMIP_OK) return st;
+  return launch_status(launch_gather_av(static_cast<const uint16_t*>(v), N, H, d, topk,
+                                        topk_idx, topk_score, out, s));
 }
 
 kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t N, int H,

@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
     L.kmip_forward_f32.restype = i32
     L.kmip_backward_f32.argtypes = L.kmip_backward.argtypes
     L.kmip_backward_f32.restype = i32
+    L.kmip_forward_no_workspace.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, i32, vp, vp, vp,
+                                            vp]
+    L.kmip_forward_no_workspace.restype = i32
     _lib = L
     return L
 
@@ -66,7 +69,10 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["kmip_status_string", "kmip_version", "kmip_forward_workspace_bytes",
             "kmip_backward_workspace_bytes", "kmip_forward", "kmip_backward",
             "kmip_score_topk", "kmip_gather_softmax_av", "kmip_forward_f32_workspace_bytes",
-            "kmip_forward_f32", "kmip_backward_f32"]
+            "kmip_forward_f32", "kmip_backward_f32", "kmip_forward_no_workspace"]
+
+# Scratch bytes per GPU of kmip_forward_no_workspace (KMIP_NO_WORKSPACE_BYTES).
+NO_WORKSPACE_BYTES = 32 << 20
 
 
 def status_string(status: int) -> str:
@@ -141,6 +147,30 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
             _ptr(topk_score), _ptr(workspace), ws_bytes, _stream(stream))
     if st != KMIP_OK:
         raise KmipError(st, "kmip_forward_f32" if f32 else "kmip_forward")
+    return out, topk_idx, topk_score
+
+
+def forward_no_workspace(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
+                         graph_offsets: Optional[torch.Tensor] = None, *, out=None,
+                         topk_idx=None, topk_score=None, stream=None):
+    """kmip_forward on the library's own per-GPU scratch array (no
+    workspace).  bf16 q, k, v; outputs may be passed in so that nothing is
+    allocated.  Returns (out, topk_idx, topk_score)."""
+    _check_qkv(q, k, v)
+    N, H, d = q.shape
+    go, B = _graphs(graph_offsets)
+    dev = q.device
+    if out is None:
+        out = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((N, H, topk), dtype=torch.int32, device=dev)
+    if topk_score is None:
+        topk_score = torch.empty((N, H, topk), dtype=torch.float32, device=dev)
+    st = lib().kmip_forward_no_workspace(_ptr(q), _ptr(k), _ptr(v), N, H, d, topk, _ptr(go), B,
+                                         _ptr(out), _ptr(topk_idx), _ptr(topk_score),
+                                         _stream(stream))
+    if st != KMIP_OK:
+        raise KmipError(st, "kmip_forward_no_workspace")
     return out, topk_idx, topk_score
 
 

@@ -19,7 +19,9 @@
  *    topk_idx / topk_score are [N][H][topk].
  *  - Ownership: every pointer is device memory owned by the caller.  The
  *    library allocates nothing, keeps no state between calls and is
- *    reentrant; scratch space comes in through `workspace`.
+ *    reentrant; scratch space comes in through `workspace`.  The one
+ *    exception is kmip_forward_no_workspace, whose scratch is a per-GPU
+ *    library array (see its declaration).
  *  - Streams: all work is enqueued on `stream` (a hipStream_t; NULL is the
  *    default stream).  A return of KMIP_OK means the work was enqueued; the
  *    library never synchronises.
@@ -154,6 +156,32 @@ kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t
                             const int32_t* topk_idx, const float* topk_score,
                             const float* dout, float* dq, float* dk, float* dv,
                             void* workspace, size_t workspace_bytes, kmip_stream_t stream);
+
+/*
+ * kmip_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP-graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, results and errors are
+ * those of kmip_forward; the scratch space (the same layout as
+ * kmip_forward's workspace) is a library-owned device array of
+ * KMIP_NO_WORKSPACE_BYTES per GPU, held until the process ends, on the device
+ * current at the call (which must be the stream's device).
+ *
+ *  - Limit: sizes whose kmip_forward_workspace_bytes(...) exceeds
+ *    KMIP_NO_WORKSPACE_BYTES return KMIP_ERR_WORKSPACE before anything is
+ *    enqueued (about 3 * 10^6 (node, head) rows for topk <= 16; lists longer
+ *    than 16 need 2 KB per row, so about 16000 rows).
+ *  - Races: every call on one GPU uses the same scratch array, so calls whose
+ *    work may overlap on that GPU (different streams, other threads) race;
+ *    serialise them.  Calls on one stream are ordered and safe.
+ *  - The first call on a device looks up the array's device address
+ *    (hipGetSymbolAddress); no call allocates or frees memory.
+ */
+#define KMIP_NO_WORKSPACE_BYTES (32u << 20)
+
+kmip_status_t kmip_forward_no_workspace(const void* q, const void* k, const void* v, int64_t N,
+                                        int H, int d, int topk, const int32_t* graph_offsets,
+                                        int num_graphs, float* out, int32_t* topk_idx,
+                                        float* topk_score, kmip_stream_t stream);
 
 /*
  * fp32-input variants.  The page's own k-MIP timings (same page, Tables 15

@@ -125,3 +125,23 @@ def test_f32_workspace_adds_split_rows():
             N, H, d, k, B)
         assert 12 * N * H * d <= extra <= 12 * N * H * d + 512
     assert kmip.forward_f32_workspace_bytes(10, 4, 48, 15, 0) == 0
+
+
+def test_no_workspace_forward_rejects_before_any_gpu_call():
+    """Sizes beyond the static scratch and invalid arguments are refused on
+    the host, before the scratch array's address is looked up."""
+    L = kmip.lib()
+    # lists longer than 16 need 2 KB of candidate arrays per row: 4e5 rows
+    st = L.kmip_forward_no_workspace(FAKE, FAKE, FAKE, 100000, 4, 32, 45, None, 0, FAKE, FAKE,
+                                     FAKE, None)
+    assert st == 3                                     # KMIP_ERR_WORKSPACE
+    st = L.kmip_forward_no_workspace(FAKE, FAKE, FAKE, 4 * 10 ** 6, 4, 32, 15, None, 0, FAKE,
+                                     FAKE, FAKE, None)
+    assert st == 3
+    st = L.kmip_forward_no_workspace(None, FAKE, FAKE, 1000, 4, 32, 15, None, 0, FAKE, FAKE,
+                                     FAKE, None)
+    assert st == 1                                     # KMIP_ERR_INVALID_VALUE
+    st = L.kmip_forward_no_workspace(FAKE, FAKE, FAKE, 1000, 4, 48, 15, None, 0, FAKE, FAKE,
+                                     FAKE, None)
+    assert st == 2                                     # KMIP_ERR_UNSUPPORTED
+    assert kmip.forward_workspace_bytes(500000, 4, 32, 15, 0) <= kmip.NO_WORKSPACE_BYTES

@@ -64,7 +64,16 @@ __global__ void tile_fill_kernel(const int32_t* __restrict__ offsets, int B, int
 // fewer 32-key blocks holding a candidate for any of its queries.  The order
 // only changes which queries share a wavefront; every query's result is
 // independent of it.
+//
+// The groups themselves are placed in the order of a pivot rank: pivots are
+// sorted by their nearest anchor (ORDER_ANCHORS pivots at even spacing, the
+// lowest anchor index on ties), stably by pivot index.  Pivots that point the
+// same way share an anchor, so the groups of one cluster of similar queries
+// sit next to each other in the order, and a window of nearby positions holds
+// most of a query's similar nodes (the threshold window in the scan uses
+// this).
 constexpr int ORDER_PIVOTS = 1024;                // pivots staged in LDS at a time
+constexpr int ORDER_ANCHORS = 64;
 constexpr int ORDER_MAX_PIVOTS = 16384;           // codes are 16-bit
 int order_pivots(int64_t N) {
   const int64_t p = (N / 96) & ~int64_t(31);
@@ -81,8 +90,101 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
   if (i < n) p[i] = 0;
 }
 
-// codes[h*N + i] = nearest pivot of query i of head h, and per-(head, pivot)
-// counts.  Rows hold D bf16 elements; the inner products use the first DP
+// Node id of pivot p of a head: evenly spaced, clamped to the last node.
+__device__ __forceinline__ int64_t pivot_node(int p, int64_t N, int npiv) {
+  const int64_t stride = N / npiv > 0 ? N / npiv : 1;
+  const int64_t r = (int64_t)p * stride;
+  return r < N ? r : N - 1;
+}
+
+// anchor[h*npiv + p] = the anchor (pivot a * (npiv / ORDER_ANCHORS)) with the
+// largest inner product with pivot p, over the first DP elements of the rows
+// (fp32 sums of exact bf16 products, in element order).  One thread per pivot.
+template <int D, int DP>
+__global__ __launch_bounds__(256) void pivot_anchor_kernel(const uint16_t* __restrict__ Q,
+                                                           int64_t N, int H, int npiv,
+                                                           uint8_t* __restrict__ anchor) {
+  __shared__ float av[ORDER_ANCHORS][DP];
+  const int h = blockIdx.y;
+  const int nanch = npiv < ORDER_ANCHORS ? npiv : ORDER_ANCHORS;
+  const int astep = npiv / nanch;
+  for (int t = threadIdx.x; t < nanch * DP; t += blockDim.x) {
+    const int a = t / DP, c = t % DP;
+    const int64_t row = pivot_node(a * astep, N, npiv);
+    av[a][c] = __uint_as_float((uint32_t)Q[(row * H + h) * D + c] << 16);
+  }
+  __syncthreads();
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= npiv) return;
+  const uint16_t* qp = Q + (pivot_node(p, N, npiv) * H + h) * D;
+  float x[DP];
+#pragma unroll
+  for (int c = 0; c < DP; ++c) x[c] = __uint_as_float((uint32_t)qp[c] << 16);
+  float best = -__builtin_inff();
+  int ba = 0;
+  for (int a = 0; a < nanch; ++a) {
+    float sc = 0.f;
+#pragma unroll
+    for (int c = 0; c < DP; ++c) sc = fmaf(x[c], av[a][c], sc);
+    if (sc > best) {
+      best = sc;
+      ba = a;
+    }
+  }
+  anchor[(int64_t)h * npiv + p] = (uint8_t)ba;
+}
+
+// prank[h*npiv + p] = position of pivot p when the head's pivots are sorted by
+// (anchor, pivot index).  One wavefront per head: the anchors are counted
+// (LDS atomics), scanned, and then the pivots are numbered 64 at a time in
+// index order, a pivot's place among equal anchors of its 64 coming from six
+// ballots.
+__global__ __launch_bounds__(64) void pivot_rank_kernel(const uint8_t* __restrict__ anchor,
+                                                        int npiv, int32_t* __restrict__ prank) {
+  __shared__ int32_t cnt[ORDER_ANCHORS];
+  __shared__ int32_t next[ORDER_ANCHORS];
+  static_assert(ORDER_ANCHORS == 64, "one anchor per lane");
+  const int h = blockIdx.x, lane = threadIdx.x;
+  const uint8_t* an = anchor + (int64_t)h * npiv;
+  cnt[lane] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  for (int p = lane; p < npiv; p += 64) atomicAdd(&cnt[an[p]], 1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  int32_t x = cnt[lane], incl = x;                // exclusive scan over the 64 anchors
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  next[lane] = incl - x;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int base = 0; base < npiv; base += 64) {
+    const int p = base + lane;
+    const bool valid = p < npiv;
+    const int g = valid ? an[p] : 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+      const uint64_t bal = __ballot((g >> bit) & 1);
+      peers &= ((g >> bit) & 1) ? bal : ~bal;
+    }
+    const int32_t first = next[g];
+    if (valid) prank[(int64_t)h * npiv + p] = first + __popcll(peers & lt);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    const bool leader = valid && (peers >> lane) == 1ull;   // last lane of its anchor
+    if (leader) next[g] = first + __popcll(peers);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// codes[h*N + i] = rank of the nearest pivot of query i of head h, and
+// per-(head, pivot rank) counts.  Rows hold D bf16 elements; the inner products use the first DP
 // (for split-precision rows, the high parts).  The workgroup stages the
 // head's pivots in LDS, ORDER_PIVOTS at a time, in MFMA operand order
 // (block j*NM + m: pivots [32j, 32j + 32) of the batch, elements
@@ -91,14 +193,14 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
 // npiv is a multiple of 32.
 template <int D, int DP>
 __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
-    const uint16_t* __restrict__ Q, int64_t N, int H, int npiv, uint16_t* __restrict__ codes,
+    const uint16_t* __restrict__ Q, int64_t N, int H, int npiv,
+    const int32_t* __restrict__ prank, uint16_t* __restrict__ codes,
     int32_t* __restrict__ counts) {
   constexpr int NM = DP / 16;
   constexpr int PER_THREAD = ORDER_PIVOTS * DP / 8 / (ORDER_WAVES * 64);
   static_assert(PER_THREAD * ORDER_WAVES * 64 * 8 == ORDER_PIVOTS * DP, "fill covers a batch");
   __shared__ __attribute__((aligned(16))) unsigned char piv[ORDER_PIVOTS * DP * 2];
   const int h = blockIdx.y;
-  const int64_t stride = N / npiv > 0 ? N / npiv : 1;
   const int lane = threadIdx.x & 63, lrow = lane & 31, lhalf = lane >> 5;
   const int64_t i0 = ((int64_t)blockIdx.x * ORDER_WAVES + (threadIdx.x >> 6)) * (32 * ORDER_QB);
   const bool active = i0 < N;                     // uniform per wavefront
@@ -135,8 +237,7 @@ __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
       const int tu = threadIdx.x + u * ORDER_WAVES * 64;
       const int t = tu < pieces ? tu : pieces - 1;   // loads stay in range; stores are skipped
       const int blk = t >> 6, l = t & 63;
-      const int64_t pr = (int64_t)(base + (blk / NM) * 32 + (l & 31)) * stride;
-      const int64_t row = pr < N ? pr : N - 1;
+      const int64_t row = pivot_node(base + (blk / NM) * 32 + (l & 31), N, npiv);
       pv[u] = *reinterpret_cast<const uint4*>(Q + (row * H + h) * D + 16 * (blk % NM) +
                                               8 * (l >> 5));
     }
@@ -187,8 +288,9 @@ __global__ __launch_bounds__(ORDER_WAVES * 64) void pivot_code_kernel(
     if (ob > best[b] || (ob == best[b] && op < bp)) bp = op;
     const int64_t i = i0 + 32 * b + lrow;
     if (lhalf == 0 && i < N) {
-      codes[h * N + i] = (uint16_t)bp;
-      atomicAdd(&counts[((int64_t)h * npiv + bp) * ORDER_COPIES + (i & (ORDER_COPIES - 1))], 1);
+      const int g = prank[(int64_t)h * npiv + bp];
+      codes[h * N + i] = (uint16_t)g;
+      atomicAdd(&counts[((int64_t)h * npiv + g) * ORDER_COPIES + (i & (ORDER_COPIES - 1))], 1);
     }
   }
 }
@@ -229,9 +331,11 @@ hipError_t launch_tile_plan(const int32_t* offsets, int num_graphs, int64_t max_
 }
 
 size_t query_order_bytes(int64_t N, int H) {
-  const int64_t nb = (int64_t)H * order_pivots(N) * ORDER_COPIES;
+  const int64_t np = (int64_t)H * order_pivots(N);
+  const int64_t nb = np * ORDER_COPIES;
   return align256((size_t)N * H * 4) + align256((size_t)N * H * 2) + 2 * align256((size_t)nb * 4) +
-         align256((size_t)scan_aux_elems(nb) * 4);
+         align256((size_t)scan_aux_elems(nb) * 4) + align256((size_t)np) +
+         align256((size_t)np * 4);
 }
 
 hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* ws,
@@ -243,20 +347,39 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
   uint16_t* codes = reinterpret_cast<uint16_t*>(p); p += align256((size_t)N * H * 2);
   int32_t* counts = reinterpret_cast<int32_t*>(p); p += align256((size_t)nb * 4);
   int32_t* cursor = reinterpret_cast<int32_t*>(p); p += align256((size_t)nb * 4);
-  int32_t* aux = reinterpret_cast<int32_t*>(p);
+  int32_t* aux = reinterpret_cast<int32_t*>(p); p += align256((size_t)scan_aux_elems(nb) * 4);
+  uint8_t* anchor = reinterpret_cast<uint8_t*>(p); p += align256((size_t)H * npiv);
+  int32_t* prank = reinterpret_cast<int32_t*>(p);
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, s,
                      counts, nb);
   const dim3 grid((unsigned)ceil_div(N, ORDER_WAVES * 32 * ORDER_QB), (unsigned)H);
   const dim3 block(ORDER_WAVES * 64);
-  void (*code_kernel)(const uint16_t*, int64_t, int, int, uint16_t*, int32_t*);
+  void (*code_kernel)(const uint16_t*, int64_t, int, int, const int32_t*, uint16_t*, int32_t*);
+  void (*anchor_kernel)(const uint16_t*, int64_t, int, int, uint8_t*);
   switch (d) {      // split-precision rows (3d) are grouped by their high parts
-    case 32: code_kernel = pivot_code_kernel<32, 32>; break;
-    case 64: code_kernel = pivot_code_kernel<64, 64>; break;
-    case 96: code_kernel = pivot_code_kernel<96, 32>; break;
-    case 192: code_kernel = pivot_code_kernel<192, 64>; break;
+    case 32:
+      code_kernel = pivot_code_kernel<32, 32>;
+      anchor_kernel = pivot_anchor_kernel<32, 32>;
+      break;
+    case 64:
+      code_kernel = pivot_code_kernel<64, 64>;
+      anchor_kernel = pivot_anchor_kernel<64, 64>;
+      break;
+    case 96:
+      code_kernel = pivot_code_kernel<96, 32>;
+      anchor_kernel = pivot_anchor_kernel<96, 32>;
+      break;
+    case 192:
+      code_kernel = pivot_code_kernel<192, 64>;
+      anchor_kernel = pivot_anchor_kernel<192, 64>;
+      break;
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(code_kernel, grid, block, 0, s, q, N, H, npiv, codes, counts);
+  hipLaunchKernelGGL(anchor_kernel, dim3((unsigned)ceil_div(npiv, 256), (unsigned)H), dim3(256),
+                     0, s, q, N, H, npiv, anchor);
+  hipLaunchKernelGGL(pivot_rank_kernel, dim3((unsigned)H), dim3(ORDER_ANCHORS), 0, s, anchor,
+                     npiv, prank);
+  hipLaunchKernelGGL(code_kernel, grid, block, 0, s, q, N, H, npiv, prank, codes, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Exclusive scan over (head, pivot, copy): head h's positions start at h*N.

@@ -155,6 +155,23 @@ __device__ __forceinline__ float next_down(float x) {
   return __uint_as_float(x > 0.f ? u - 1u : u + 1u);
 }
 
+// Largest of a lane's 16 scores of a 32x32 block, as one max and seven
+// three-input maxima.  The hit path tests quarters with plain compares, so
+// that the compiler shares no partial maxima with it and keeps this tree.
+__device__ __forceinline__ float block_max(const floatx16_t& x) {
+  const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]);
+  const float m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+  const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]);
+  const float m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+  const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+  return fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), x[15]));
+}
+
+// Some score of quarter qq (scores 4qq .. 4qq + 3) exceeds t.
+__device__ __forceinline__ bool quarter_hit(const floatx16_t& x, int qq, float t) {
+  return (x[4 * qq] > t) | (x[4 * qq + 1] > t) | (x[4 * qq + 2] > t) | (x[4 * qq + 3] > t);
+}
+
 struct SubTile {
   int h;
   int64_t q0, q1;     // query rows [q0, q1)
@@ -235,9 +252,14 @@ struct Scanner {
     // nodes and N = 8192 measured 9-15 % faster than at stride 4), SAMPLE up
     // to 2^16 keys (stride 2 at N = 31623 was 5 % slower), 4 * SAMPLE from
     // 2^16 keys on (1-2 % faster than 2 * SAMPLE at N = 10^5 and 5 * 10^5).
+    // With a query order the window pass (window_thresh_kernel) supplies the
+    // tight bound, and this sample only guards inputs without cluster
+    // structure: 8 times sparser (N = 10^5: 3.10 -> 3.02 ms for the whole
+    // selection; dropping it entirely gained no more).
+    const int sparse = perm != nullptr ? 8 : 1;
     const int sample = !(PRE && KP <= 16)       ? SAMPLE
-                       : nkeys >= (int64_t)1 << 16 ? 4 * SAMPLE
-                       : nkeys >= (int64_t)1 << 14 ? SAMPLE
+                       : nkeys >= (int64_t)1 << 16 ? 4 * SAMPLE * sparse
+                       : nkeys >= (int64_t)1 << 14 ? SAMPLE * sparse
                                                    : 1;
     const int nproc = (nchunks + sample - 1) / sample;
 
@@ -432,24 +454,15 @@ struct Scanner {
             }
           }
         } else if constexpr (MODE == M_COLLECT) {
-          float g[QB][4], mx[QB];
-#pragma unroll
-          for (int b = 0; b < QB; ++b) {
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-              g[b][qq] = fmaxf(fmaxf(s[b][4 * qq], s[b][4 * qq + 1]),
-                               fmaxf(s[b][4 * qq + 2], s[b][4 * qq + 3]));
-            mx[b] = fmaxf(fmaxf(g[b][0], g[b][1]), fmaxf(g[b][2], g[b][3]));
-          }
           bool hit = false;
 #pragma unroll
-          for (int b = 0; b < QB; ++b) hit = hit || (mx[b] > thr[b]);
+          for (int b = 0; b < QB; ++b) hit = hit || (block_max(s[b]) > thr[b]);
           if (__ballot(hit) != 0ull) {
 #pragma unroll
             for (int b = 0; b < QB; ++b)
 #pragma unroll
               for (int qq = 0; qq < 4; ++qq) {
-                if (__ballot(g[b][qq] > thr[b]) != 0ull) {
+                if (__ballot(quarter_hit(s[b], qq, thr[b])) != 0ull) {
 #pragma unroll
                   for (int r = 0; r < 4; ++r) {
                     const float sv = s[b][4 * qq + r];
@@ -464,19 +477,15 @@ struct Scanner {
               }
           }
         } else {
-          float g[QB][4], mx[QB];
-#pragma unroll
-          for (int b = 0; b < QB; ++b) {
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-              g[b][qq] = fmaxf(fmaxf(s[b][4 * qq], s[b][4 * qq + 1]),
-                               fmaxf(s[b][4 * qq + 2], s[b][4 * qq + 3]));
-            mx[b] = fmaxf(fmaxf(g[b][0], g[b][1]), fmaxf(g[b][2], g[b][3]));
-          }
           bool hit = false;
 #pragma unroll
-          for (int b = 0; b < QB; ++b) hit = hit || (mx[b] > thr[b]);
+          for (int b = 0; b < QB; ++b) hit = hit || (block_max(s[b]) > thr[b]);
           if (__ballot(hit) != 0ull) {
+            bool g[QB][4];
+#pragma unroll
+            for (int b = 0; b < QB; ++b)
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) g[b][qq] = quarter_hit(s[b], qq, thr[b]);
             // Appends go in halves of two quarters (at most 8 = SCAN_CAP per
             // lane): make room first, so each half has a single drain site.
             // A lane with a hit in a quarter writes all four scores, without
@@ -489,11 +498,11 @@ struct Scanner {
             for (int hf = 0; hf < 2; ++hf) {
               int room = cnt;
 #pragma unroll
-              for (int qq = 2 * hf; qq < 2 * hf + 2; ++qq) room += g[b][qq] > thr[b] ? 4 : 0;
+              for (int qq = 2 * hf; qq < 2 * hf + 2; ++qq) room += g[b][qq] ? 4 : 0;
               if (__ballot(room > SCAN_CAP) != 0ull) drain();
 #pragma unroll
               for (int qq = 2 * hf; qq < 2 * hf + 2; ++qq) {
-                if (g[b][qq] > thr[b]) {
+                if (g[b][qq]) {
 #pragma unroll
                   for (int r = 0; r < 4; ++r) {
                     const float sv = s[b][4 * qq + r];
@@ -791,10 +800,112 @@ __global__ __launch_bounds__(256) void collect_topk_kernel(ScanArgs a) {
   }
 }
 
+// Window bound (one graph, with a query order).  Each workgroup takes WIN_ROWS
+// consecutive positions [q0, q1) of one head's query order and scores its
+// queries against the keys of the positions [q0 - WIN_HALF, q1 + WIN_HALF)
+// (cut to a multiple of 32 keys): the nodes grouped next to them, which for
+// inputs with cluster structure hold most of each query's best keys.  The
+// window's keys are dealt round-robin over its NB 32-key sub-blocks (window
+// key w goes to sub-block w % NB, row w / NB), so every sub-block samples the
+// whole window.  Per lane, the maximum of each sub-block's 16 scores enters a
+// top-k value list; these are scores of distinct keys, so the k-th largest
+// over both lane halves is a lower bound of the query's k-th score, and the
+// row's threshold becomes the larger of it and the sampled bound already
+// there.  Keys are gathered into LDS in MFMA operand order with plain loads,
+// one chunk of sub-blocks at a time.
+constexpr int WIN_WAVES = 8;
+constexpr int WIN_ROWS = WIN_WAVES * 32;
+constexpr int WIN_HALF = 1024;
+constexpr int WIN_CHUNK_BYTES = 32768;
+
+template <int D, int KP>
+__global__ __launch_bounds__(WIN_WAVES * 64) void window_thresh_kernel(ScanArgs a) {
+  constexpr int NM = D / 16;
+  constexpr int TK = WIN_CHUNK_BYTES / (2 * D) / 32 * 32;   // keys per chunk
+  constexpr int SUBT = TK / 32;
+  constexpr int MAXW = WIN_ROWS + 2 * WIN_HALF;
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[SUBT * NM * 1024];
+  __shared__ int32_t ids[MAXW];
+  const int64_t N = a.N;
+  const int H = a.H;
+  const int h = blockIdx.y;
+  const int64_t q0 = (int64_t)blockIdx.x * WIN_ROWS;
+  if (q0 >= N) return;                          // uniform over the workgroup
+  const int64_t q1 = q0 + WIN_ROWS < N ? q0 + WIN_ROWS : N;
+  const int64_t w0 = q0 > WIN_HALF ? q0 - WIN_HALF : 0;
+  const int64_t w1 = q1 + WIN_HALF < N ? q1 + WIN_HALF : N;
+  const int NB = (int)((w1 - w0) / 32);          // sub-blocks; the window is nw = 32 NB keys
+  if (NB == 0) return;
+  const int nw = NB * 32;
+  const int32_t* perm = a.perm + (int64_t)h * N;
+  for (int t = threadIdx.x; t < nw; t += blockDim.x) ids[t] = perm[w0 + t];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const bool wave_active = q0 + wave * 32 < q1;
+  const int64_t pos = q0 + wave * 32 + lrow;
+  const bool qvalid = pos < q1;
+  const int64_t qrow = perm[qvalid ? pos : q1 - 1];
+  bf16x8_t qb[NM];
+  const uint16_t* qp = a.q + (qrow * H + h) * D + 8 * lhalf;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
+  const int nsent = KP - a.topk;
+  float ls[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) ls[i] = i < nsent ? kInf : -kInf;
+  __syncthreads();                              // ids are in LDS
+
+  for (int b0 = 0; b0 < NB; b0 += SUBT) {
+    const int nsb = NB - b0 < SUBT ? NB - b0 : SUBT;
+    // Piece t: lane t % 64 of operand block t / 64 (sub-block b0 + blk / NM,
+    // K-slice blk % NM); row r of sub-block b is window key r * NB + b.
+    for (int t = tid; t < nsb * NM * 64; t += WIN_WAVES * 64) {
+      const int blk = t >> 6, l = t & 63;
+      const int64_t node = ids[(l & 31) * NB + b0 + blk / NM];
+      *reinterpret_cast<uint4*>(kbuf + (size_t)t * 16) = *reinterpret_cast<const uint4*>(
+          a.k + (node * H + h) * D + 16 * (blk % NM) + 8 * (l >> 5));
+    }
+    __syncthreads();
+    if (wave_active) {
+      for (int st = 0; st < nsb; ++st) {
+        floatx16_t acc = {};
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *reinterpret_cast<const bf16x8_t*>(kbuf + (st * NM + m) * 1024 + lane * 16), qb[m],
+              acc, 0, 0, 0);
+        const float mx = block_max(acc);
+        if (mx > ls[KP - 1]) value_insert<KP>(ls, mx);
+      }
+    }
+    __syncthreads();                            // the chunk is read before it is refilled
+  }
+  if (!wave_active) return;
+  float ps[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) ps[i] = __shfl_xor(ls[i], 32);
+#pragma unroll
+  for (int i = 0; i < KP; ++i)
+    if (i >= nsent && ps[i] > ls[KP - 1]) value_insert<KP>(ls, ps[i]);
+  if (qvalid && lhalf == 0) {
+    float* t = a.thr + qrow * H + h;
+    *t = fmaxf(*t, ls[KP - 1]);
+  }
+}
+
 template <int D, int KP>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
   hipError_t e = launch_pass<D, KP, M_THRESH>(a, s);
   if (e != hipSuccess) return e;
+  if (a.perm != nullptr) {
+    hipLaunchKernelGGL((window_thresh_kernel<D, KP>),
+                       dim3((unsigned)ceil_div(a.N, WIN_ROWS), (unsigned)a.H),
+                       dim3(WIN_WAVES * 64), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if constexpr (KP > 16) {
     // Long lists: collect candidates, select from them, then recompute the
     // rows whose candidate arrays overflowed (that pass usually only checks

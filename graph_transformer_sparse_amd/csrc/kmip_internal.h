@@ -25,12 +25,13 @@ constexpr int COLLECT_CAP = 128;                  // candidates per row and lane
 
 // Key-side backward: consecutive sorted (key, pair) positions per slice.
 constexpr int SEG_SLICE = 64;
-// Radix sort: elements per block tile, digit width.
+// Radix sort: elements per block tile; digits of up to 11 bits, so that keys
+// of up to 22 bits (N*H < 4M) sort in two passes.
 constexpr int SORT_THREADS = 256;
-constexpr int SORT_ITEMS = 8;
+constexpr int SORT_ITEMS = 16;
 constexpr int SORT_TILE = SORT_THREADS * SORT_ITEMS;
-constexpr int SORT_BITS = 8;
-constexpr int SORT_BINS = 1 << SORT_BITS;
+constexpr int SORT_MAX_BITS = 11;
+constexpr int SORT_MAX_BINS = 1 << SORT_MAX_BITS;
 // Device-wide exclusive scan tile.
 constexpr int SCAN_THREADS = 256;
 constexpr int SCAN_ITEMS = 16;
@@ -135,8 +136,10 @@ struct SortScratch {
   uint32_t* keys[2];
   uint32_t* vals[2];      // pair ids
   float2* pay[2];         // (p, ds); pay[0] is the caller's pairs array
-  int32_t* hist;          // SORT_BINS * nblocks
-  int32_t* scan_aux;      // block sums of the device-wide scan
+  int32_t* hist;          // [tiles][bins] digit counts, then output offsets
+  int32_t* colsum;        // [row groups][bins] column sums of hist
+  int32_t* binbase;       // [bins + 1] start of each digit in the pass output
+  int32_t* bintot;        // [bins] pairs per digit
   int32_t* key_ptr;       // H*N + 2
   int final_buf;          // which of keys/vals/pay holds the sorted result
 };

@@ -160,65 +160,102 @@ __device__ __forceinline__ double sum16d(double x) {
   return x;
 }
 
-// Reduce-scatter over a 16-lane group: each lane holds 16 partial sums v[u];
-// lane l returns the total of v[l] over the group.  Round o (8, 4, 2, 1)
-// keeps the half of the live values whose index bit matches the lane's bit o
-// and adds the partner's copy of it: 15 shuffles for 16 sums.
-__device__ __forceinline__ double reduce_scatter16(const double (&v)[16], int l16) {
-  double a8[8], a4[4], a2[2];
-  const bool b8 = (l16 & 8) != 0, b4 = (l16 & 4) != 0, b2 = (l16 & 2) != 0,
-             b1 = (l16 & 1) != 0;
+// CPL consecutive row elements as fp32 (bf16 bit patterns or fp32), and
+// the same elements copied as stored.
+template <int CPL>
+__device__ __forceinline__ void load_span(const uint16_t* p, float* x) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    a8[i] = (b8 ? v[i + 8] : v[i]) + __shfl_xor(b8 ? v[i] : v[i + 8], 8, 16);
+  for (int h = 0; h < CPL / 8; ++h) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p + 8 * h);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    a4[i] = (b4 ? a8[i + 4] : a8[i]) + __shfl_xor(b4 ? a8[i] : a8[i + 4], 4, 16);
+    for (int i = 0; i < 4; ++i) {
+      x[8 * h + 2 * i] = __uint_as_float(u[i] << 16);
+      x[8 * h + 2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+}
+template <int CPL>
+__device__ __forceinline__ void load_span(const float* p, float* x) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    a2[i] = (b2 ? a4[i + 2] : a4[i]) + __shfl_xor(b2 ? a4[i] : a4[i + 2], 2, 16);
-  return (b1 ? a2[1] : a2[0]) + __shfl_xor(b1 ? a2[0] : a2[1], 1, 16);
+  for (int h = 0; h < CPL / 4; ++h) {
+    const float4 w = *reinterpret_cast<const float4*>(p + 4 * h);
+    x[4 * h] = w.x;
+    x[4 * h + 1] = w.y;
+    x[4 * h + 2] = w.z;
+    x[4 * h + 3] = w.w;
+  }
+}
+template <int CPL>
+__device__ __forceinline__ void store_span(uint16_t* p, const float* x) {
+#pragma unroll
+  for (int h = 0; h < CPL / 8; ++h) {
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = (__float_as_uint(x[8 * h + 2 * i]) >> 16) |
+             (__float_as_uint(x[8 * h + 2 * i + 1]) & 0xffff0000u);
+    *reinterpret_cast<uint4*>(p + 8 * h) = make_uint4(u[0], u[1], u[2], u[3]);
+  }
+}
+template <int CPL>
+__device__ __forceinline__ void store_span(float* p, const float* x) {
+#pragma unroll
+  for (int h = 0; h < CPL / 4; ++h)
+    *reinterpret_cast<float4*>(p + 4 * h) = make_float4(x[4 * h], x[4 * h + 1], x[4 * h + 2],
+                                                        x[4 * h + 3]);
 }
 
+// A query row is handled by 16 lanes.  Pass 1 takes the row's keys 16 at a
+// time in four steps of four: in step p, lane l works on slot p*4 + (l & 3)
+// and on the column quarter l >> 2, so the four lanes of a key read its K
+// and V rows as one coalesced segment, each forming fp64 partial dot
+// products over d/4 columns; two butterfly steps add the quarters, and lane
+// l keeps the sums of step l >> 2, which are those of slot l.  Pass 2 gives
+// each lane d/16 columns of dq = sum_t ds_t k_t; the ds_t and the first
+// chunk's K rows reach it through LDS (later chunks' K rows are read again).
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_query_kernel(
     const T* __restrict__ Q, const T* __restrict__ Kt, const T* __restrict__ V, int64_t NH,
     int H, int topk, const int32_t* __restrict__ idx, const float* __restrict__ dout,
     float* __restrict__ dq, float2* __restrict__ pairs) {
-  constexpr int EPL = D / 16;
-  const int l16 = threadIdx.x & 15;
-  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 4);
-  if (row >= NH) return;
+  constexpr int EPL = D / 16;        // pass 2: columns per lane
+  constexpr int CPL = D / 4;         // pass 1: columns per lane (one quarter)
+  // First chunk's K rows, [group][slot][D] (+ padding so that the four
+  // groups of a wave start on different banks), ds and key of every slot.
+  constexpr int KROW = 16 * D + 64 / (int)sizeof(T);
+  __shared__ T klds[ROWS_PER_BLOCK * KROW];
+  __shared__ double dsl[ROWS_PER_BLOCK][MAXK];
+  __shared__ int32_t jl[ROWS_PER_BLOCK][MAXK];
+  const int l16 = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + grp;
+  if (row >= NH) return;                // whole 16-lane groups; no block barriers below
   const int h = (int)(row % H);
+  const int64_t self = row / H;
   const int32_t* ir = idx + row * topk;
+  const int qt = l16 >> 2, ks = l16 & 3;
+  T* kg = klds + grp * KROW;
 
-  int jv[MAXK / 16];
+  // This lane's quarter of q and dO, widened once.
+  float qf[CPL], gf[CPL];
+  load_span<CPL>(Q + row * D + qt * CPL, qf);
+  load_span<CPL>(dout + row * D + qt * CPL, gf);
+  double qd[CPL], gd[CPL];
 #pragma unroll
-  for (int c = 0; c < MAXK / 16; ++c) {
-    const int t = c * 16 + l16;
-    jv[c] = t < topk ? ir[t] : -1;
+  for (int e = 0; e < CPL; ++e) {
+    qd[e] = (double)qf[e];
+    gd[e] = (double)gf[e];
   }
-  float g[EPL], qx[EPL];
-  load_cols<EPL>(dout + row * D + l16 * EPL, g);
-  load_cols<EPL>(Q + row * D + l16 * EPL, qx);
 
-  // Pass 1: weights w_t and dp_t; lane (t % 16) keeps entry t.  The 16 K
-  // and V rows of a chunk are requested together (unused slots read the
-  // query's own row and count zero), and their partial dot products with q
-  // and dO are reduced in butterflies that leave entry t's score and dp in
-  // lane t % 16.  The scores are recomputed here in fp64 from the input
-  // rows (exact products), not taken from the forward's fp32 scores: where
-  // the gradient is a cancelling sum of small softmax terms, the fp32
+  // Pass 1.  The scores are recomputed here in fp64 from the input rows
+  // (exact products), not taken from the forward's fp32 scores: where the
+  // gradient is a cancelling sum of small softmax terms, the fp32
   // accumulation error of the scores (a few ulps) would be amplified.
   // dp_t - D is evaluated as (dp_t - dp_0) - sum_u p_u (dp_u - dp_0), with
   // entry 0 the best score (the largest weight): the same value, without the
   // cancellation that loses the small terms of sum_u p_u dp_u when the
-  // softmax is nearly one-hot.
-  const int64_t self = row / H;
-  // The first chunk's K rows (this lane's columns) are kept in LDS for pass
-  // 2, lane-major so that the accesses are conflict-free.
-  __shared__ float kl[16 * EPL * 256];
-  float* kmine = kl + threadIdx.x;
+  // softmax is nearly one-hot.  Unused slots read the query's own row and
+  // count zero.
   double wv[MAXK / 16], dpv[MAXK / 16];
   double zl = 0.0, dl = 0.0;    // this lane's share of Z and sum w (dp - dp_0)
   double dp0 = 0.0, m = 0.0;    // entry 0's dp and score (the forward's best)
@@ -227,34 +264,40 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
     wv[c] = 0.0;
     dpv[c] = 0.0;
     if (c * 16 < topk) {
-      double part[16], spart[16];
+      double sc = 0.0, dp = 0.0;
+      int32_t jmine = -1;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int j = __shfl(jv[c], u, 16);
-        const int64_t jr = ((j >= 0 ? (int64_t)j : self) * H + h) * D + l16 * EPL;
-        float x[EPL], y[EPL];
-        load_cols<EPL>(V + jr, x);
-        load_cols<EPL>(Kt + jr, y);
-        double pp = 0.0, ss = 0.0;
+      for (int p = 0; p < 4; ++p) {
+        const int t = c * 16 + p * 4 + ks;
+        const int32_t jraw = ir[t < topk ? t : topk - 1];
+        const int32_t j = t < topk ? jraw : -1;
+        const int64_t jr = ((j >= 0 ? (int64_t)j : self) * H + h) * D + qt * CPL;
+        float kx[CPL], vx[CPL];
+        load_span<CPL>(Kt + jr, kx);
+        load_span<CPL>(V + jr, vx);
+        if (c == 0) store_span<CPL>(kg + (p * 4 + ks) * D + qt * CPL, kx);
+        double s = 0.0, g = 0.0;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          pp = fma((double)g[e], (double)x[e], pp);
-          ss = fma((double)qx[e], (double)y[e], ss);
+        for (int e = 0; e < CPL; ++e) {
+          s = fma(qd[e], (double)kx[e], s);
+          g = fma(gd[e], (double)vx[e], g);
         }
-        part[u] = j >= 0 ? pp : 0.0;
-        spart[u] = j >= 0 ? ss : 0.0;
-        if (c == 0) {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) kmine[(u * EPL + e) * 256] = y[e];
+        s += __shfl_xor(s, 4, 16);
+        g += __shfl_xor(g, 4, 16);
+        s += __shfl_xor(s, 8, 16);
+        g += __shfl_xor(g, 8, 16);
+        if (p == qt) {                  // slot p*4 + ks == c*16 + l16
+          sc = s;
+          dp = g;
+          jmine = j;
         }
       }
-      const double dp = reduce_scatter16(part, l16);
-      const double sc = reduce_scatter16(spart, l16);
+      jl[grp][c * 16 + l16] = jmine;
       if (c == 0) {
         dp0 = __shfl(dp, 0, 16);
         m = __shfl(sc, 0, 16);
       }
-      const bool live = jv[c] >= 0;        // slot c*16 + l16 holds a key
+      const bool live = jmine >= 0;
       // fp64 exp: weights far below the best (e^-87 and less) stay normal
       // numbers instead of underflowing in fp32.
       const double w = live ? exp(sc - m) : 0.0;
@@ -267,10 +310,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   const double inv = 1.0 / sum16d(zl);
   const double Dm = sum16d(dl) * inv;
 
-  // Pass 2: ds_t and dq = sum ds_t k_t.
-  double acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
+  // Pass 2: ds_t, then dq = sum ds_t k_t over this lane's columns.
 #pragma unroll
   for (int c = 0; c < MAXK / 16; ++c) {
     if (c * 16 < topk) {
@@ -278,15 +318,24 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
       const double p = wv[c] * inv;
       const double ds = p * (dpv[c] - Dm);
       if (t < topk) pairs[row * topk + t] = make_float2((float)p, (float)ds);
+      dsl[grp][t] = ds;                    // 0 on unused slots
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  double acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
+#pragma unroll
+  for (int c = 0; c < MAXK / 16; ++c) {
+    if (c * 16 < topk) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int j = __shfl(jv[c], u, 16);
-        const double dsu = __shfl(ds, u, 16);   // 0 on unused slots
+        const double dsu = dsl[grp][c * 16 + u];
         float x[EPL];
         if (c == 0) {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) x[e] = kmine[(u * EPL + e) * 256];
+          load_cols<EPL>(kg + u * D + l16 * EPL, x);
         } else {
+          const int32_t j = jl[grp][c * 16 + u];
           load_cols<EPL>(Kt + ((j >= 0 ? (int64_t)j : self) * H + h) * D + l16 * EPL, x);
         }
 #pragma unroll

@@ -569,8 +569,12 @@ __global__ __launch_bounds__(256) void segreduce_kernel(
   flush(cur, run0, s1);
 }
 
-// One 16-lane group per key: zeros for unselected keys, and the in-order sum
-// of slice partials for keys whose segment crosses a slice boundary.
+// One 16-lane group per SEGFIX_KEYS consecutive keys: zeros for unselected
+// keys, and the in-order sum of slice partials for keys whose segment
+// crosses a slice boundary (keys inside one slice were written by
+// segreduce_kernel).  The group reads the keys' segment pointers with one
+// load and takes them by shuffles.
+constexpr int SEGFIX_KEYS = 8;
 template <int D>
 __global__ __launch_bounds__(256) void segfix_kernel(const int32_t* __restrict__ key_ptr,
                                                      int64_t N, int H,
@@ -579,35 +583,43 @@ __global__ __launch_bounds__(256) void segfix_kernel(const int32_t* __restrict__
                                                      float* __restrict__ dv) {
   constexpr int EPL = D / 16;
   const int l16 = threadIdx.x & 15;
-  const int64_t key = (int64_t)blockIdx.x * SEG_GROUPS + (threadIdx.x >> 4);
   const int64_t HN = N * H;
-  if (key >= HN) return;
-  const int64_t a = key_ptr[key], b = key_ptr[key + 1];
-  const int64_t orow = (key % N) * H + key / N;
-  double ak[EPL], av[EPL];
+  const int64_t key0 = ((int64_t)blockIdx.x * SEG_GROUPS + (threadIdx.x >> 4)) * SEGFIX_KEYS;
+  if (key0 >= HN) return;
+  // key_ptr has H*N + 2 entries; lanes past the end re-read the last one
+  const int64_t pk = key0 + l16 <= HN + 1 ? key0 + l16 : HN + 1;
+  const int32_t kp = key_ptr[pk];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) ak[e] = av[e] = 0.0;
-  if (a < b) {
+  for (int i = 0; i < SEGFIX_KEYS; ++i) {
+    const int64_t key = key0 + i;
+    if (key >= HN) break;
+    const int64_t a = __shfl(kp, i, 16), b = __shfl(kp, i + 1, 16);
     const int64_t sa = a / SEG_SLICE, sb = (b - 1) / SEG_SLICE;
-    if (sa == sb) return;                       // written by segreduce_kernel
-    for (int64_t s = sa; s <= sb; ++s) {
-      const int slot = (s == sa && a != sa * SEG_SLICE) ? 1 : 0;
-      const double* src = partials + ((s * 2 + slot) * 2) * D + l16 * EPL;
+    if (a < b && sa == sb) continue;          // written by segreduce_kernel
+    const int64_t orow = (key % N) * H + key / N;
+    double ak[EPL], av[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        ak[e] += src[e];
-        av[e] += src[D + e];
+    for (int e = 0; e < EPL; ++e) ak[e] = av[e] = 0.0;
+    if (a < b) {
+      for (int64_t s = sa; s <= sb; ++s) {
+        const int slot = (s == sa && a != sa * SEG_SLICE) ? 1 : 0;
+        const double* src = partials + ((s * 2 + slot) * 2) * D + l16 * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          ak[e] += src[e];
+          av[e] += src[D + e];
+        }
       }
     }
-  }
-  float fk[EPL], fv[EPL];
+    float fk[EPL], fv[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    fk[e] = (float)ak[e];
-    fv[e] = (float)av[e];
+    for (int e = 0; e < EPL; ++e) {
+      fk[e] = (float)ak[e];
+      fv[e] = (float)av[e];
+    }
+    store_cols<EPL>(dk + orow * D + l16 * EPL, fk);
+    store_cols<EPL>(dv + orow * D + l16 * EPL, fv);
   }
-  store_cols<EPL>(dk + orow * D + l16 * EPL, fk);
-  store_cols<EPL>(dv + orow * D + l16 * EPL, fv);
 }
 
 // key_ptr[key] = first position of the sorted keys that is >= key, for key
@@ -764,7 +776,7 @@ void launch_keys_t(const QT* q, const float* dout, int64_t N, int H, int topk,
   const int64_t HN = N * H;
   const int64_t nslices = ceil_div(P, SEG_SLICE);
   const unsigned b1 = (unsigned)(8 * ceil_div(ceil_div(nslices, SEG_GROUPS), 8));
-  const unsigned b2 = (unsigned)ceil_div(HN, SEG_GROUPS);
+  const unsigned b2 = (unsigned)ceil_div(HN, SEG_GROUPS * SEGFIX_KEYS);
   hipLaunchKernelGGL((segreduce_kernel<D, QT>), dim3(b1), dim3(256), 0, s, q, dout,
                      sc->pay[sc->final_buf], sc->keys[sc->final_buf], sc->vals[sc->final_buf],
                      sc->key_ptr, N, H, topk, nslices, partials, dk, dv);

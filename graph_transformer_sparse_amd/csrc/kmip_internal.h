@@ -24,7 +24,7 @@ constexpr int SCAN_CHUNKS = 32;                   // threshold pass: key ranges 
 constexpr int COLLECT_CAP = 128;                  // candidates per row and lane half
 
 // Key-side backward: consecutive sorted (key, pair) positions per slice.
-constexpr int SEG_SLICE = 64;
+constexpr int SEG_SLICE = 128;
 // Radix sort: elements per block tile; digits of up to 11 bits, so that keys
 // of up to 22 bits (N*H < 4M) sort in two passes.
 constexpr int SORT_THREADS = 256;

@@ -84,6 +84,15 @@ def test_f32_query_order_path(n, heads, d):
     assert st["rows"] == 600 * heads
 
 
+def test_f32_batched_clustered_all_rows():
+    """Batched graphs of a few thousand nodes, four heads, fp32 inputs
+    (split-precision rows of width 96); every row, forward and backward."""
+    w = with_offsets("f32_clustered_batch", [3000, 2500, 1, 3500], heads=4, d=32, topk=15,
+                     law="clustered", clusters=40, seed=77, dtype="f32")
+    t, out, idx, score, st = _forward_check(w)
+    _backward_check(w, t, idx, score)
+
+
 def test_f32_exact_ties_follow_ascending_id():
     from tests.gpu_util import np_, run_forward
     w = small_case(256, 2, 32, 6, seed=31, dtype="f32")

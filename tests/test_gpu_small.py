@@ -134,6 +134,21 @@ def test_ragged_graphs(sizes, topk):
     _backward_check(w, t, idx, score)
 
 
+@pytest.mark.parametrize("sizes,heads,d,topk", [
+    ([3000, 1, 257, 4100, 0, 900, 2600], 4, 32, 15),
+    ([2500, 5000, 900], 4, 64, 8),
+    ([3000, 2200, 4000], 4, 32, 45),
+])
+def test_batched_clustered_all_rows(sizes, heads, d, topk):
+    """Batched graphs of up to 5000 nodes, four heads, clustered rows (many
+    sub-tiles per graph, partial last tiles, empty and one-node graphs),
+    d = 32 and 64, short and long lists.  Every row, forward and backward."""
+    w = with_offsets(f"clustered_batch_{len(sizes)}_{topk}", sizes, heads=heads, d=d,
+                     topk=topk, law="clustered", clusters=48, seed=sum(sizes) + d + topk)
+    t, out, idx, score, st = _forward_check(w)
+    _backward_check(w, t, idx, score)
+
+
 def test_single_node_graph_is_identity():
     from tests.gpu_util import np_, run_backward, run_forward
     w = with_offsets("singletons", [1, 1, 1, 1, 1], heads=2, d=64, topk=4, seed=9)

@@ -87,6 +87,9 @@ struct ScanArgs {
   uint2* cand;
   int32_t* cand_cnt;
   int cap;
+  // Selection pass: first rank it computes (0, or 16, 32, ... in the passes
+  // that recompute rows with overflowing candidate arrays).
+  int rank0;
 };
 hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s);
 // Per row width (bf16 elements; 96 and 192 are split-precision rows of 32

@@ -24,11 +24,14 @@
 //    ascending key order.
 //  * Two passes.  The threshold pass scores a sample of the chunks (with
 //    lists of at most 16: every chunk below 2^14 keys, every fourth up to
-//    2^16 keys, every sixteenth beyond; every second for longer lists) and
-//    keeps, per lane and query, the top-k of the maxima of SCAN_CHUNKS
-//    consecutive ranges of those keys (uniform, lockstep insertions).  These
-//    maxima are scores of distinct keys, so the k-th largest over both halves
-//    is a lower bound T of the query's k-th score.
+//    2^16 keys, every sixteenth beyond, and eight times sparser still when
+//    the queries are grouped; every second for longer lists) and keeps, per
+//    lane and query, the top-k of the maxima of SCAN_CHUNKS consecutive
+//    ranges of those keys (uniform, lockstep insertions).  These maxima are
+//    scores of distinct keys, so the k-th largest over both halves is a lower
+//    bound T of the query's k-th score.  With grouped queries a window pass
+//    (window_thresh_kernel) raises T with the exact k-th score over the keys
+//    of nearby positions in the query order.
 //    The selection pass then runs the exact running top-k seeded with
 //    next_down(T): a block of scores is rejected with a max tree and one
 //    compare, rare hits go to a per-lane LDS candidate buffer, and buffers
@@ -37,7 +40,8 @@
 //    (score descending, id ascending).  Lists longer than 16 collect their
 //    candidates in per-row arrays instead (COLLECT below).
 //  * One graph: each head's queries are first grouped by their nearest of
-//    1024 pivot queries (largest inner product), so a wavefront's 32 queries
+//    about N/96 pivot queries (largest inner product), the groups placed in
+//    the order of their pivots' nearest anchor, so a wavefront's 32 queries
 //    tend to share their candidate keys.  A persistent grid of exactly the co-resident
 //    workgroups, each taking an equal contiguous range of query blocks (no
 //    partial last round), with logical ids permuted so that the workgroups of
@@ -117,27 +121,17 @@ struct ScanShape {
 // (ls[t], ls[t-1], s): one v_med3 per slot; ids follow the compares.
 template <int KP>
 __device__ __forceinline__ void list_insert(float (&ls)[KP], int (&lj)[KP], float s, int j) {
+  static_assert(KP <= 16, "register lists of the selection pass");
   bool b[KP];
 #pragma unroll
   for (int t = 0; t < KP; ++t) b[t] = s > ls[t];
-  if constexpr (KP <= 16) {
 #pragma unroll
-    for (int t = KP - 1; t >= 1; --t) {
-      lj[t] = b[t] ? (b[t - 1] ? lj[t - 1] : j) : lj[t];
-      ls[t] = __builtin_amdgcn_fmed3f(ls[t], ls[t - 1], s);
-    }
-    lj[0] = b[0] ? j : lj[0];
-    ls[0] = fmaxf(ls[0], s);
-  } else {
-    // Long lists live partly in scratch; this form keeps their spills small.
-#pragma unroll
-    for (int t = KP - 1; t >= 1; --t) {
-      ls[t] = b[t - 1] ? ls[t - 1] : (b[t] ? s : ls[t]);
-      lj[t] = b[t - 1] ? lj[t - 1] : (b[t] ? j : lj[t]);
-    }
-    ls[0] = b[0] ? s : ls[0];
-    lj[0] = b[0] ? j : lj[0];
+  for (int t = KP - 1; t >= 1; --t) {
+    lj[t] = b[t] ? (b[t - 1] ? lj[t - 1] : j) : lj[t];
+    ls[t] = __builtin_amdgcn_fmed3f(ls[t], ls[t - 1], s);
   }
+  lj[0] = b[0] ? j : lj[0];
+  ls[0] = fmaxf(ls[0], s);
 }
 
 template <int KP>
@@ -289,7 +283,7 @@ struct Scanner {
     bool wave_rows = bact[0];
 #pragma unroll
     for (int b = 0; b < QB; ++b) keep[b] = qvalid[b];
-    if constexpr (MODE == M_SELECT && KP > 16) {
+    if constexpr (MODE == M_SELECT) {
       if (a.cand_cnt != nullptr) {
         const int64_t r = qrow[0] * H + t.h;
         keep[0] = qvalid[0] && (a.cand_cnt[2 * r] > a.cap || a.cand_cnt[2 * r + 1] > a.cap);
@@ -309,9 +303,26 @@ struct Scanner {
     const bool wave_active = wave_rows;
     const int aoff = lane * 16;
 
-    // Lists: slots [0, KP-topk) hold +inf sentinels that nothing displaces, so
-    // the live top-k occupies the tail and its k-th score is ls[.][KP-1].
-    const int nsent = KP - topk;
+    // This call computes ranks [rank0, rank0 + kk) of each row: all of them
+    // (rank0 = 0, kk = topk) except in the rank passes that recompute rows
+    // with overflowing candidate arrays for lists longer than 16, 16 ranks
+    // at a time.  A rank pass keeps only keys ordered after the row's entry
+    // rank0 - 1 (score descending, id ascending), written by the pass before.
+    const int rank0 = MODE == M_SELECT ? a.rank0 : 0;
+    const int kk = topk - rank0 < KP ? topk - rank0 : KP;
+    float ubs = kInf;
+    int ubj = -1;
+    if constexpr (MODE == M_SELECT) {
+      if (rank0 > 0 && keep[0]) {
+        const int64_t r = (qrow[0] * H + t.h) * topk + rank0 - 1;
+        ubs = out_score[r];
+        ubj = out_idx[r];
+        if (ubj < 0) ubs = -kInf;           // the row has no keys past rank0 - 1
+      }
+    }
+    // Lists: slots [0, KP-kk) hold +inf sentinels that nothing displaces, so
+    // the live top-kk occupies the tail and its kk-th score is ls[.][KP-1].
+    const int nsent = KP - kk;
     float ls[QB][KP];
     int lj[QB][KP];
 #pragma unroll
@@ -369,9 +380,11 @@ struct Scanner {
           const int tag = (int)(e.y >> 31);
 #pragma unroll
           for (int b = 0; b < QB; ++b) {
-            if (tag == b && sv > thr[b]) {
-              list_insert<KP>(ls[b], lj[b], sv, key);
-              thr[b] = fmaxf(thr[b], ls[b][KP - 1]);
+            if constexpr (MODE == M_SELECT) {
+              if (tag == b && sv > thr[b] && (sv < ubs || (sv == ubs && key > ubj))) {
+                list_insert<KP>(ls[b], lj[b], sv, key);
+                thr[b] = fmaxf(thr[b], ls[b][KP - 1]);
+              }
             }
           }
         }
@@ -548,95 +561,56 @@ struct Scanner {
     } else {
       drain();
       const bool lower = lhalf == 0;
-      if constexpr (KP <= 16) {
-        static_assert(QB == 1 && SCAN_CAP * 64 >= 32 * 16, "32 rows of 16 entries per region");
-        // Two-pointer merge of the half-lists of each query (lanes l, l ^ 32)
-        // under (score descending, id ascending): the upper lane publishes its
-        // live entries, best first, in the drained candidate buffer; the lower
-        // lane walks them beside its own list and writes the top-k in order.
-        // Only padding entries (-inf, -1) can tie exactly; the lower lane's
-        // go first.
-        uint2* wl = cbuf + wave * CBW;
-        if (!lower) {
+      static_assert(KP <= 16 && QB == 1 && SCAN_CAP * 64 >= 32 * 16,
+                    "register lists; 32 rows of 16 entries per region");
+      // Two-pointer merge of the half-lists of each query (lanes l, l ^ 32)
+      // under (score descending, id ascending): the upper lane publishes its
+      // live entries, best first, in the drained candidate buffer; the lower
+      // lane walks them beside its own list and writes the top-kk in order,
+      // at ranks rank0, rank0 + 1, ...  Only padding entries (-inf, -1) can
+      // tie exactly; the lower lane's go first.
+      uint2* wl = cbuf + wave * CBW;
+      if (!lower) {
 #pragma unroll
-          for (int i = 0; i < KP; ++i)
-            if (i >= nsent)
-              wl[lrow * 16 + (i - nsent)] =
-                  make_uint2(__float_as_uint(ls[0][i]), (unsigned)lj[0][i]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lower && keep[0]) {
-          int32_t* oi = out_idx + (qrow[0] * H + t.h) * topk;
-          float* os = out_score + (qrow[0] * H + t.h) * topk;
-          const uint2* pl = wl + lrow * 16;
-          int u = 0, r = 0;
-          uint2 pu = pl[0];
-          auto emit = [&](float sv, int j) __attribute__((always_inline)) {
-            const float sc = j < 0 ? -kInf : sv;
-            oi[r] = j;
-            os[r] = sc;
-            ++r;
-          };
+        for (int i = 0; i < KP; ++i)
+          if (i >= nsent)
+            wl[lrow * 16 + (i - nsent)] =
+                make_uint2(__float_as_uint(ls[0][i]), (unsigned)lj[0][i]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lower && keep[0]) {
+        int32_t* oi = out_idx + (qrow[0] * H + t.h) * topk + rank0;
+        float* os = out_score + (qrow[0] * H + t.h) * topk + rank0;
+        const uint2* pl = wl + lrow * 16;
+        int u = 0, r = 0;
+        uint2 pu = pl[0];
+        auto emit = [&](float sv, int j) __attribute__((always_inline)) {
+          const float sc = j < 0 ? -kInf : sv;
+          oi[r] = j;
+          os[r] = sc;
+          ++r;
+        };
 #pragma unroll
-          for (int i = 0; i < KP; ++i) {
-            if (i >= nsent) {
-              const float sv = ls[0][i];
-              const int j = lj[0][i];
-              while (r < topk && u < topk &&
-                     (__uint_as_float(pu.x) > sv ||
-                      (__uint_as_float(pu.x) == sv && (int)pu.y < j))) {
-                emit(__uint_as_float(pu.x), (int)pu.y);
-                ++u;
-                pu = pl[u < 16 ? u : 15];
-              }
-              if (r < topk) emit(sv, j);
+        for (int i = 0; i < KP; ++i) {
+          if (i >= nsent) {
+            const float sv = ls[0][i];
+            const int j = lj[0][i];
+            while (r < kk && u < kk &&
+                   (__uint_as_float(pu.x) > sv ||
+                    (__uint_as_float(pu.x) == sv && (int)pu.y < j))) {
+              emit(__uint_as_float(pu.x), (int)pu.y);
+              ++u;
+              pu = pl[u < 16 ? u : 15];
             }
-          }
-          while (r < topk) {                  // r < topk implies u < topk
-            emit(__uint_as_float(pu.x), (int)pu.y);
-            ++u;
-            pu = pl[u < 16 ? u : 15];
+            if (r < kk) emit(sv, j);
           }
         }
-      } else {
-        // Merge the two half-lists of each query by rank: live entry i of my
-        // list (slots [nsent, KP)) lands at (i - nsent) + the number of partner
-        // live entries ordered before it.  Lower-half lanes win exact (score,
-        // id) ties, which only padding entries (-inf, -1) can produce.
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-          float ps[KP];
-          int pj[KP];
-#pragma unroll
-          for (int i = 0; i < KP; ++i) {
-            ps[i] = __shfl_xor(ls[b][i], 32);
-            pj[i] = __shfl_xor(lj[b][i], 32);
-          }
-          if (keep[b]) {
-            int32_t* oi = out_idx + (qrow[b] * H + t.h) * topk;
-            float* os = out_score + (qrow[b] * H + t.h) * topk;
-#pragma unroll
-            for (int i = 0; i < KP; ++i) {
-              if (i >= nsent) {
-                int rank = i - nsent;
-#pragma unroll
-                for (int u = 0; u < KP; ++u) {
-                  const bool before =
-                      u >= nsent && (ps[u] > ls[b][i] ||
-                                     (ps[u] == ls[b][i] && (lower ? pj[u] < lj[b][i]
-                                                                  : pj[u] <= lj[b][i])));
-                  rank += before ? 1 : 0;
-                }
-                if (rank < topk) {
-                  const float sc = lj[b][i] < 0 ? -kInf : ls[b][i];
-                  oi[rank] = lj[b][i];
-                  os[rank] = sc;
-                }
-              }
-            }
-          }
+        while (r < kk) {                      // r < kk implies u < kk
+          emit(__uint_as_float(pu.x), (int)pu.y);
+          ++u;
+          pu = pl[u < 16 ? u : 15];
         }
       }
     }
@@ -916,7 +890,16 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
                        dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_pass<D, KP, M_SELECT>(a, s);
+    // Rows whose arrays overflowed: exact selection with 16-entry register
+    // lists, 16 ranks per pass, each pass keeping the keys ordered after the
+    // previous pass's last entry.
+    for (int r0 = 0; r0 < a.topk; r0 += 16) {
+      ScanArgs b = a;
+      b.rank0 = r0;
+      e = launch_pass<D, 16, M_SELECT>(b, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   } else {
     ScanArgs b = a;
     b.cand_cnt = nullptr;                      // SELECT writes every row

@@ -11,12 +11,15 @@ re-derives, from the formulas the kernel uses, every index it forms:
   the per-row candidate arrays and counts (collecting pass), and the output
   slots.
 
-and checks each against the size of what it indexes.  The first case is
-the launch shape of a GPU memory fault recorded while an uncommitted
-key-window threshold variant was in the tree: the long-list selection pass
-`score_topk_kernel<32, 45, 1, 8>` at N = 10^5, H = 4 with 256 workgroups of
-512 threads and 64 KB of LDS.  With the committed formulas every access of
-that launch stays inside its buffer.  CPU only.
+and checks each against the size of what it indexes.  Two GPU memory
+faults were recorded in a former long-list selection pass,
+`score_topk_kernel<32, 45, 1, 8>` (45-entry lists partly in scratch) at
+N = 10^5, H = 4 with 256 workgroups of 512 threads and 64 KB of LDS, both
+times with many rows whose candidate arrays had overflowed.  The first case
+below re-derives that launch: every index it forms stays inside its buffer,
+so the cause was not found in the address arithmetic.  That kernel is no
+longer built; overflowing rows are now recomputed by rank passes of the
+16-entry selection kernel, whose launches are checked too.  CPU only.
 """
 import math
 
@@ -66,7 +69,7 @@ def subtiles(N, H, W, nwg):
     return out
 
 
-def check_launch(N, H, D, KP, mode, W, nwg, topk, sample=1):
+def check_launch(N, H, D, KP, mode, W, nwg, topk, sample=1, rank0=0):
     s = shape(D, mode, W)
     NH = N * H
     tiles = subtiles(N, H, W, nwg)
@@ -126,16 +129,29 @@ def check_launch(N, H, D, KP, mode, W, nwg, topk, sample=1):
         # cand[(lhalf*cap + n)*NH + r], n < cap; cand_cnt[2r + lhalf]
         assert (1 * COLLECT_CAP + COLLECT_CAP - 1) * NH + (NH - 1) < 2 * COLLECT_CAP * NH
         assert 2 * (NH - 1) + 1 < 2 * NH
-    # outputs: (row*H + h)*topk + slot, slot < topk
-    assert ((N - 1) * H + H - 1) * topk + topk - 1 < NH * topk
+    # outputs: (row*H + h)*topk + rank0 + r, r < kk = min(KP, topk - rank0);
+    # a rank pass also reads entry rank0 - 1 of the row
+    kk = min(KP, topk - rank0)
+    assert kk >= 1 and ((N - 1) * H + H - 1) * topk + rank0 + kk - 1 < NH * topk
+    if rank0 > 0:
+        assert 0 <= rank0 - 1 < topk
     return kb_bytes + cb_bytes
 
 
 def test_recorded_fault_launch_shape_stays_in_bounds():
-    # score_topk_kernel<32, 45, 1, 8>: 256 workgroups x 512 threads
-    # (grid 131072), 64 KB of LDS, as in the record
+    # the former score_topk_kernel<32, 45, 1, 8>: 256 workgroups x 512
+    # threads (grid 131072), 64 KB of LDS, as in the records
     lds = check_launch(N=100000, H=4, D=32, KP=45, mode=M_SELECT, W=8, nwg=256, topk=45)
     assert lds == 65536
+
+
+@pytest.mark.parametrize("rank0", [0, 16, 32])
+def test_long_list_rank_passes_stay_in_bounds(rank0):
+    # score_topk_kernel<32, 16, 1, 16> recomputing overflowing rows of k = 45:
+    # one 1024-thread workgroup per CU (128 KB of LDS)
+    lds = check_launch(N=100000, H=4, D=32, KP=16, mode=M_SELECT, W=16, nwg=256, topk=45,
+                       rank0=rank0)
+    assert lds == 131072
 
 
 @pytest.mark.parametrize("N,H,D,KP,mode,W,nwg,topk,sample", [
@@ -147,7 +163,7 @@ def test_recorded_fault_launch_shape_stays_in_bounds():
     (31623, 4, 32, 15, M_SELECT, 16, 256, 15, 1),
     (8192, 4, 64, 8, M_SELECT, 16, 256, 8, 1),
     (16384, 2, 96, 15, M_SELECT, 16, 256, 15, 1),
-    (12288, 4, 32, 45, M_SELECT, 8, 512, 45, 1),
+    (12288, 4, 32, 16, M_SELECT, 16, 256, 45, 1),
 ])
 def test_one_graph_launches_stay_in_bounds(N, H, D, KP, mode, W, nwg, topk, sample):
     lds = check_launch(N, H, D, KP, mode, W, nwg, topk, sample)

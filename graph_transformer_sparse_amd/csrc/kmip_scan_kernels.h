@@ -72,7 +72,9 @@ constexpr int QB = 1;                       // query blocks of 32 per wavefront
 // than 16): every key scoring above next_down(T) is appended to a per-row
 // candidate array, and a second kernel selects the top-k from it; rows whose
 // arrays overflow are then recomputed by SELECT.
-constexpr int M_THRESH = 0, M_SELECT = 1, M_COLLECT = 2;
+// RANK: SELECT restricted to the rows whose candidate arrays overflowed,
+// computing 16 ranks of each per call (see Scanner::run).
+constexpr int M_THRESH = 0, M_SELECT = 1, M_COLLECT = 2, M_RANK = 3;
 template <int MODE> struct PassCfg;
 // SAMPLE: THRESH scores every SAMPLE-th chunk only.  Any subset of a
 // query's keys yields a valid lower bound of its k-th score; a sparser subset
@@ -83,6 +85,7 @@ template <> struct PassCfg<M_THRESH> {
 template <> struct PassCfg<M_SELECT> {
   static constexpr int LPW = 2, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = 1;
 };
+template <> struct PassCfg<M_RANK> : PassCfg<M_SELECT> {};
 template <> struct PassCfg<M_COLLECT> {
   static constexpr int LPW = 2, NBUF = 2, BATCH = KMIP_SCAN_BATCH, SAMPLE = 1;
 };
@@ -175,6 +178,8 @@ struct SubTile {
 template <int D, int KP, int MODE, int W>
 struct Scanner {
   static constexpr bool PRE = MODE == M_THRESH;
+  static constexpr bool RANK = MODE == M_RANK;
+  static constexpr bool SEL = MODE == M_SELECT || RANK;   // register-list selection
   // uint2 entries of LDS per wavefront: the candidate buffer (SCAN_CAP per
   // lane); after the last drain the same space holds the upper lanes' lists
   // for the merge.
@@ -276,29 +281,27 @@ struct Scanner {
 #pragma unroll
       for (int m = 0; m < S::NM; ++m) qb[b][m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
     }
-    // Rows this call writes.  SELECT with candidate counts (after COLLECT)
-    // recomputes only the rows whose candidate arrays overflowed and skips
-    // sub-tiles that have none.
+    // Rows this call writes.  A rank pass (after COLLECT) recomputes only the
+    // rows whose candidate arrays overflowed and skips sub-tiles that have
+    // none.
     bool keep[QB];
     bool wave_rows = bact[0];
 #pragma unroll
     for (int b = 0; b < QB; ++b) keep[b] = qvalid[b];
-    if constexpr (MODE == M_SELECT) {
-      if (a.cand_cnt != nullptr) {
-        const int64_t r = qrow[0] * H + t.h;
-        keep[0] = qvalid[0] && (a.cand_cnt[2 * r] > a.cap || a.cand_cnt[2 * r + 1] > a.cap);
-        wave_rows = __ballot(keep[0]) != 0ull;
-        // The first ring word serves as the workgroup's flag: no key load is
-        // in flight here and every wavefront is past the previous sub-tile.
-        volatile int* wg_flag = reinterpret_cast<volatile int*>(kbuf);
-        if (tid == 0) *wg_flag = 0;
-        __syncthreads();
-        if (wave_rows && lane == 0) *wg_flag = 1;
-        __syncthreads();
-        const bool any = *wg_flag != 0;
-        __syncthreads();                      // all have read it before the ring is refilled
-        if (!any) return;                     // uniform over the workgroup
-      }
+    if constexpr (RANK) {
+      const int64_t r = qrow[0] * H + t.h;
+      keep[0] = qvalid[0] && (a.cand_cnt[2 * r] > a.cap || a.cand_cnt[2 * r + 1] > a.cap);
+      wave_rows = __ballot(keep[0]) != 0ull;
+      // The first ring word serves as the workgroup's flag: no key load is
+      // in flight here and every wavefront is past the previous sub-tile.
+      volatile int* wg_flag = reinterpret_cast<volatile int*>(kbuf);
+      if (tid == 0) *wg_flag = 0;
+      __syncthreads();
+      if (wave_rows && lane == 0) *wg_flag = 1;
+      __syncthreads();
+      const bool any = *wg_flag != 0;
+      __syncthreads();                        // all have read it before the ring is refilled
+      if (!any) return;                       // uniform over the workgroup
     }
     const bool wave_active = wave_rows;
     const int aoff = lane * 16;
@@ -308,11 +311,11 @@ struct Scanner {
     // with overflowing candidate arrays for lists longer than 16, 16 ranks
     // at a time.  A rank pass keeps only keys ordered after the row's entry
     // rank0 - 1 (score descending, id ascending), written by the pass before.
-    const int rank0 = MODE == M_SELECT ? a.rank0 : 0;
+    const int rank0 = RANK ? a.rank0 : 0;
     const int kk = topk - rank0 < KP ? topk - rank0 : KP;
     float ubs = kInf;
     int ubj = -1;
-    if constexpr (MODE == M_SELECT) {
+    if constexpr (RANK) {
       if (rank0 > 0 && keep[0]) {
         const int64_t r = (qrow[0] * H + t.h) * topk + rank0 - 1;
         ubs = out_score[r];
@@ -380,8 +383,13 @@ struct Scanner {
           const int tag = (int)(e.y >> 31);
 #pragma unroll
           for (int b = 0; b < QB; ++b) {
-            if constexpr (MODE == M_SELECT) {
+            if constexpr (RANK) {
               if (tag == b && sv > thr[b] && (sv < ubs || (sv == ubs && key > ubj))) {
+                list_insert<KP>(ls[b], lj[b], sv, key);
+                thr[b] = fmaxf(thr[b], ls[b][KP - 1]);
+              }
+            } else if constexpr (SEL) {
+              if (tag == b && sv > thr[b]) {
                 list_insert<KP>(ls[b], lj[b], sv, key);
                 thr[b] = fmaxf(thr[b], ls[b][KP - 1]);
               }
@@ -634,7 +642,7 @@ void score_topk_kernel(ScanArgs a, int nwg) {
   using S = ScanShape<D, MODE, W>;
   // One LDS block: the key ring, then (SELECT) the candidate buffers.
   constexpr int KB = S::NBUF * S::CHUNK_BYTES;
-  constexpr int CB = MODE == M_SELECT ? W * Scanner<D, KP, MODE, W>::CBW * 8 : 0;
+  constexpr int CB = Scanner<D, KP, MODE, W>::SEL ? W * Scanner<D, KP, MODE, W>::CBW * 8 : 0;
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[KB + CB];
   uint2* cbuf = reinterpret_cast<uint2*>(kbuf + KB);
   const unsigned kbuf_lds =
@@ -896,7 +904,7 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     for (int r0 = 0; r0 < a.topk; r0 += 16) {
       ScanArgs b = a;
       b.rank0 = r0;
-      e = launch_pass<D, 16, M_SELECT>(b, s);
+      e = launch_pass<D, 16, M_RANK>(b, s);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

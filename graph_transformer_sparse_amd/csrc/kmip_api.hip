@@ -49,13 +49,22 @@ size_t collect_ws(int64_t N, int H, int topk) {
          align256((size_t)2 * N * H * sizeof(int32_t));
 }
 
-size_t forward_ws(int64_t N, int H, int topk, int num_graphs) {
+// One graph with a query order, bf16 rows of 32 or 64, lists of at most 16:
+// the pruned selection (its buffers follow the query order).  The entry
+// point without a workspace leaves it off: its static array holds the other
+// buffers only.
+bool use_prune(int64_t N, int H, int d_rows, int topk, int num_graphs, bool prune) {
+  return prune && num_graphs <= 1 && use_query_order(N, H) && prune_applies(N, H, d_rows, topk);
+}
+
+size_t forward_ws(int64_t N, int H, int d_rows, int topk, int num_graphs, bool prune = true) {
   size_t b = align256((size_t)N * H * sizeof(float));
   if (num_graphs > 1) {
     const int64_t tiles = scan_max_tiles(N, num_graphs);
     b += align256((size_t)(num_graphs + 1) * 4) + align256((size_t)tiles * sizeof(int2));
   } else if (use_query_order(N, H)) {
     b += query_order_bytes(N, H);
+    if (use_prune(N, H, d_rows, topk, num_graphs, prune)) b += prune_ws(N, H, d_rows, topk);
   }
   return b + collect_ws(N, H, topk);
 }
@@ -78,7 +87,8 @@ size_t split_ws(int64_t N, int H, int d) { return 2 * align256((size_t)N * H * 3
 // past any split rows.
 kmip_status_t score_topk_core(const uint16_t* q, const uint16_t* k, int64_t N, int H, int d_rows,
                               int topk, const int32_t* graph_offsets, int num_graphs,
-                              int32_t* topk_idx, float* topk_score, char* w, hipStream_t s) {
+                              int32_t* topk_idx, float* topk_score, char* w, hipStream_t s,
+                              bool prune = true) {
   const bool single = single_graph(graph_offsets, num_graphs);
   const int64_t max_tiles = scan_max_tiles(N, num_graphs);
   ScanArgs a{};
@@ -109,6 +119,10 @@ kmip_status_t score_topk_core(const uint16_t* q, const uint16_t* k, int64_t N, i
     if (st != KMIP_OK) return st;
     a.perm = perm;
     w += query_order_bytes(N, H);
+    if (use_prune(N, H, d_rows, topk, 1, prune)) {
+      prune_setup(a, d_rows, w);
+      w += prune_ws(N, H, d_rows, topk);
+    }
   }
   if (collect_ws(N, H, topk) > 0) {
     a.cand = reinterpret_cast<uint2*>(w);
@@ -131,7 +145,7 @@ kmip_status_t check_topk_args(const void* q, const void* k, int64_t N, int H, in
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(topk_idx, 4) || !aligned(topk_score, 4))
     return KMIP_ERR_INVALID_VALUE;
   const bool single = single_graph(graph_offsets, num_graphs);
-  const size_t need = forward_ws(N, H, topk, single ? 0 : num_graphs);
+  const size_t need = forward_ws(N, H, d, topk, single ? 0 : num_graphs);
   if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
   return KMIP_OK;
@@ -213,7 +227,7 @@ int kmip_version(void) { return kVersion; }
 
 size_t kmip_forward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
   if (check_shape(N, H, d, topk, num_graphs) != KMIP_OK) return 0;
-  return forward_ws(N, H, topk, num_graphs);
+  return forward_ws(N, H, d, topk, num_graphs);
 }
 
 size_t kmip_backward_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
@@ -278,7 +292,8 @@ kmip_status_t kmip_forward_no_workspace(const void* q, const void* k, const void
       !aligned(topk_idx, 4) || !aligned(topk_score, 4))
     return KMIP_ERR_INVALID_VALUE;
   const bool single = single_graph(graph_offsets, num_graphs);
-  if (forward_ws(N, H, topk, single ? 0 : num_graphs) > (size_t)KMIP_NO_WORKSPACE_BYTES)
+  if (forward_ws(N, H, d, topk, single ? 0 : num_graphs, false) >
+      (size_t)KMIP_NO_WORKSPACE_BYTES)
     return KMIP_ERR_WORKSPACE;
   void* ws = nullptr;
   st = static_scratch(&ws);
@@ -286,7 +301,7 @@ kmip_status_t kmip_forward_no_workspace(const void* q, const void* k, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = score_topk_core(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), N, H,
                        d, topk, graph_offsets, num_graphs, topk_idx, topk_score,
-                       static_cast<char*>(ws), s);
+                       static_cast<char*>(ws), s, false);
   if (st != KMIP_OK) return st;
   return launch_status(launch_gather_av(static_cast<const uint16_t*>(v), N, H, d, topk,
                                         topk_idx, topk_score, out, s));
@@ -303,7 +318,7 @@ kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t
 
 size_t kmip_forward_f32_workspace_bytes(int64_t N, int H, int d, int topk, int num_graphs) {
   if (check_shape(N, H, d, topk, num_graphs) != KMIP_OK) return 0;
-  return split_ws(N, H, d) + forward_ws(N, H, topk, num_graphs);
+  return split_ws(N, H, d) + forward_ws(N, H, 3 * d, topk, num_graphs);
 }
 
 kmip_status_t kmip_forward_f32(const float* q, const float* k, const float* v, int64_t N, int H,
@@ -318,7 +333,7 @@ kmip_status_t kmip_forward_f32(const float* q, const float* k, const float* v, i
       !aligned(topk_idx, 4) || !aligned(topk_score, 4))
     return KMIP_ERR_INVALID_VALUE;
   const bool single = single_graph(graph_offsets, num_graphs);
-  const size_t need = split_ws(N, H, d) + forward_ws(N, H, topk, single ? 0 : num_graphs);
+  const size_t need = split_ws(N, H, d) + forward_ws(N, H, 3 * d, topk, single ? 0 : num_graphs);
   if (workspace == nullptr || workspace_bytes < need) return KMIP_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return KMIP_ERR_INVALID_VALUE;
 

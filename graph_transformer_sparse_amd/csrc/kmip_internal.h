@@ -90,8 +90,51 @@ struct ScanArgs {
   // Selection pass: first rank it computes (0, or 16, 32, ... in the passes
   // that recompute rows with overflowing candidate arrays).
   int rank0;
+  // Pruned selection (one graph with a query order, rows of 32 or 64 bf16,
+  // lists of at most 16; kop == nullptr: off).  Keys are taken in the query
+  // order, in 32-key blocks (nkb per head, padded to ngr groups of 32):
+  //   kop  [H][nkb][D/16][64][8]  the block's keys in MFMA operand order;
+  //   bop  [H][ngr][D/8][64][8]   per block a bound row [mid | rad], D + D
+  //                               elements, in operand order (see
+  //                               key_pack_kernel);
+  //   live [wid1 - wid0][ngr]     per query block (wid = h * nkb + block of
+  //                               32 positions) a bit per key block whose
+  //                               bound reaches one of its thresholds;
+  //   qb_cnt [H * nkb]            live key blocks per query block;
+  //   range_cnt [nrange]          live key blocks per range of live_rows
+  //                               query blocks;
+  //   heavy_list [heavy_max], heavy_cnt [nrange]  query blocks of the current
+  //                               range with many live key blocks (split over
+  //                               several wavefronts), and their number per
+  //                               range;
+  //   heavy_parts [heavy_max][parts][32][16]  the parts' lists per query.
+  // A range whose query blocks have on average half of the key blocks live
+  // (inputs without cluster structure) is left to the streaming selection
+  // pass; the pruned pass takes the others.
+  uint16_t* kop;
+  uint16_t* bop;
+  uint32_t* live;
+  int32_t* qb_cnt;
+  int32_t* range_cnt;
+  int32_t* heavy_list;
+  int32_t* heavy_cnt;
+  uint2* heavy_parts;
+  int heavy_max;
+  int64_t nkb, ngr, wid0, wid1, live_rows, nrange;
 };
 hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s);
+// Pruned selection workspace for one graph of N nodes, H heads, rows of d
+// bf16 (0 when the pruned path does not apply): key copy, bound rows, one
+// range of live words, per-query-block counts.
+constexpr int64_t PRUNE_LIVE_BYTES = (int64_t)16 << 20;
+// Heavy query blocks (many live key blocks) held per range, and the
+// wavefronts each is split over.
+constexpr int PRUNE_HEAVY_MAX = 4096;
+constexpr int PRUNE_HEAVY_PARTS = 8;
+bool prune_applies(int64_t N, int H, int d, int topk);
+size_t prune_ws(int64_t N, int H, int d, int topk);
+// Carves the pruned-selection buffers out of w (prune_ws bytes) into a.
+void prune_setup(ScanArgs& a, int d, char* w);
 // Per row width (bf16 elements; 96 and 192 are split-precision rows of 32
 // and 64 fp32 elements), kp = scan_list_len(topk).
 hipError_t launch_scan_d32(int kp, const ScanArgs& a, hipStream_t s);

@@ -392,6 +392,70 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
   return hipGetLastError();
 }
 
+// Pruned selection buffers (see ScanArgs).  The live words of one range of
+// query blocks are kept at a time: PRUNE_LIVE_BYTES bound them whatever N is.
+namespace {
+struct PruneSizes {
+  int64_t nkb, ngr, live_rows, nrange, heavy_max;
+  size_t kop, bop, live, cnt, rcnt, heavy, parts;
+};
+PruneSizes prune_sizes(int64_t N, int H, int d) {
+  PruneSizes z{};
+  z.nkb = ceil_div(N, 32);
+  z.ngr = ceil_div(z.nkb, 32);
+  const int64_t rows = (int64_t)H * z.nkb;
+  const int64_t fit = PRUNE_LIVE_BYTES / (z.ngr * 4) / 16 * 16;
+  z.live_rows = rows < fit ? rows : (fit > 16 ? fit : 16);
+  z.kop = align256((size_t)rows * (d / 16) * 1024);
+  z.bop = align256((size_t)H * z.ngr * (d / 8) * 1024);
+  z.live = align256((size_t)z.live_rows * z.ngr * 4);
+  z.cnt = align256((size_t)rows * 4);
+  z.nrange = ceil_div(rows, z.live_rows);
+  z.rcnt = align256((size_t)z.nrange * 4);
+  z.heavy_max = z.live_rows < PRUNE_HEAVY_MAX ? z.live_rows : (int64_t)PRUNE_HEAVY_MAX;
+  z.heavy = align256((size_t)z.heavy_max * 4) + align256((size_t)z.nrange * 4);
+  z.parts = align256((size_t)z.heavy_max * PRUNE_HEAVY_PARTS * 32 * 16 * 8);
+  return z;
+}
+}  // namespace
+
+bool prune_applies(int64_t N, int H, int d, int topk) {
+  (void)H;
+  // the pruned pass keeps a query block's live words in LDS: 512 words,
+  // N <= 2^19
+  return (d == 32 || d == 64) && scan_list_len(topk) <= 16 && N <= ((int64_t)1 << 19);
+}
+
+size_t prune_ws(int64_t N, int H, int d, int topk) {
+  if (!prune_applies(N, H, d, topk)) return 0;
+  const PruneSizes z = prune_sizes(N, H, d);
+  return z.kop + z.bop + z.live + z.cnt + z.rcnt + z.heavy + z.parts;
+}
+
+void prune_setup(ScanArgs& a, int d, char* w) {
+  const PruneSizes z = prune_sizes(a.N, a.H, d);
+  a.kop = reinterpret_cast<uint16_t*>(w);
+  w += z.kop;
+  a.bop = reinterpret_cast<uint16_t*>(w);
+  w += z.bop;
+  a.live = reinterpret_cast<uint32_t*>(w);
+  w += z.live;
+  a.qb_cnt = reinterpret_cast<int32_t*>(w);
+  w += z.cnt;
+  a.range_cnt = reinterpret_cast<int32_t*>(w);
+  w += z.rcnt;
+  a.heavy_list = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)z.heavy_max * 4);
+  a.heavy_cnt = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)z.nrange * 4);
+  a.heavy_parts = reinterpret_cast<uint2*>(w);
+  a.heavy_max = (int)z.heavy_max;
+  a.nkb = z.nkb;
+  a.ngr = z.ngr;
+  a.live_rows = z.live_rows;
+  a.nrange = z.nrange;
+}
+
 hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s) {
   const int kp = scan_list_len(args.topk);
   switch (d) {

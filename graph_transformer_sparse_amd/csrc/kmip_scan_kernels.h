@@ -169,6 +169,18 @@ __device__ __forceinline__ bool quarter_hit(const floatx16_t& x, int qq, float t
   return (x[4 * qq] > t) | (x[4 * qq + 1] > t) | (x[4 * qq + 2] > t) | (x[4 * qq + 3] > t);
 }
 
+// Pruned selection: the range of query blocks that wid belongs to has on
+// average at least half of the key blocks live, or more heavy query blocks
+// than the pruned pass holds, so the streaming pass takes it (the counts are
+// complete once the range's bound pass has run).
+__device__ __forceinline__ bool prune_range_dense(const ScanArgs& a, int64_t wid) {
+  const int64_t r = wid / a.live_rows;
+  const int64_t r0 = r * a.live_rows;
+  const int64_t total = (int64_t)a.H * a.nkb;
+  const int64_t rows = total - r0 < a.live_rows ? total - r0 : a.live_rows;
+  return 2 * (int64_t)a.range_cnt[r] >= rows * a.nkb || a.heavy_cnt[r] > a.heavy_max;
+}
+
 struct SubTile {
   int h;
   int64_t q0, q1;     // query rows [q0, q1)
@@ -282,16 +294,27 @@ struct Scanner {
       for (int m = 0; m < S::NM; ++m) qb[b][m] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * m);
     }
     // Rows this call writes.  A rank pass (after COLLECT) recomputes only the
-    // rows whose candidate arrays overflowed and skips sub-tiles that have
-    // none.
+    // rows whose candidate arrays overflowed; after the pruned selection the
+    // selection pass takes only the query blocks left to it (qb_cnt at least
+    // dense_min).  Both skip sub-tiles with no such row.
     bool keep[QB];
     bool wave_rows = bact[0];
 #pragma unroll
     for (int b = 0; b < QB; ++b) keep[b] = qvalid[b];
+    bool filtered = RANK;
     if constexpr (RANK) {
       const int64_t r = qrow[0] * H + t.h;
       keep[0] = qvalid[0] && (a.cand_cnt[2 * r] > a.cap || a.cand_cnt[2 * r + 1] > a.cap);
       wave_rows = __ballot(keep[0]) != 0ull;
+    } else if constexpr (MODE == M_SELECT) {
+      static_assert(QB == 1, "one query block per wavefront");
+      if (a.range_cnt != nullptr) {
+        filtered = true;
+        wave_rows = bact[0] && prune_range_dense(a, t.h * a.nkb + t.q0 / 32 + wave);
+        keep[0] = keep[0] && wave_rows;
+      }
+    }
+    if (filtered) {
       // The first ring word serves as the workgroup's flag: no key load is
       // in flight here and every wavefront is past the previous sub-tile.
       volatile int* wg_flag = reinterpret_cast<volatile int*>(kbuf);
@@ -877,6 +900,8 @@ __global__ __launch_bounds__(WIN_WAVES * 64) void window_thresh_kernel(ScanArgs 
   }
 }
 
+#include "kmip_prune.h"
+
 template <int D, int KP>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
   hipError_t e = launch_pass<D, KP, M_THRESH>(a, s);
@@ -910,7 +935,15 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     return hipSuccess;
   } else {
     ScanArgs b = a;
-    b.cand_cnt = nullptr;                      // SELECT writes every row
+    b.cand_cnt = nullptr;
+    b.range_cnt = nullptr;                     // SELECT writes every row...
+    if constexpr (D == 32 || D == 64) {
+      if (a.kop != nullptr) {                  // ...but those of the pruned pass
+        e = launch_prune<D, KP>(a, s);
+        if (e != hipSuccess) return e;
+        b.range_cnt = a.range_cnt;
+      }
+    }
     return launch_pass<D, KP, M_SELECT>(b, s);
   }
 }

@@ -40,8 +40,12 @@ int main() {
             const size_t f = kmip_forward_workspace_bytes(N, H, d, k, B);
             const size_t f32 = kmip_forward_f32_workspace_bytes(N, H, d, k, B);
             const size_t b = kmip_backward_workspace_bytes(N, H, d, k, B);
-            expect(f > 0 && b > 0 && f32 >= f, "sizes of a valid shape", (long)N, k);
-            expect(kmip_forward_workspace_bytes(2 * N, H, d, k, B) >= f, "forward grows", (long)N, k);
+            expect(f > 0 && b > 0 && f32 > 0, "sizes of a valid shape", (long)N, k);
+            // one graph, lists of at most 16: the pruned selection's buffers
+            // (about 2d + 5 bytes per row) are held up to N = 2^19 only
+            const bool prune_edge = B <= 1 && k <= 16 && N <= (1 << 19) && 2 * N > (1 << 19);
+            if (!prune_edge)
+              expect(kmip_forward_workspace_bytes(2 * N, H, d, k, B) >= f, "forward grows", (long)N, k);
             expect(kmip_backward_workspace_bytes(2 * N, H, d, k, B) >= b, "backward grows", (long)N, k);
           }
   expect(kmip_forward_workspace_bytes(0, 4, 32, 15, 0) == 0, "N = 0");

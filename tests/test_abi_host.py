@@ -84,10 +84,21 @@ def test_workspace_sizes_are_linear_in_n():
     # One graph: an fp32 threshold, an int32 query-order entry and a 16-bit
     # code per row, plus per-head pivot counters (two int32 tables of 16
     # copies per pivot, one pivot per ~96 nodes: under 1.5 bytes per row).
+    # The pruned selection adds per row a copy of its key (2d bytes), a
+    # share of its block's bound row (d/8 bytes) and of its block's count,
+    # plus the live words of one range of query blocks (ceil(N/1024) words
+    # per block of 32 rows, at most 16 MiB) and the part lists of up to 4096
+    # heavy query blocks (128 MiB).
     rows = 100000 * 4
-    assert rows * 10 <= f(100000, 4, 32, 15, 0) <= rows * 10 + (4 << 20)
-    grow = f(200000, 4, 32, 15, 0) - f(100000, 4, 32, 15, 0)   # linear in N
-    assert rows * 10 <= grow <= rows * 10 + rows * 3 // 2 + 4096
+    per_row = 10 + 64 + 4
+    live1 = 4 * 3125 * 98 * 4
+    parts = 4096 * 8 * 32 * 16 * 8                      # heavy query blocks' part lists
+    assert rows * per_row + live1 + parts <= f(100000, 4, 32, 15, 0) <= rows * per_row + live1 + parts + (4 << 20)
+    grow = f(200000, 4, 32, 15, 0) - f(100000, 4, 32, 15, 0)   # linear in N but the live words
+    assert rows * per_row <= grow <= rows * per_row + rows * 3 // 2 + (16 << 20) - live1 + (64 << 10)
+    assert f(500000, 4, 32, 15, 0) <= 2000000 * (per_row + 2) + (16 << 20) + parts + (4 << 20)
+    # without the pruned pass (lists longer than 16): the first three terms only
+    assert rows * 10 <= f(100000, 4, 32, 45, 0) - 2 * 128 * rows * 8 - rows * 8 <= rows * 10 + (4 << 20)
     assert f(100000, 4, 32, 15, 64) > rows * 4                # thresholds plus the tile plan
     b1, b2 = b(100000, 4, 32, 15), b(200000, 4, 32, 15)
     assert 1.9 < b2 / b1 < 2.1                              # O(N * H * k)
@@ -119,11 +130,29 @@ def test_backward_f32_rejects():
     assert L.kmip_backward_f32(*args, FAKE, 1 << 40, None) == INVALID
 
 
+def _pruned_bytes(N, H, d):
+    """Buffers of the pruned selection (one graph with a query order, bf16
+    rows of 32 or 64, lists of at most 16)."""
+    a = lambda x: (x + 255) // 256 * 256
+    nkb = -(-N // 32)
+    ngr = -(-nkb // 32)
+    rows = H * nkb
+    live_rows = min(rows, max(16, (16 << 20) // (ngr * 4) // 16 * 16))
+    nrange = -(-rows // live_rows)
+    heavy = min(live_rows, 4096)
+    return (a(rows * (d // 16) * 1024) + a(H * ngr * (d // 8) * 1024) + a(live_rows * ngr * 4)
+            + a(rows * 4) + 2 * a(nrange * 4) + a(heavy * 4) + a(heavy * 8 * 32 * 16 * 8))
+
+
 def test_f32_workspace_adds_split_rows():
-    # The fp32 forward also holds q and k as bf16 rows of 3d elements.
-    for (N, H, d, k, B) in [(1000, 2, 32, 15, 0), (100000, 4, 32, 15, 0), (5000, 4, 64, 45, 7)]:
+    # The fp32 forward also holds q and k as bf16 rows of 3d elements; its
+    # rows are 3d wide, so it has no pruned selection.
+    for (N, H, d, k, B, pruned) in [(1000, 2, 32, 15, 0, False), (100000, 4, 32, 15, 0, True),
+                                    (5000, 4, 64, 45, 7, False)]:
         extra = kmip.forward_f32_workspace_bytes(N, H, d, k, B) - kmip.forward_workspace_bytes(
             N, H, d, k, B)
+        if pruned:
+            extra += _pruned_bytes(N, H, d)
         assert 12 * N * H * d <= extra <= 12 * N * H * d + 512
     assert kmip.forward_f32_workspace_bytes(10, 4, 48, 15, 0) == 0
 
@@ -145,4 +174,7 @@ def test_no_workspace_forward_rejects_before_any_gpu_call():
     st = L.kmip_forward_no_workspace(FAKE, FAKE, FAKE, 1000, 4, 48, 15, None, 0, FAKE, FAKE,
                                      FAKE, None)
     assert st == 2                                     # KMIP_ERR_UNSUPPORTED
-    assert kmip.forward_workspace_bytes(500000, 4, 32, 15, 0) <= kmip.NO_WORKSPACE_BYTES
+    # the entry without a workspace runs without the pruned selection: the
+    # rest of the forward workspace fits its static array up to N = 5e5
+    assert (kmip.forward_workspace_bytes(500000, 4, 32, 15, 0) - _pruned_bytes(500000, 4, 32)
+            <= kmip.NO_WORKSPACE_BYTES)

@@ -242,3 +242,38 @@ def test_gradient_identities_on_gpu_outputs():
         sdo = w.dout[lo:hi].astype(np.float64).sum(0)
         assert np.allclose(dv[lo:hi].sum(0), sdo, atol=1e-3 * np.abs(sdo).max() + 1e-4)
         assert np.abs(dk[lo:hi].sum(0)).max() <= 1e-3 * np.abs(dk[lo:hi]).sum(0).max() + 1e-5
+
+
+def test_exact_ties_on_the_pruned_path():
+    """One graph with a query order (N*H >= 32768), so the selection scores
+    the live key blocks of each query block in the query order, out of node
+    order: 97 distinct key rows, each repeated ~340 times, give bitwise-equal
+    scores, and the smaller node id must still win every tie."""
+    from tests.gpu_util import np_, run_forward
+    w = small_case(8192, 4, 32, 15, law="clustered", clusters=48, seed=131)
+    w.k = w.k[np.arange(8192) % 97]
+    print(f"[case] ties n={w.n} H={w.heads} d={w.d} k={w.topk}", flush=True)
+    t, out, idx, score = run_forward(w)
+    q, k, v = decode(w)
+    fw = orc.kmip_forward(q, k, v, None, w.topk)
+    assert np.array_equal(np_(idx), fw["idx"].astype(np.int32))
+
+
+@pytest.mark.parametrize("d", [32, 64])
+def test_pruned_and_streaming_query_blocks_mixed(d):
+    """Half of the nodes in tight clusters, half i.i.d.: the clustered query
+    blocks take the pruned selection, the i.i.d. ones (whose bounds leave most
+    key blocks live) the streaming pass; every row against the oracle,
+    forward and backward."""
+    from workloads import f32_to_bf16_bits
+    n, heads = 16384, 2
+    w = small_case(n, heads, d, 8, law="clustered", clusters=32, seed=171 + d)
+    rng = np.random.default_rng(5 + d)
+    half = n // 2
+    for name in ("q", "k"):
+        x = getattr(w, name).copy()
+        x[half:] = f32_to_bf16_bits(rng.standard_normal((n - half, heads, d), dtype=np.float32) * 1.4)
+        setattr(w, name, x)
+    t, out, idx, score, st = _forward_check(w)
+    assert st["rows"] == n * heads
+    _backward_check(w, t, idx, score)

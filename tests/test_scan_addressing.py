@@ -178,3 +178,135 @@ def test_partition_is_contiguous_per_workgroup():
         by_wg.setdefault(L, []).append(h * nbph * 32 + q0)
     for L, starts in by_wg.items():
         assert starts == sorted(starts)
+
+
+# ---------------------------------------------------------------- pruned selection
+PR_WAVES, PS_WAVES, PR_MAX_WORDS, PR_LPW, PR_NBUF, PS_NPF = 16, 4, 512, 2, 3, 4
+
+
+def pruned_sizes(N, H, D):
+    nkb = -(-N // 32)
+    ngr = -(-nkb // 32)
+    rows = H * nkb
+    live_rows = min(rows, max(16, (16 << 20) // (ngr * 4) // 16 * 16))
+    return nkb, ngr, live_rows
+
+
+def check_pruned(N, H, D, nwg=256):
+    """Every index formed by key_pack_kernel, bound_live_kernel and
+    pruned_select_kernel (elements of kop / bop / live, LDS offsets) against
+    the sizes the host gives those buffers."""
+    NM, NMB = D // 16, D // 8
+    nkb, ngr, live_rows = pruned_sizes(N, H, D)
+    kop_elems, bop_elems = H * nkb * NM * 512, H * ngr * NMB * 512
+    assert ngr <= PR_MAX_WORDS
+    # key_pack_kernel: grid (ceil(32 ngr / 4), H) x 4 wavefronts
+    for h in (0, H - 1):
+        for b in (0, nkb - 1, nkb, ngr * 32 - 1):
+            if b >= ngr * 32:
+                continue
+            g, br = b // 32, b % 32
+            for lane in (0, 31, 32, 63):
+                lh = lane >> 5
+                for m in range(2 * NM):
+                    e = ((h * ngr + g) * 2 * NM + m) * 512 + (br + 32 * lh) * 8
+                    assert 0 <= e and e + 8 <= bop_elems
+                if b < nkb:
+                    pos = b * 32 + (lane & 31)
+                    assert h * N + min(pos, N - 1) < H * N
+                    for m in range(NM):
+                        node = N - 1
+                        assert (node * H + h) * D + 8 * lh + 16 * m + 8 <= N * H * D
+                        e = ((h * nkb + b) * NM + m) * 512 + lane * 8
+                        assert e + 8 <= kop_elems
+    # bound_live_kernel: ranges of live_rows query blocks, sub-tiles of <= 16
+    total = H * nkb
+    nrange = -(-total // live_rows)
+    GPB = PR_WAVES * PR_LPW // NMB
+    assert GPB * NMB == PR_WAVES * PR_LPW
+    SLOT = GPB * NMB * 1024
+    assert PR_NBUF * SLOT + PR_WAVES * PR_MAX_WORDS * 4 <= 160 * 1024
+    covered = 0
+    for r0 in range(0, total, live_rows):
+        r1 = min(total, r0 + live_rows)
+        seen = set()
+        for L in range(nwg):
+            b, be = r0 + (r1 - r0) * L // nwg, r0 + (r1 - r0) * (L + 1) // nwg
+            while b < be:
+                h, nb0 = b // nkb, b % nkb
+                rem = be - b
+                nst = -(-rem // PR_WAVES)
+                n = min(-(-rem // nst), nkb - nb0)
+                assert 1 <= n <= PR_WAVES
+                for w in range(n):
+                    wid = b + w
+                    assert wid not in seen and r0 <= wid < r1
+                    seen.add(wid)
+                    assert (wid - r0) * ngr + ngr - 1 < live_rows * ngr
+                    assert wid < total and wid // live_rows < nrange
+                b += n
+        assert len(seen) == r1 - r0
+        covered += len(seen)
+        # ring loads: wavefront w, piece p = w + i * PR_WAVES, batch ib (groups
+        # past the last one re-read the last)
+        for ib in (0, -(-ngr // GPB) - 1):
+            for w in range(PR_WAVES):
+                for i in range(PR_LPW):
+                    p = w + i * PR_WAVES
+                    g = min(ib * GPB + p // NMB, ngr - 1)
+                    e = ((H - 1) * ngr + g) * NMB * 512 + (p % NMB) * 512 + 63 * 8
+                    assert e + 8 <= bop_elems
+                    lds = (PR_NBUF - 1) * SLOT + p * 1024 + 63 * 16
+                    assert lds + 16 <= PR_NBUF * SLOT
+        # pruned_select_kernel: 8 * ceil(ceil(n / 4) / 8) workgroups
+        wgs = -(-(r1 - r0) // PS_WAVES)
+        grid = 8 * -(-wgs // 8)
+        per = grid // 8
+        logical = sorted((bx % 8) * per + bx // 8 for bx in range(grid))
+        assert logical == list(range(grid))
+        # the largest wid it scores and the block reads
+        assert r0 + (grid - 1) * PS_WAVES + 3 >= r1 - 1
+        PSLOT = NM * 1024 + 256
+        assert PS_WAVES * PS_NPF * PSLOT + PS_WAVES * 8 * 64 * 8 <= 160 * 1024
+        for bb in (0, nkb - 1):
+            for m in range(NM):
+                e = (H - 1) * nkb * NM * 512 + 63 * 8 + (bb * NM + m) * 512
+                assert e + 8 <= kop_elems
+                lds = (PS_WAVES - 1) * PS_NPF * PSLOT + (PS_NPF - 1) * PSLOT + m * 1024 + 63 * 16
+                assert lds + 16 <= PS_WAVES * PS_NPF * PSLOT
+            # ids: lane offset (p - 32 bb) * 4 from perm + h N + 32 bb, p < N
+            for lane in (0, 31, 63):
+                p = min(bb * 32 + (lane & 31), N - 1)
+                assert 0 <= (p - bb * 32) * 4 <= 124 and (H - 1) * N + p < H * N
+            lds = (PS_NPF - 1) * PSLOT + NM * 1024 + 63 * 4
+            assert lds + 4 <= PS_NPF * PSLOT
+    assert covered == total
+    # the last key block holds N - 32 (nkb - 1) keys; live bits past nkb are masked
+    assert 1 <= N - 32 * (nkb - 1) <= 32
+    return nkb, ngr, live_rows
+
+
+@pytest.mark.parametrize("N,H,D", [(100000, 4, 32), (31623, 4, 32), (8192, 4, 32), (16384, 2, 64),
+                                   (500000, 4, 32), (524288, 4, 64), (9000, 4, 32)])
+def test_pruned_selection_indices_stay_in_bounds(N, H, D):
+    nkb, ngr, live_rows = check_pruned(N, H, D)
+    assert live_rows * ngr * 4 <= 16 << 20
+
+
+@pytest.mark.parametrize("N,H", [(100000, 4), (500000, 4), (8192, 4), (40000, 1)])
+def test_heavy_parts_and_merge_stay_in_bounds(N, H):
+    """pruned_part_kernel / pruned_merge_kernel: heavy query block i (i <
+    heavy_max, slots past it are never written) in PARTS parts; part t = i
+    PARTS + p writes entries ((t 32 + q) 16 + r), r < topk <= 16, and the
+    merge reads entries ((i PARTS 32 + q) 16) + p 32 16 + at, at < topk; the
+    parts' words p, p + PARTS, ... cover each word once."""
+    PARTS, HMAX = 8, 4096
+    nkb, ngr, live_rows = pruned_sizes(N, H, 32)
+    heavy_max = min(live_rows, HMAX)
+    size = heavy_max * PARTS * 32 * 16
+    i, q, p, r = heavy_max - 1, 31, PARTS - 1, 15
+    t = i * PARTS + p
+    assert (t * 32 + q) * 16 + r < size
+    assert (i * PARTS * 32 + q) * 16 + p * 32 * 16 + r < size
+    words = sorted(w for p in range(PARTS) for w in range(p, ngr, PARTS))
+    assert words == list(range(ngr))

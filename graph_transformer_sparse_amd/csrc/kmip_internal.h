@@ -100,37 +100,43 @@ struct ScanArgs {
   //   live [wid1 - wid0][ngr]     per query block (wid = h * nkb + block of
   //                               32 positions) a bit per key block whose
   //                               bound reaches one of its thresholds;
-  //   qb_cnt [H * nkb]            live key blocks per query block;
+  //   qb_cnt [H * nkb]            live key blocks per query block (negated
+  //                               for a heavy one left unsplit);
   //   range_cnt [nrange]          live key blocks per range of live_rows
-  //                               query blocks;
+  //                               (= 2^live_shift) query blocks;
+  //   range_stream [nrange]       1: the streaming pass takes the range;
   //   heavy_list [heavy_max], heavy_cnt [nrange]  query blocks of the current
   //                               range with many live key blocks (split over
   //                               several wavefronts), and their number per
   //                               range;
   //   heavy_parts [heavy_max][parts][32][16]  the parts' lists per query.
-  // A range whose query blocks have on average half of the key blocks live
-  // (inputs without cluster structure) is left to the streaming selection
-  // pass; the pruned pass takes the others.
+  // A range whose query blocks have on average more than PRUNE_STREAM_NUM /
+  // PRUNE_STREAM_DEN of the key blocks live (inputs without enough cluster
+  // structure) is left to the streaming selection pass; the pruned pass
+  // takes the others.
   uint16_t* kop;
   uint16_t* bop;
   uint32_t* live;
   int32_t* qb_cnt;
   int32_t* range_cnt;
+  int32_t* range_stream;
   int32_t* heavy_list;
   int32_t* heavy_cnt;
   uint2* heavy_parts;
   int heavy_max;
   int64_t nkb, ngr, wid0, wid1, live_rows, nrange;
+  int live_shift;
 };
 hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s);
 // Pruned selection workspace for one graph of N nodes, H heads, rows of d
 // bf16 (0 when the pruned path does not apply): key copy, bound rows, one
 // range of live words, per-query-block counts.
 constexpr int64_t PRUNE_LIVE_BYTES = (int64_t)16 << 20;
-// Heavy query blocks (many live key blocks) held per range, and the
-// wavefronts each is split over.
-constexpr int PRUNE_HEAVY_MAX = 4096;
+// Heavy query blocks (many live key blocks) split per range (further ones
+// run unsplit), and the wavefronts each is split over.
+constexpr int PRUNE_HEAVY_MAX = 8192;
 constexpr int PRUNE_HEAVY_PARTS = 8;
+constexpr int PRUNE_STREAM_NUM = 1, PRUNE_STREAM_DEN = 4;
 bool prune_applies(int64_t N, int H, int d, int topk);
 size_t prune_ws(int64_t N, int H, int d, int topk);
 // Carves the pruned-selection buffers out of w (prune_ws bytes) into a.

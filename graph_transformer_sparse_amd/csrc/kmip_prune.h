@@ -292,12 +292,15 @@ __global__ __launch_bounds__(PR_WAVES * 64) void bound_live_kernel(ScanArgs a, i
       uint32_t* lw = a.live + (wid - a.wid0) * ngr;
       for (int64_t w = lane; w < ngr; w += 64) lw[w] = ws[w];
       if (lane == 0) {
-        a.qb_cnt[wid] = cnt;
-        atomicAdd(a.range_cnt + wid / a.live_rows, cnt);
+        atomicAdd(a.range_cnt + ((int)wid >> a.live_shift), cnt);
+        // a heavy block without a place in the heavy list (-cnt) runs unsplit
+        int c = cnt;
         if (cnt > PR_HEAVY) {
-          const int slot = atomicAdd(a.heavy_cnt + wid / a.live_rows, 1);
+          const int slot = atomicAdd(a.heavy_cnt + ((int)wid >> a.live_shift), 1);
           if (slot < a.heavy_max) a.heavy_list[slot] = (int32_t)wid;
+          else c = -cnt;
         }
+        a.qb_cnt[wid] = c;
       }
     }
   }
@@ -376,6 +379,7 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
     }
   };
   auto drain = [&]() __attribute__((always_inline)) {
+#pragma unroll 1
     for (int c = 0; __ballot(c < cnt) != 0ull; ++c) {
       if (c < cnt) {
         const uint2 e = cb[c * 64];
@@ -471,17 +475,25 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
   // Everything this wavefront loaded so far has arrived: from here the ring
   // loads are counted.
   __builtin_amdgcn_s_waitcnt(0x0f70);
-  int bq[NPF];
-#pragma unroll
-  for (int i = 0; i < NPF; ++i) {
-    bq[i] = next();
-    fill(i, bq[i]);
+  static_assert(NPF >= 2 && NPF <= 4, "blocks in flight");
+  // the next NPF blocks (bq0 first); slot `slot` holds bq0
+  int bq0 = next(), bq1 = -1, bq2 = -1, bq3 = -1;
+  fill(0, bq0);
+  bq1 = next();
+  fill(1, bq1);
+  if constexpr (NPF > 2) {
+    bq2 = next();
+    fill(2, bq2);
+  }
+  if constexpr (NPF > 3) {
+    bq3 = next();
+    fill(3, bq3);
   }
 
-  auto process = [&](int i) __attribute__((always_inline)) {
-    // slot i's loads were followed by those of the NPF - 1 other slots
+  auto process = [&](int slot, int bb) __attribute__((always_inline)) {
+    // the slot's loads were followed by those of the NPF - 1 other slots
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NPF - 1) * LPB) : "memory");
-    const unsigned char* sl = wring + i * SLOT;
+    const unsigned char* sl = wring + slot * SLOT;
     floatx16_t s = {};
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -491,7 +503,7 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
     // Rows past the last key (zero rows of the copy) may pass this test;
     // they are never appended.
     if (__ballot(block_max(s) > thr) == 0ull) return;
-    const int nrow = bq[i] == last ? nlast : 32;
+    const int nrow = bb == last ? nlast : 32;
     const int32_t* ids = reinterpret_cast<const int32_t*>(sl + NM * 1024);
     bool gq[4];
 #pragma unroll
@@ -519,18 +531,19 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
     }
   };
 
-  bool more = bq[0] >= 0;
-  while (more) {
-#pragma unroll
-    for (int i = 0; i < NPF; ++i) {
-      if (bq[i] < 0) {
-        more = false;
-        break;
-      }
-      process(i);
-      bq[i] = next();
-      fill(i, bq[i]);
-    }
+  // One copy of the block step: the slot index and the queue of block ids
+  // rotate (blocks come out of next() in order, so once bq0 is -1 all are).
+  int slot = 0;
+#pragma unroll 1
+  while (bq0 >= 0) {
+    process(slot, bq0);
+    const int nb = next();
+    fill(slot, nb);
+    bq0 = bq1;
+    bq1 = NPF > 2 ? bq2 : nb;
+    bq2 = NPF > 3 ? bq3 : nb;
+    bq3 = nb;
+    slot = slot + 1 == NPF ? 0 : slot + 1;
   }
   // the ring loads still in flight land in this wavefront's own slots
   __builtin_amdgcn_s_waitcnt(0x0f70);
@@ -538,12 +551,13 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
 }
 
 // One wavefront per query block wid in [wid0, wid1) of a range left to this
-// pass, with at most PR_HEAVY live key blocks.  Workgroups of PS_WAVES
+// pass, with at most PR_HEAVY live key blocks, or more but no place in the
+// heavy list (qb_cnt negative).  Workgroups of PS_WAVES
 // wavefronts; logical ids grouped per XCD (gridDim.x is a multiple of 8),
 // so each XCD's L2 serves neighbouring query blocks, which share most live
 // key blocks.
 template <int D, int KP>
-__global__ __launch_bounds__(PS_WAVES * 64) void pruned_select_kernel(ScanArgs a) {
+__global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3))) void pruned_select_kernel(ScanArgs a) {
   static_assert(KP <= 16, "register lists");
   constexpr int CBW = SCAN_CAP * 64;
   constexpr int SLOT = (D / 16) * 1024 + 256;
@@ -556,8 +570,8 @@ __global__ __launch_bounds__(PS_WAVES * 64) void pruned_select_kernel(ScanArgs a
   const int64_t L = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
   const int64_t wid = a.wid0 + L * PS_WAVES + wave;
   if (wid >= a.wid1) return;
-  if (prune_range_dense(a, wid)) return;               // left to the streaming pass
-  if (a.qb_cnt[wid] > PR_HEAVY) return;                // left to the heavy pass
+  if (prune_range_stream(a, wid)) return;              // left to the streaming pass
+  if (a.qb_cnt[wid] > PR_HEAVY) return;                // left to the parts (below)
   const int H = a.H, topk = a.topk;
   const int h = (int)(wid / a.nkb);
   float ls[KP];
@@ -620,9 +634,9 @@ __global__ __launch_bounds__(PS_WAVES * 64) void pruned_select_kernel(ScanArgs a
 //   parts[((i PH_PARTS + p) 32 + query) 16 + r],  r < topk.
 // One wavefront per part; the grid covers heavy_max * PH_PARTS parts, and
 // wavefronts past heavy_cnt * PH_PARTS (heavy_list as the bound pass left
-// it) return at once.
+// it) return at once (a persistent loop over the parts measured slower).
 template <int D, int KP>
-__global__ __launch_bounds__(PS_WAVES * 64) void pruned_part_kernel(ScanArgs a) {
+__global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3))) void pruned_part_kernel(ScanArgs a) {
   static_assert(KP <= 16, "register lists");
   constexpr int CBW = SCAN_CAP * 64;
   constexpr int SLOT = (D / 16) * 1024 + 256;
@@ -631,10 +645,11 @@ __global__ __launch_bounds__(PS_WAVES * 64) void pruned_part_kernel(ScanArgs a) 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int nparts = a.heavy_cnt[a.wid0 / a.live_rows] * PH_PARTS;
+  const int nh = a.heavy_cnt[(int)a.wid0 >> a.live_shift];
+  const int nparts = (nh < a.heavy_max ? nh : a.heavy_max) * PH_PARTS;
   const int t = blockIdx.x * PS_WAVES + wave;
   if (t >= nparts) return;
-  if (prune_range_dense(a, a.wid0)) return;            // the whole range streams
+  if (prune_range_stream(a, a.wid0)) return;           // the whole range streams
   const int topk = a.topk;
   const int nsent = KP - topk;
   uint2* wl = cbuf + wave * CBW;
@@ -691,8 +706,9 @@ template <int KP>
 __global__ __launch_bounds__(256) void pruned_merge_kernel(ScanArgs a) {
   constexpr int E = PH_PARTS * 32 * 16;
   __shared__ uint2 sl[E];
-  if (prune_range_dense(a, a.wid0)) return;
-  const int nh = a.heavy_cnt[a.wid0 / a.live_rows];
+  if (prune_range_stream(a, a.wid0)) return;
+  const int nh0 = a.heavy_cnt[(int)a.wid0 >> a.live_shift];
+  const int nh = nh0 < a.heavy_max ? nh0 : a.heavy_max;
   const int topk = a.topk;
   const int H = a.H;
   for (int hi = blockIdx.x; hi < nh; hi += gridDim.x) {
@@ -732,6 +748,15 @@ __global__ __launch_bounds__(256) void pruned_merge_kernel(ScanArgs a) {
   }
 }
 
+// After a range's bound pass: whether the streaming pass takes the range
+// (more than PRUNE_STREAM_NUM / PRUNE_STREAM_DEN of its key blocks live on
+// average).
+__global__ void prune_decide_kernel(ScanArgs a) {
+  const int r = (int)a.wid0 >> a.live_shift;
+  const int64_t rows = a.wid1 - a.wid0;
+  a.range_stream[r] = (int64_t)a.range_cnt[r] * PRUNE_STREAM_DEN >= rows * a.nkb * PRUNE_STREAM_NUM;
+}
+
 // Key copy and bound rows, then per range of query blocks the bound pass and
 // the pruned selection: light query blocks, the parts of heavy ones, their
 // merge.  range_cnt / heavy_cnt then tell the streaming pass which ranges are
@@ -752,6 +777,9 @@ hipError_t launch_prune(const ScanArgs& a, hipStream_t s) {
     b.wid0 = r;
     b.wid1 = r + a.live_rows < total ? r + a.live_rows : total;
     hipLaunchKernelGGL(bk, dim3((unsigned)nwg), dim3(PR_WAVES * 64), 0, s, b, nwg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prune_decide_kernel, dim3(1), dim3(1), 0, s, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t wgs = ceil_div(b.wid1 - b.wid0, PS_WAVES);

@@ -397,6 +397,7 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
 namespace {
 struct PruneSizes {
   int64_t nkb, ngr, live_rows, nrange, heavy_max;
+  int live_shift;
   size_t kop, bop, live, cnt, rcnt, heavy, parts;
 };
 PruneSizes prune_sizes(int64_t N, int H, int d) {
@@ -404,15 +405,21 @@ PruneSizes prune_sizes(int64_t N, int H, int d) {
   z.nkb = ceil_div(N, 32);
   z.ngr = ceil_div(z.nkb, 32);
   const int64_t rows = (int64_t)H * z.nkb;
-  const int64_t fit = PRUNE_LIVE_BYTES / (z.ngr * 4) / 16 * 16;
-  z.live_rows = rows < fit ? rows : (fit > 16 ? fit : 16);
+  // ranges of 2^live_shift query blocks (at least 16), as many as the live
+  // words' budget holds (one range up to a few 10^5 nodes: each range is a
+  // chain of launches with its own tail)
+  const int64_t fit = PRUNE_LIVE_BYTES / (z.ngr * 4);
+  z.live_shift = 4;
+  while (((int64_t)2 << z.live_shift) <= fit && ((int64_t)1 << z.live_shift) < rows) ++z.live_shift;
+  z.live_rows = (int64_t)1 << z.live_shift;
+  const int64_t held = rows < z.live_rows ? rows : z.live_rows;
   z.kop = align256((size_t)rows * (d / 16) * 1024);
   z.bop = align256((size_t)H * z.ngr * (d / 8) * 1024);
-  z.live = align256((size_t)z.live_rows * z.ngr * 4);
+  z.live = align256((size_t)held * z.ngr * 4);
   z.cnt = align256((size_t)rows * 4);
   z.nrange = ceil_div(rows, z.live_rows);
-  z.rcnt = align256((size_t)z.nrange * 4);
-  z.heavy_max = z.live_rows < PRUNE_HEAVY_MAX ? z.live_rows : (int64_t)PRUNE_HEAVY_MAX;
+  z.rcnt = 2 * align256((size_t)z.nrange * 4);
+  z.heavy_max = held < PRUNE_HEAVY_MAX ? held : (int64_t)PRUNE_HEAVY_MAX;
   z.heavy = align256((size_t)z.heavy_max * 4) + align256((size_t)z.nrange * 4);
   z.parts = align256((size_t)z.heavy_max * PRUNE_HEAVY_PARTS * 32 * 16 * 8);
   return z;
@@ -421,9 +428,12 @@ PruneSizes prune_sizes(int64_t N, int H, int d) {
 
 bool prune_applies(int64_t N, int H, int d, int topk) {
   (void)H;
-  // the pruned pass keeps a query block's live words in LDS: 512 words,
-  // N <= 2^19
-  return (d == 32 || d == 64) && scan_list_len(topk) <= 16 && N <= ((int64_t)1 << 19);
+  // From 2^16 nodes on: below, the streaming pass is faster (N = 31623:
+  // 0.48 against 0.68 ms; the pruned pass pays a bound pass and a fixed
+  // cost per wavefront).  Up to 2^19: block and word indices are 32-bit
+  // shifts of the query block index.
+  return (d == 32 || d == 64) && scan_list_len(topk) <= 16 && N >= ((int64_t)1 << 16) &&
+         N <= ((int64_t)1 << 19);
 }
 
 size_t prune_ws(int64_t N, int H, int d, int topk) {
@@ -443,7 +453,9 @@ void prune_setup(ScanArgs& a, int d, char* w) {
   a.qb_cnt = reinterpret_cast<int32_t*>(w);
   w += z.cnt;
   a.range_cnt = reinterpret_cast<int32_t*>(w);
-  w += z.rcnt;
+  w += z.rcnt / 2;
+  a.range_stream = reinterpret_cast<int32_t*>(w);
+  w += z.rcnt / 2;
   a.heavy_list = reinterpret_cast<int32_t*>(w);
   w += align256((size_t)z.heavy_max * 4);
   a.heavy_cnt = reinterpret_cast<int32_t*>(w);
@@ -453,6 +465,7 @@ void prune_setup(ScanArgs& a, int d, char* w) {
   a.nkb = z.nkb;
   a.ngr = z.ngr;
   a.live_rows = z.live_rows;
+  a.live_shift = z.live_shift;
   a.nrange = z.nrange;
 }
 

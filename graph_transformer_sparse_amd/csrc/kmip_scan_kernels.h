@@ -169,16 +169,10 @@ __device__ __forceinline__ bool quarter_hit(const floatx16_t& x, int qq, float t
   return (x[4 * qq] > t) | (x[4 * qq + 1] > t) | (x[4 * qq + 2] > t) | (x[4 * qq + 3] > t);
 }
 
-// Pruned selection: the range of query blocks that wid belongs to has on
-// average at least half of the key blocks live, or more heavy query blocks
-// than the pruned pass holds, so the streaming pass takes it (the counts are
-// complete once the range's bound pass has run).
-__device__ __forceinline__ bool prune_range_dense(const ScanArgs& a, int64_t wid) {
-  const int64_t r = wid / a.live_rows;
-  const int64_t r0 = r * a.live_rows;
-  const int64_t total = (int64_t)a.H * a.nkb;
-  const int64_t rows = total - r0 < a.live_rows ? total - r0 : a.live_rows;
-  return 2 * (int64_t)a.range_cnt[r] >= rows * a.nkb || a.heavy_cnt[r] > a.heavy_max;
+// Pruned selection: the streaming pass takes the range of query blocks
+// that wid belongs to (decided once the range's bound pass has run).
+__device__ __forceinline__ bool prune_range_stream(const ScanArgs& a, int64_t wid) {
+  return a.range_stream[(int)wid >> a.live_shift] != 0;
 }
 
 struct SubTile {
@@ -306,11 +300,11 @@ struct Scanner {
       const int64_t r = qrow[0] * H + t.h;
       keep[0] = qvalid[0] && (a.cand_cnt[2 * r] > a.cap || a.cand_cnt[2 * r + 1] > a.cap);
       wave_rows = __ballot(keep[0]) != 0ull;
-    } else if constexpr (MODE == M_SELECT) {
+    } else if constexpr (MODE == M_SELECT && (D == 32 || D == 64)) {
       static_assert(QB == 1, "one query block per wavefront");
-      if (a.range_cnt != nullptr) {
+      if (a.range_stream != nullptr) {
         filtered = true;
-        wave_rows = bact[0] && prune_range_dense(a, t.h * a.nkb + t.q0 / 32 + wave);
+        wave_rows = bact[0] && prune_range_stream(a, t.h * a.nkb + t.q0 / 32 + wave);
         keep[0] = keep[0] && wave_rows;
       }
     }
@@ -936,12 +930,14 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
   } else {
     ScanArgs b = a;
     b.cand_cnt = nullptr;
-    b.range_cnt = nullptr;                     // SELECT writes every row...
+    b.range_stream = nullptr;                  // SELECT writes every row...
     if constexpr (D == 32 || D == 64) {
       if (a.kop != nullptr) {                  // ...but those of the pruned pass
-        e = launch_prune<D, KP>(a, s);
+        // short lists run the pruned pass with 8-entry lists (sentinels fill
+        // the rest): 5-entry instantiations compile to far more registers
+        e = launch_prune<D, (KP < 8 ? 8 : KP)>(a, s);
         if (e != hipSuccess) return e;
-        b.range_cnt = a.range_cnt;
+        b.range_stream = a.range_stream;
       }
     }
     return launch_pass<D, KP, M_SELECT>(b, s);

@@ -87,16 +87,20 @@ def test_workspace_sizes_are_linear_in_n():
     # The pruned selection adds per row a copy of its key (2d bytes), a
     # share of its block's bound row (d/8 bytes) and of its block's count,
     # plus the live words of one range of query blocks (ceil(N/1024) words
-    # per block of 32 rows, at most 16 MiB) and the part lists of up to 4096
-    # heavy query blocks (128 MiB).
+    # per block of 32 rows, at most 16 MiB) and the part lists of up to 8192
+    # heavy query blocks (256 MiB).
     rows = 100000 * 4
     per_row = 10 + 64 + 4
-    live1 = 4 * 3125 * 98 * 4
-    parts = 4096 * 8 * 32 * 16 * 8                      # heavy query blocks' part lists
+    live1 = 12500 * 98 * 4                              # one range of all query blocks
+    parts = 8192 * 8 * 32 * 16 * 8                      # heavy query blocks' part lists
     assert rows * per_row + live1 + parts <= f(100000, 4, 32, 15, 0) <= rows * per_row + live1 + parts + (4 << 20)
-    grow = f(200000, 4, 32, 15, 0) - f(100000, 4, 32, 15, 0)   # linear in N but the live words
-    assert rows * per_row <= grow <= rows * per_row + rows * 3 // 2 + (16 << 20) - live1 + (64 << 10)
+    # linear in N but the live words (at most 16 MiB)
+    grow = f(200000, 4, 32, 15, 0) - f(100000, 4, 32, 15, 0)
+    assert rows * per_row - live1 <= grow <= rows * per_row + rows * 3 // 2 + (16 << 20) + (64 << 10)
     assert f(500000, 4, 32, 15, 0) <= 2000000 * (per_row + 2) + (16 << 20) + parts + (4 << 20)
+    for (N, H, d) in [(100000, 4, 32), (200000, 4, 32), (500000, 4, 32), (8192, 4, 64)]:
+        without = f(N, H, d, 15, 0) - _pruned_bytes(N, H, d)
+        assert 10 * N * H <= without <= 12 * N * H + (1 << 20)
     # without the pruned pass (lists longer than 16): the first three terms only
     assert rows * 10 <= f(100000, 4, 32, 45, 0) - 2 * 128 * rows * 8 - rows * 8 <= rows * 10 + (4 << 20)
     assert f(100000, 4, 32, 15, 64) > rows * 4                # thresholds plus the tile plan
@@ -132,16 +136,22 @@ def test_backward_f32_rejects():
 
 def _pruned_bytes(N, H, d):
     """Buffers of the pruned selection (one graph with a query order, bf16
-    rows of 32 or 64, lists of at most 16)."""
+    rows of 32 or 64, lists of at most 16, 2^16 <= N <= 2^19)."""
+    if not (1 << 16) <= N <= (1 << 19):
+        return 0
     a = lambda x: (x + 255) // 256 * 256
     nkb = -(-N // 32)
     ngr = -(-nkb // 32)
     rows = H * nkb
-    live_rows = min(rows, max(16, (16 << 20) // (ngr * 4) // 16 * 16))
-    nrange = -(-rows // live_rows)
-    heavy = min(live_rows, 4096)
-    return (a(rows * (d // 16) * 1024) + a(H * ngr * (d // 8) * 1024) + a(live_rows * ngr * 4)
-            + a(rows * 4) + 2 * a(nrange * 4) + a(heavy * 4) + a(heavy * 8 * 32 * 16 * 8))
+    fit = (16 << 20) // (ngr * 4)
+    shift = 4
+    while (2 << shift) <= fit and (1 << shift) < rows:
+        shift += 1
+    held = min(rows, 1 << shift)
+    nrange = -(-rows // (1 << shift))
+    heavy = min(held, 8192)
+    return (a(rows * (d // 16) * 1024) + a(H * ngr * (d // 8) * 1024) + a(held * ngr * 4)
+            + a(rows * 4) + 3 * a(nrange * 4) + a(heavy * 4) + a(heavy * 8 * 32 * 16 * 8))
 
 
 def test_f32_workspace_adds_split_rows():

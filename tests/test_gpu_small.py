@@ -226,6 +226,13 @@ def test_deterministic_repeat_query_order(topk):
     _repeat(small_case(12288, 4, 32, topk, law="clustered", clusters=24, seed=55 + topk))
 
 
+def test_deterministic_repeat_pruned():
+    """2^16 nodes: the pruned selection, whose heavy query blocks are listed
+    through an atomic counter (their order, and where their parts' lists
+    go, change between calls); results must not."""
+    _repeat(small_case(65536, 2, 32, 15, law="clustered", clusters=64, seed=57))
+
+
 def test_deterministic_repeat_batched():
     """Batched graphs: the ragged tile plan and 8-wavefront sub-tiles."""
     sizes = list(np.random.default_rng(56).integers(1, 2600, 23))
@@ -244,29 +251,38 @@ def test_gradient_identities_on_gpu_outputs():
         assert np.abs(dk[lo:hi].sum(0)).max() <= 1e-3 * np.abs(dk[lo:hi]).sum(0).max() + 1e-5
 
 
+def _sample(n, m, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=m, replace=False)]))
+
+
 def test_exact_ties_on_the_pruned_path():
-    """One graph with a query order (N*H >= 32768), so the selection scores
-    the live key blocks of each query block in the query order, out of node
-    order: 97 distinct key rows, each repeated ~340 times, give bitwise-equal
-    scores, and the smaller node id must still win every tie."""
+    """One graph of 2^16 nodes (the pruned selection: keys scored in the
+    query order, out of node order): 97 distinct key rows, each repeated
+    ~676 times, give bitwise-equal scores, and the smaller node id must still
+    win every tie, in the oracle's order, on 4096 sampled rows."""
     from tests.gpu_util import np_, run_forward
-    w = small_case(8192, 4, 32, 15, law="clustered", clusters=48, seed=131)
-    w.k = w.k[np.arange(8192) % 97]
+    from tests.parity import oracle_forward
+    n = 65536
+    w = small_case(n, 1, 32, 15, law="clustered", clusters=48, seed=131, backward=False)
+    w.k = w.k[np.arange(n) % 97]
     print(f"[case] ties n={w.n} H={w.heads} d={w.d} k={w.topk}", flush=True)
     t, out, idx, score = run_forward(w)
     q, k, v = decode(w)
-    fw = orc.kmip_forward(q, k, v, None, w.topk)
-    assert np.array_equal(np_(idx), fw["idx"].astype(np.int32))
+    rows = _sample(n, 4096, 5)
+    ref = oracle_forward(q, k, v, None, w.topk, rows)
+    assert np.array_equal(np_(idx)[rows], ref["idx"].astype(np.int32))
 
 
 @pytest.mark.parametrize("d", [32, 64])
 def test_pruned_and_streaming_query_blocks_mixed(d):
-    """Half of the nodes in tight clusters, half i.i.d.: the clustered query
-    blocks take the pruned selection, the i.i.d. ones (whose bounds leave most
-    key blocks live) the streaming pass; every row against the oracle,
-    forward and backward."""
+    """One graph of 2^16 nodes, half of them in tight clusters, half i.i.d.:
+    the clustered query blocks' key blocks are mostly ruled out by their
+    bounds, the i.i.d. ones (whose bounds leave most key blocks live) become
+    heavy blocks split over several wavefronts; 4096 sampled rows against the
+    oracle, forward and backward."""
     from workloads import f32_to_bf16_bits
-    n, heads = 16384, 2
+    n, heads = 65536, 1
     w = small_case(n, heads, d, 8, law="clustered", clusters=32, seed=171 + d)
     rng = np.random.default_rng(5 + d)
     half = n // 2
@@ -274,6 +290,21 @@ def test_pruned_and_streaming_query_blocks_mixed(d):
         x = getattr(w, name).copy()
         x[half:] = f32_to_bf16_bits(rng.standard_normal((n - half, heads, d), dtype=np.float32) * 1.4)
         setattr(w, name, x)
-    t, out, idx, score, st = _forward_check(w)
-    assert st["rows"] == n * heads
-    _backward_check(w, t, idx, score)
+    rows = _sample(n, 4096, 7 + d)
+    t, out, idx, score, st = _forward_check(w, rows=rows)
+    assert st["rows"] == rows.size * heads
+    from tests.gpu_util import np_, run_backward
+    dq, dk, dv = run_backward(w, t, idx, score)
+    q, k, v = decode(w)
+    rq, _, _ = orc.kmip_backward_on_sets(q, k, v, np_(idx)[rows].astype(np.int64),
+                                         w.dout.astype(np.float64), rows=rows)
+    assert_rows_close(np_(dq)[rows], rq, "dq")
+
+
+def test_pruned_path_streams_inputs_without_cluster_structure():
+    """One graph of 2^16 i.i.d. nodes: nearly every key block stays live, so
+    the range goes to the streaming pass; 2048 sampled rows against the
+    oracle."""
+    w = small_case(65536, 1, 32, 15, law="iid", seed=191, backward=False)
+    rows = _sample(65536, 2048, 9)
+    _forward_check(w, rows=rows)

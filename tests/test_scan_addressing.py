@@ -185,11 +185,16 @@ PR_WAVES, PS_WAVES, PR_MAX_WORDS, PR_LPW, PR_NBUF, PS_NPF = 16, 4, 512, 2, 3, 4
 
 
 def pruned_sizes(N, H, D):
+    """(nkb, ngr, live_rows): ranges of 2^s query blocks (s >= 4), as many
+    as 16 MiB of live words hold."""
     nkb = -(-N // 32)
     ngr = -(-nkb // 32)
     rows = H * nkb
-    live_rows = min(rows, max(16, (16 << 20) // (ngr * 4) // 16 * 16))
-    return nkb, ngr, live_rows
+    fit = (16 << 20) // (ngr * 4)
+    shift = 4
+    while (2 << shift) <= fit and (1 << shift) < rows:
+        shift += 1
+    return nkb, ngr, 1 << shift
 
 
 def check_pruned(N, H, D, nwg=256):
@@ -242,7 +247,7 @@ def check_pruned(N, H, D, nwg=256):
                     wid = b + w
                     assert wid not in seen and r0 <= wid < r1
                     seen.add(wid)
-                    assert (wid - r0) * ngr + ngr - 1 < live_rows * ngr
+                    assert (wid - r0) * ngr + ngr - 1 < min(live_rows, total) * ngr
                     assert wid < total and wid // live_rows < nrange
                 b += n
         assert len(seen) == r1 - r0
@@ -290,7 +295,7 @@ def check_pruned(N, H, D, nwg=256):
                                    (500000, 4, 32), (524288, 4, 64), (9000, 4, 32)])
 def test_pruned_selection_indices_stay_in_bounds(N, H, D):
     nkb, ngr, live_rows = check_pruned(N, H, D)
-    assert live_rows * ngr * 4 <= 16 << 20
+    assert min(live_rows, H * nkb) * ngr * 4 <= 16 << 20
 
 
 @pytest.mark.parametrize("N,H", [(100000, 4), (500000, 4), (8192, 4), (40000, 1)])
@@ -300,9 +305,9 @@ def test_heavy_parts_and_merge_stay_in_bounds(N, H):
     PARTS + p writes entries ((t 32 + q) 16 + r), r < topk <= 16, and the
     merge reads entries ((i PARTS 32 + q) 16) + p 32 16 + at, at < topk; the
     parts' words p, p + PARTS, ... cover each word once."""
-    PARTS, HMAX = 8, 4096
+    PARTS, HMAX = 8, 8192
     nkb, ngr, live_rows = pruned_sizes(N, H, 32)
-    heavy_max = min(live_rows, HMAX)
+    heavy_max = min(live_rows, H * nkb, HMAX)
     size = heavy_max * PARTS * 32 * 16
     i, q, p, r = heavy_max - 1, 31, PARTS - 1, 15
     t = i * PARTS + p

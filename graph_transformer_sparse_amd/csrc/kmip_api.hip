@@ -115,7 +115,8 @@ kmip_status_t score_topk_core(const uint16_t* q, const uint16_t* k, int64_t N, i
     a.tiles = tiles;
   } else if (use_query_order(N, H)) {
     int32_t* perm = nullptr;
-    st = launch_status(launch_query_order(a.q, N, H, d_rows, w, &perm, s));
+    st = launch_status(launch_query_order(a.q, N, H, d_rows, w, &perm, s, &a.order_counts,
+                                          &a.npiv));
     if (st != KMIP_OK) return st;
     a.perm = perm;
     w += query_order_bytes(N, H);

@@ -92,8 +92,21 @@ struct ScanArgs {
   int rank0;
   // Pruned selection (one graph with a query order, rows of 32 or 64 bf16,
   // lists of at most 16; kop == nullptr: off).  Keys are taken in the query
-  // order, in 32-key blocks (nkb per head, padded to ngr groups of 32):
-  //   kop  [H][nkb][D/16][64][8]  the block's keys in MFMA operand order;
+  // order, in 32-key blocks.  Every pivot group of the order starts a new
+  // key block (its last block padded with empty slots), so the keys of a
+  // block belong to one group and its bound is tight; nkp = nkb + npiv
+  // blocks per head are allocated (padded to ngr groups of 32), nkp_h[h] of
+  // them used:
+  //   gstart, gsize, pstart [H][npiv]  per group (pivot rank r) its first
+  //                               position in the head's order, its size,
+  //                               and its first padded key slot (a multiple
+  //                               of 32);
+  //   bgroup [H][nkp]             the group of padded key block b (-1 past
+  //                               nkp_h[h]);
+  //   kid  [H][nkp][32]           node id of each padded key slot (-1: an
+  //                               empty slot);
+  //   kop  [H][nkp][D/16][64][8]  the block's keys in MFMA operand order
+  //                               (zero rows in empty slots);
   //   bop  [H][ngr][D/8][64][8]   per block a bound row [mid | rad], D + D
   //                               elements, in operand order (see
   //                               key_pack_kernel);
@@ -114,6 +127,14 @@ struct ScanArgs {
   // PRUNE_STREAM_DEN of the key blocks live (inputs without enough cluster
   // structure) is left to the streaming selection pass; the pruned pass
   // takes the others.
+  const int32_t* order_counts;   // [H][npiv][copies] group sizes from the order
+  int npiv;
+  int32_t* gstart;
+  int32_t* gsize;
+  int32_t* pstart;
+  int32_t* bgroup;
+  int32_t* nkp_h;
+  int32_t* kid;
   uint16_t* kop;
   uint16_t* bop;
   uint32_t* live;
@@ -124,7 +145,7 @@ struct ScanArgs {
   int32_t* heavy_cnt;
   uint2* heavy_parts;
   int heavy_max;
-  int64_t nkb, ngr, wid0, wid1, live_rows, nrange;
+  int64_t nkb, nkp, ngr, wid0, wid1, live_rows, nrange;
   int live_shift;
 };
 hipError_t launch_score_topk(const ScanArgs& args, int d, hipStream_t s);
@@ -137,6 +158,8 @@ constexpr int64_t PRUNE_LIVE_BYTES = (int64_t)16 << 20;
 constexpr int PRUNE_HEAVY_MAX = 8192;
 constexpr int PRUNE_HEAVY_PARTS = 8;
 constexpr int PRUNE_STREAM_NUM = 1, PRUNE_STREAM_DEN = 4;
+// Live words (32 key blocks each) per query block the bound pass holds.
+constexpr int PRUNE_MAX_WORDS = 704;
 bool prune_applies(int64_t N, int H, int d, int topk);
 size_t prune_ws(int64_t N, int H, int d, int topk);
 // Carves the pruned-selection buffers out of w (prune_ws bytes) into a.
@@ -151,9 +174,13 @@ hipError_t launch_scan_d192(int kp, const ScanArgs& a, hipStream_t s);
 // Query order for one graph: groups each head's queries by their nearest
 // pivot query (largest inner product).  Workspace: query_order_bytes(N, H); *perm points
 // into it ([H][N] node ids).
+// *counts (if not null) points at the per-(head, pivot rank, copy) group
+// counts [H][npiv][ORDER_COPIES] and *npiv receives the pivots per head.
 size_t query_order_bytes(int64_t N, int H);
 hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* ws,
-                              int32_t** perm, hipStream_t s);
+                              int32_t** perm, hipStream_t s, const int32_t** counts = nullptr,
+                              int* npiv = nullptr);
+constexpr int ORDER_COPIES = 16;
 
 // Split-precision rows for the fp32 entry points: per (node, head) row of d
 // fp32 elements x = hi + lo + r (hi = bf16(x), lo = bf16(x - hi)),

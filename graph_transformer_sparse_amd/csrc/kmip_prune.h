@@ -10,8 +10,14 @@
 // order point the same way, and one bound per (query, block)
 //   q . k  <=  q . mid + |q| . rad         (|k_c - mid_c| <= rad_c)
 // rules most blocks out for a wavefront's 32 queries (which sit next to
-// each other in the same order).  Three kernels:
+// each other in the same order).  A block never straddles two groups (the
+// last block of a group is padded with empty slots): a block holding the
+// tail of one group and the head of the next has a wide box, and on the
+// clustered inputs that padding halves the live blocks.  Kernels:
 //
+//   group_layout_kernel  per pivot group of the order its size, first
+//                      position and first key slot, every group starting a
+//                      new 32-key block;
 //   key_pack_kernel    keys of each head in query order, per 32-key block in
 //                      MFMA operand order, and the block's bound row
 //                      [mid | rad] (rad widened to cover fp32 rounding);
@@ -41,7 +47,7 @@
 constexpr int PR_WAVES = 16;              // bound pass: wavefronts per workgroup
 constexpr int PS_WAVES = 4;               // pruned selection: wavefronts per workgroup
 constexpr float PR_PAD = 0x1p-13f;        // rad widening relative to the block's max |k|
-constexpr int PR_MAX_WORDS = 512;         // live words per query block: N <= 2^19
+constexpr int PR_MAX_WORDS = PRUNE_MAX_WORDS;  // live words per query block
 constexpr int PR_LPW = 2;                 // bound pass: operand pieces per wavefront per batch
 constexpr int PR_NBUF = 3;                // bound pass: ring slots
 constexpr int PS_NPF = 4;                 // pruned selection: key blocks in flight per wavefront
@@ -58,12 +64,67 @@ __device__ __forceinline__ uint32_t bf16_bits_up(float x) {
   return (t == u ? t : t + 0x10000u) >> 16;
 }
 
-// One wavefront per key block b of head blockIdx.y (blocks past the last
-// key, up to the group multiple, get zero bound rows).  Lane l holds row
-// l % 32 of the block (position 32 b + l % 32 of the query order) and, for
-// K-slice m, its elements 8 (2m + l / 32) .. + 7: exactly the A operand
-// lane l supplies for that slice.
-//   kop[((h nkb + b) NM + m) 512 + 8 l + e]
+// Per head (one workgroup): each group's size (the sum of its copies'
+// counts), first position in the head's order (exclusive scan of the sizes)
+// and first padded key slot (exclusive scan of the sizes rounded up to 32),
+// then the group of every padded key block (-1 past the head's last).
+constexpr int GL_THREADS = 1024;
+__global__ __launch_bounds__(GL_THREADS) void group_layout_kernel(ScanArgs a) {
+  __shared__ int s0[GL_THREADS], s1[GL_THREADS];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int npiv = a.npiv;
+  const int per = (npiv + GL_THREADS - 1) / GL_THREADS;
+  const int r0 = t * per < npiv ? t * per : npiv;
+  const int r1 = r0 + per < npiv ? r0 + per : npiv;
+  const int32_t* cnt = a.order_counts + (int64_t)h * npiv * ORDER_COPIES;
+  auto gsz = [&](int r) __attribute__((always_inline)) {
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < ORDER_COPIES; ++c) n += cnt[r * ORDER_COPIES + c];
+    return n;
+  };
+  int sz = 0, pz = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int n = gsz(r);
+    sz += n;
+    pz += (n + 31) & ~31;
+  }
+  s0[t] = sz;
+  s1[t] = pz;
+  __syncthreads();
+  for (int o = 1; o < GL_THREADS; o <<= 1) {       // inclusive scans
+    const int x0 = t >= o ? s0[t - o] : 0, x1 = t >= o ? s1[t - o] : 0;
+    __syncthreads();
+    s0[t] += x0;
+    s1[t] += x1;
+    __syncthreads();
+  }
+  int g = s0[t] - sz, p = s1[t] - pz;
+  const int64_t gb = (int64_t)h * npiv;
+  int32_t* bg = a.bgroup + (int64_t)h * a.nkp;
+  for (int r = r0; r < r1; ++r) {
+    const int n = gsz(r);
+    a.gstart[gb + r] = g;
+    a.gsize[gb + r] = n;
+    a.pstart[gb + r] = p;
+    const int pn = (n + 31) & ~31;
+    for (int b = p >> 5; b < (p + pn) >> 5; ++b) bg[b] = r;
+    g += n;
+    p += pn;
+  }
+  const int nkph = s1[GL_THREADS - 1] >> 5;
+  if (t == 0) a.nkp_h[h] = nkph;
+  for (int64_t b = nkph + t; b < a.nkp; b += GL_THREADS) bg[b] = -1;
+}
+
+// One wavefront per padded key block b of head blockIdx.y (blocks past the
+// head's last, up to the group multiple, get zero bound rows).  Lane l holds
+// slot l % 32 of the block (position pstart + 32 b + l % 32 - pstart[r] of
+// the order, r the block's group, while inside the group; an empty slot
+// otherwise) and, for K-slice m, its elements 8 (2m + l / 32) .. + 7:
+// exactly the A operand lane l supplies for that slice.
+//   kop[((h nkp + b) NM + m) 512 + 8 l + e]
+//   kid[(h nkp + b) 32 + l]                           for l < 32
 //   bop[((h ngr + g) 2NM + m') 512 + 8 (r + 32 s) + e]   for block 32 g + r:
 //       slices m' < NM hold mid, NM + m' rad, element 16 m' + 8 s + e.
 template <int D>
@@ -80,22 +141,26 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
   const int64_t g = b / 32;
   const int br = (int)(b % 32);
   uint16_t* bo = a.bop + (((int64_t)h * a.ngr + g) * (2 * NM)) * 512 + (br + 32 * lhalf) * 8;
-  if (b >= a.nkb) {
+  const int r = b < a.nkp ? a.bgroup[(int64_t)h * a.nkp + b] : -1;
+  if (r < 0) {
     if (lrow == 0) {
 #pragma unroll
       for (int m = 0; m < 2 * NM; ++m) *reinterpret_cast<uint4*>(bo + m * 512) = uint4{0, 0, 0, 0};
     }
     return;
   }
-  const int64_t pos = b * 32 + lrow;
-  const bool valid = pos < N;
-  const int64_t node = a.perm[(int64_t)h * N + (valid ? pos : N - 1)];
+  const int64_t gr = (int64_t)h * a.npiv + r;
+  const int o = (int)(b * 32 + lrow) - a.pstart[gr];
+  const bool valid = o < a.gsize[gr];
+  const int64_t pos = a.gstart[gr] + (valid ? o : 0);
+  const int64_t node = a.perm[(int64_t)h * N + pos];
+  if (lhalf == 0) a.kid[((int64_t)h * a.nkp + b) * 32 + lrow] = valid ? (int32_t)node : -1;
   const uint16_t* src = a.k + (node * H + h) * D + 8 * lhalf;
   uint4 v[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
     v[m] = valid ? *reinterpret_cast<const uint4*>(src + 16 * m) : uint4{0, 0, 0, 0};
-  uint16_t* ko = a.kop + (((int64_t)h * a.nkb + b) * NM) * 512 + lane * 8;
+  uint16_t* ko = a.kop + (((int64_t)h * a.nkp + b) * NM) * 512 + lane * 8;
 #pragma unroll
   for (int m = 0; m < NM; ++m) *reinterpret_cast<uint4*>(ko + m * 512) = v[m];
 
@@ -212,6 +277,7 @@ __global__ __launch_bounds__(PR_WAVES * 64) void bound_live_kernel(ScanArgs a, i
     int64_t n = (rem + nst - 1) / nst;
     n = n < nkb - nb0 ? n : nkb - nb0;
     const int64_t wid = b + wave;
+    const int64_t nkph = a.nkp_h[h];
     b += n;
     __syncthreads();                        // the previous sub-tile is done with the ring
     const bool active = wave < n;
@@ -276,8 +342,8 @@ __global__ __launch_bounds__(PR_WAVES * 64) void bound_live_kernel(ScanArgs a, i
 #pragma unroll
           for (int r = 0; r < 16; ++r) any |= __ballot(ab[u][r] > tq[r]);
           uint32_t mask = (uint32_t)any | (uint32_t)(any >> 32);
-          const int64_t nv = nkb - gu * 32;
-          if (nv < 32) mask &= (1u << nv) - 1u;
+          const int64_t nv = nkph - gu * 32;
+          mask = nv <= 0 ? 0u : nv < 32 ? mask & ((1u << nv) - 1u) : mask;
           cnt += __builtin_popcount(mask);
           if ((int)(gu & 63) == lane) wacc = mask;
           if ((gu & 63) == 63 || gu == ngr - 1) {
@@ -413,7 +479,9 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
   const uint32_t* lw = a.live + (wid - a.wid0) * ngr;
   const int ngr32 = (int)ngr;
   const int nmine = ngr32 > start ? (ngr32 - start + stride - 1) / stride : 0;
-  const int own = (int)((wid % nkb) >> 5);
+  // the word of the padded key block nearest the query block's positions
+  const int64_t nkph = a.nkp_h[h];
+  const int own = (int)(((wid % nkb) * nkph / nkb) >> 5);
   int jfirst = own > start ? (own - start + stride - 1) / stride : 0;
   jfirst = jfirst < nmine ? jfirst : 0;
   auto word_of = [&](int j) __attribute__((always_inline)) {
@@ -446,17 +514,15 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
 
   // Per wavefront: one base for the head's key copy and one for its key
   // ids; each load's block is a 32-bit lane offset.
-  const uint16_t* kbase = a.kop + (int64_t)h * nkb * NM * 512;
-  const int32_t* pb = a.perm + (int64_t)h * N;
+  const uint16_t* kbase = a.kop + (int64_t)h * a.nkp * NM * 512;
+  const int32_t* pb = a.kid + (int64_t)h * a.nkp * 32;
   const unsigned wring_lds =
       (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)wring;
-  const int last = (int)nkb - 1;
-  const int nlast = (int)(N - (int64_t)last * 32);     // keys in the last block
-  const int nm1 = (int)(N - 1);
   // Block b into ring slot i (an exhausted slot loads block 0, never scored,
   // so every fill is LPB loads): slice m from the operand-order copy (lane
-  // l's 16 bytes at l * 16), then the ids of rows 0..31 (lanes 32..63 repeat
-  // them; rows past the last key repeat it, and are never appended).
+  // l's 16 bytes at l * 16), then the ids of slots 0..31 (lanes 32..63
+  // repeat them; empty slots hold -1 and zero keys, and are never
+  // appended).
   auto fill = [&](int i, int bq) __attribute__((always_inline)) {
     const unsigned bb = bq < 0 ? 0u : (unsigned)bq;
     const unsigned sl = wring_lds + (unsigned)(i * SLOT);
@@ -467,8 +533,7 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
                    "s"(kbase), "{m0}"(__builtin_amdgcn_readfirstlane(sl + (unsigned)(m * 1024)))
                    : "memory");
     }
-    const int p = (int)(bb * 32u) + lrow;
-    asm volatile("global_load_lds_dword %0, %1" ::"v"((unsigned)(p < nm1 ? p : nm1) * 4u),
+    asm volatile("global_load_lds_dword %0, %1" ::"v"((bb * 32u + (unsigned)lrow) * 4u),
                  "s"(pb), "{m0}"(__builtin_amdgcn_readfirstlane(sl + (unsigned)(NM * 1024)))
                  : "memory");
   };
@@ -500,10 +565,10 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           *reinterpret_cast<const bf16x8_t*>(sl + m * 1024 + lane * 16), qb[m], s, 0, 0, 0);
     // s[r]: key row 8 (r / 4) + 4 lhalf + r % 4 of the block, query lrow.
-    // Rows past the last key (zero rows of the copy) may pass this test;
-    // they are never appended.
+    // Empty slots (zero rows of the copy) may pass this test; they are never
+    // appended.
+    (void)bb;
     if (__ballot(block_max(s) > thr) == 0ull) return;
-    const int nrow = bb == last ? nlast : 32;
     const int32_t* ids = reinterpret_cast<const int32_t*>(sl + NM * 1024);
     bool gq[4];
 #pragma unroll
@@ -524,7 +589,7 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
           for (int r = 0; r < 4; ++r) {
             const float sv = s[4 * qq + r];
             cb[cnt * 64] = make_uint2(__float_as_uint(sv), (unsigned)idv[r]);
-            cnt += (sv > thr) & (8 * qq + 4 * lhalf + r < nrow) ? 1 : 0;
+            cnt += ((sv > thr) & (idv[r] >= 0)) ? 1 : 0;
           }
         }
       }
@@ -698,52 +763,56 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
   }
 }
 
-// One workgroup per heavy block (persistent over heavy_cnt): its part lists
-// (PH_PARTS x 32 queries x 16 entries) are copied to LDS with coalesced
-// loads, then one thread per query merges its PH_PARTS lists into the
-// query's top-k and writes the outputs.
+// One thread per (heavy block, query), eight heavy blocks per workgroup
+// (persistent over heavy_cnt): the heads of the query's PH_PARTS lists sit in
+// registers, and after each output entry only the list that supplied it is
+// read again, so the merge is PH_PARTS - 1 compares per entry.
 template <int KP>
 __global__ __launch_bounds__(256) void pruned_merge_kernel(ScanArgs a) {
-  constexpr int E = PH_PARTS * 32 * 16;
-  __shared__ uint2 sl[E];
+  constexpr int LS = 32 * 16;                          // entries between parts
   if (prune_range_stream(a, a.wid0)) return;
   const int nh0 = a.heavy_cnt[(int)a.wid0 >> a.live_shift];
   const int nh = nh0 < a.heavy_max ? nh0 : a.heavy_max;
   const int topk = a.topk;
   const int H = a.H;
-  for (int hi = blockIdx.x; hi < nh; hi += gridDim.x) {
-    __syncthreads();                                   // the previous block's lists are read
-    const uint2* src = a.heavy_parts + (int64_t)hi * E;
-    for (int e = threadIdx.x; e < E; e += 256) sl[e] = src[e];
-    __syncthreads();
-    const int q = threadIdx.x;
+  const int q = threadIdx.x & 31;
+  const uint2 none = make_uint2(__float_as_uint(-kInf), 0xffffffffu);
+  for (int hi = blockIdx.x * 8 + (int)(threadIdx.x >> 5); hi < nh; hi += gridDim.x * 8) {
     const int64_t wid = a.heavy_list[hi];
     const int h = (int)(wid / a.nkb);
     const int64_t pos = (wid % a.nkb) * 32 + q;
-    if (q >= 32 || pos >= a.N) continue;
+    if (pos >= a.N) continue;
+    const uint2* src = a.heavy_parts + ((int64_t)hi * PH_PARTS * 32 + q) * 16;
+    uint2 cur[PH_PARTS];
     int at[PH_PARTS];
 #pragma unroll
-    for (int p = 0; p < PH_PARTS; ++p) at[p] = 0;
+    for (int p = 0; p < PH_PARTS; ++p) {
+      at[p] = 0;
+      cur[p] = src[p * LS];                            // topk >= 1: entry 0 exists
+    }
     const int64_t row = a.perm[(int64_t)h * a.N + pos];
     int32_t* oi = a.idx + (row * H + h) * topk;
     float* os = a.score + (row * H + h) * topk;
     for (int r = 0; r < topk; ++r) {
       int best = 0;
-      uint2 e = at[0] < topk ? sl[q * 16 + at[0]] : make_uint2(__float_as_uint(-kInf), 0xffffffffu);
+      uint2 e = cur[0];
 #pragma unroll
       for (int p = 1; p < PH_PARTS; ++p) {
-        const uint2 c = at[p] < topk ? sl[(p * 32 + q) * 16 + at[p]]
-                                     : make_uint2(__float_as_uint(-kInf), 0xffffffffu);
-        if (prune_before(c, e)) {
-          e = c;
+        if (prune_before(cur[p], e)) {
+          e = cur[p];
           best = p;
         }
       }
-#pragma unroll
-      for (int p = 0; p < PH_PARTS; ++p) at[p] += p == best ? 1 : 0;
       const int jj = (int)e.y;
       oi[r] = jj;
       os[r] = jj < 0 ? -kInf : __uint_as_float(e.x);
+#pragma unroll
+      for (int p = 0; p < PH_PARTS; ++p) {
+        if (p == best) {
+          ++at[p];
+          cur[p] = at[p] < topk ? src[p * LS + at[p]] : none;
+        }
+      }
     }
   }
 }
@@ -757,12 +826,13 @@ __global__ void prune_decide_kernel(ScanArgs a) {
   a.range_stream[r] = (int64_t)a.range_cnt[r] * PRUNE_STREAM_DEN >= rows * a.nkb * PRUNE_STREAM_NUM;
 }
 
-// Key copy and bound rows, then per range of query blocks the bound pass and
+// Group layout, key copy and bound rows, then per range of query blocks the bound pass and
 // the pruned selection: light query blocks, the parts of heavy ones, their
 // merge.  range_cnt / heavy_cnt then tell the streaming pass which ranges are
 // its own.
 template <int D, int KP>
 hipError_t launch_prune(const ScanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(group_layout_kernel, dim3((unsigned)a.H), dim3(GL_THREADS), 0, s, a);
   hipLaunchKernelGGL(key_pack_kernel<D>, dim3((unsigned)ceil_div(a.ngr * 32, 4), (unsigned)a.H),
                      dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
@@ -791,7 +861,8 @@ hipError_t launch_prune(const ScanArgs& a, hipStream_t s) {
                        dim3(PS_WAVES * 64), 0, s, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pruned_merge_kernel<KP>, dim3(1024), dim3(256), 0, s, b);
+    hipLaunchKernelGGL(pruned_merge_kernel<KP>,
+                       dim3((unsigned)ceil_div((int64_t)a.heavy_max, 8)), dim3(256), 0, s, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -83,7 +83,6 @@ constexpr int ORDER_WAVES = 8;                    // wavefronts per workgroup
 constexpr int ORDER_QB = 2;                       // blocks of 32 queries per wavefront
 // Each (head, pivot) count is split over ORDER_COPIES counters picked by the
 // node id, which keeps atomic contention low when many queries share a pivot.
-constexpr int ORDER_COPIES = 16;
 
 __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -339,7 +338,8 @@ size_t query_order_bytes(int64_t N, int H) {
 }
 
 hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* ws,
-                              int32_t** perm_out, hipStream_t s) {
+                              int32_t** perm_out, hipStream_t s, const int32_t** counts_out,
+                              int* npiv_out) {
   const int npiv = order_pivots(N);
   const int64_t nb = (int64_t)H * npiv * ORDER_COPIES;
   char* p = static_cast<char*>(ws);
@@ -389,6 +389,8 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
   hipLaunchKernelGGL(order_place_kernel, dim3(rows), dim3(256), 0, s, codes, N, H, npiv,
                      cursor, perm);
   *perm_out = perm;
+  if (counts_out != nullptr) *counts_out = counts;
+  if (npiv_out != nullptr) *npiv_out = npiv;
   return hipGetLastError();
 }
 
@@ -396,14 +398,17 @@ hipError_t launch_query_order(const uint16_t* q, int64_t N, int H, int d, void* 
 // query blocks are kept at a time: PRUNE_LIVE_BYTES bound them whatever N is.
 namespace {
 struct PruneSizes {
-  int64_t nkb, ngr, live_rows, nrange, heavy_max;
-  int live_shift;
-  size_t kop, bop, live, cnt, rcnt, heavy, parts;
+  int64_t nkb, nkp, ngr, live_rows, nrange, heavy_max;
+  int npiv, live_shift;
+  size_t groups, bgroup, kid, kop, bop, live, cnt, rcnt, heavy, parts;
 };
 PruneSizes prune_sizes(int64_t N, int H, int d) {
   PruneSizes z{};
   z.nkb = ceil_div(N, 32);
-  z.ngr = ceil_div(z.nkb, 32);
+  z.npiv = order_pivots(N);
+  // each group's last block may be partly empty: at most one block per group
+  z.nkp = z.nkb + z.npiv;
+  z.ngr = ceil_div(z.nkp, 32);
   const int64_t rows = (int64_t)H * z.nkb;
   // ranges of 2^live_shift query blocks (at least 16), as many as the live
   // words' budget holds (one range up to a few 10^5 nodes: each range is a
@@ -413,7 +418,10 @@ PruneSizes prune_sizes(int64_t N, int H, int d) {
   while (((int64_t)2 << z.live_shift) <= fit && ((int64_t)1 << z.live_shift) < rows) ++z.live_shift;
   z.live_rows = (int64_t)1 << z.live_shift;
   const int64_t held = rows < z.live_rows ? rows : z.live_rows;
-  z.kop = align256((size_t)rows * (d / 16) * 1024);
+  z.groups = 3 * align256((size_t)H * z.npiv * 4) + align256((size_t)H * 4);
+  z.bgroup = align256((size_t)H * z.nkp * 4);
+  z.kid = align256((size_t)H * z.nkp * 32 * 4);
+  z.kop = align256((size_t)H * z.nkp * (d / 16) * 1024);
   z.bop = align256((size_t)H * z.ngr * (d / 8) * 1024);
   z.live = align256((size_t)held * z.ngr * 4);
   z.cnt = align256((size_t)rows * 4);
@@ -431,19 +439,36 @@ bool prune_applies(int64_t N, int H, int d, int topk) {
   // From 2^16 nodes on: below, the streaming pass is faster (N = 31623:
   // 0.48 against 0.68 ms; the pruned pass pays a bound pass and a fixed
   // cost per wavefront).  Up to 2^19: block and word indices are 32-bit
-  // shifts of the query block index.
-  return (d == 32 || d == 64) && scan_list_len(topk) <= 16 && N >= ((int64_t)1 << 16) &&
-         N <= ((int64_t)1 << 19);
+  // shifts of the query block index, and a query block's live words fit the
+  // bound pass's LDS.
+  if (!((d == 32 || d == 64) && scan_list_len(topk) <= 16 && N >= ((int64_t)1 << 16) &&
+        N <= ((int64_t)1 << 19)))
+    return false;
+  return prune_sizes(N, H, d).ngr <= PRUNE_MAX_WORDS;
 }
 
 size_t prune_ws(int64_t N, int H, int d, int topk) {
   if (!prune_applies(N, H, d, topk)) return 0;
   const PruneSizes z = prune_sizes(N, H, d);
-  return z.kop + z.bop + z.live + z.cnt + z.rcnt + z.heavy + z.parts;
+  return z.groups + z.bgroup + z.kid + z.kop + z.bop + z.live + z.cnt + z.rcnt + z.heavy +
+         z.parts;
 }
 
 void prune_setup(ScanArgs& a, int d, char* w) {
   const PruneSizes z = prune_sizes(a.N, a.H, d);
+  const size_t gb = align256((size_t)a.H * z.npiv * 4);
+  a.gstart = reinterpret_cast<int32_t*>(w);
+  w += gb;
+  a.gsize = reinterpret_cast<int32_t*>(w);
+  w += gb;
+  a.pstart = reinterpret_cast<int32_t*>(w);
+  w += gb;
+  a.nkp_h = reinterpret_cast<int32_t*>(w);
+  w += z.groups - 3 * gb;
+  a.bgroup = reinterpret_cast<int32_t*>(w);
+  w += z.bgroup;
+  a.kid = reinterpret_cast<int32_t*>(w);
+  w += z.kid;
   a.kop = reinterpret_cast<uint16_t*>(w);
   w += z.kop;
   a.bop = reinterpret_cast<uint16_t*>(w);
@@ -463,6 +488,7 @@ void prune_setup(ScanArgs& a, int d, char* w) {
   a.heavy_parts = reinterpret_cast<uint2*>(w);
   a.heavy_max = (int)z.heavy_max;
   a.nkb = z.nkb;
+  a.nkp = z.nkp;
   a.ngr = z.ngr;
   a.live_rows = z.live_rows;
   a.live_shift = z.live_shift;

@@ -84,20 +84,19 @@ def test_workspace_sizes_are_linear_in_n():
     # One graph: an fp32 threshold, an int32 query-order entry and a 16-bit
     # code per row, plus per-head pivot counters (two int32 tables of 16
     # copies per pivot, one pivot per ~96 nodes: under 1.5 bytes per row).
-    # The pruned selection adds per row a copy of its key (2d bytes), a
-    # share of its block's bound row (d/8 bytes) and of its block's count,
-    # plus the live words of one range of query blocks (ceil(N/1024) words
-    # per block of 32 rows, at most 16 MiB) and the part lists of up to 8192
-    # heavy query blocks (256 MiB).
+    # The pruned selection adds per padded key slot a copy of its key (2d
+    # bytes), its node id (4 bytes) and a share of its block's bound row (d/8
+    # bytes); every pivot group (one per ~96 nodes) starts a new 32-slot
+    # block, so there are at most N + 32 npiv slots per head.  Plus the live
+    # words of one range of query blocks (at most 16 MiB) and the part lists
+    # of up to 8192 heavy query blocks (at most 256 MiB).
     rows = 100000 * 4
-    per_row = 10 + 64 + 4
-    live1 = 12500 * 98 * 4                              # one range of all query blocks
     parts = 8192 * 8 * 32 * 16 * 8                      # heavy query blocks' part lists
-    assert rows * per_row + live1 + parts <= f(100000, 4, 32, 15, 0) <= rows * per_row + live1 + parts + (4 << 20)
-    # linear in N but the live words (at most 16 MiB)
-    grow = f(200000, 4, 32, 15, 0) - f(100000, 4, 32, 15, 0)
-    assert rows * per_row - live1 <= grow <= rows * per_row + rows * 3 // 2 + (16 << 20) + (64 << 10)
-    assert f(500000, 4, 32, 15, 0) <= 2000000 * (per_row + 2) + (16 << 20) + parts + (4 << 20)
+    for N in (100000, 200000, 500000):
+        npiv = (N // 96) & ~31
+        slots = 4 * (N + 32 * npiv)
+        pr = _pruned_bytes(N, 4, 32)
+        assert slots * (64 + 4) <= pr <= slots * (64 + 4 + 4 + 1) + parts + (17 << 20)
     for (N, H, d) in [(100000, 4, 32), (200000, 4, 32), (500000, 4, 32), (8192, 4, 64)]:
         without = f(N, H, d, 15, 0) - _pruned_bytes(N, H, d)
         assert 10 * N * H <= without <= 12 * N * H + (1 << 20)
@@ -140,8 +139,10 @@ def _pruned_bytes(N, H, d):
     if not (1 << 16) <= N <= (1 << 19):
         return 0
     a = lambda x: (x + 255) // 256 * 256
+    npiv = min(max((N // 96) & ~31, 32), 16384)
     nkb = -(-N // 32)
-    ngr = -(-nkb // 32)
+    nkp = nkb + npiv
+    ngr = -(-nkp // 32)
     rows = H * nkb
     fit = (16 << 20) // (ngr * 4)
     shift = 4
@@ -150,7 +151,8 @@ def _pruned_bytes(N, H, d):
     held = min(rows, 1 << shift)
     nrange = -(-rows // (1 << shift))
     heavy = min(held, 8192)
-    return (a(rows * (d // 16) * 1024) + a(H * ngr * (d // 8) * 1024) + a(held * ngr * 4)
+    return (3 * a(H * npiv * 4) + a(H * 4) + a(H * nkp * 4) + a(H * nkp * 32 * 4)
+            + a(H * nkp * (d // 16) * 1024) + a(H * ngr * (d // 8) * 1024) + a(held * ngr * 4)
             + a(rows * 4) + 3 * a(nrange * 4) + a(heavy * 4) + a(heavy * 8 * 32 * 16 * 8))
 
 

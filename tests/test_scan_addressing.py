@@ -23,6 +23,8 @@ longer built; overflowing rows are now recomputed by rank passes of the
 """
 import math
 
+import numpy as np
+
 import pytest
 
 SCAN_QPW = 32
@@ -181,33 +183,71 @@ def test_partition_is_contiguous_per_workgroup():
 
 
 # ---------------------------------------------------------------- pruned selection
-PR_WAVES, PS_WAVES, PR_MAX_WORDS, PR_LPW, PR_NBUF, PS_NPF = 16, 4, 512, 2, 3, 4
+PR_WAVES, PS_WAVES, PR_MAX_WORDS, PR_LPW, PR_NBUF, PS_NPF = 16, 4, 704, 2, 3, 4
+
+
+def order_pivots(N):
+    return min(max((N // 96) & ~31, 32), 16384)
 
 
 def pruned_sizes(N, H, D):
-    """(nkb, ngr, live_rows): ranges of 2^s query blocks (s >= 4), as many
-    as 16 MiB of live words hold."""
+    """(nkb, nkp, ngr, live_rows): query blocks, padded key blocks per head
+    (each pivot group starts a new block), live words, and ranges of 2^s
+    query blocks (s >= 4), as many as 16 MiB of live words hold."""
     nkb = -(-N // 32)
-    ngr = -(-nkb // 32)
+    nkp = nkb + order_pivots(N)
+    ngr = -(-nkp // 32)
     rows = H * nkb
     fit = (16 << 20) // (ngr * 4)
     shift = 4
     while (2 << shift) <= fit and (1 << shift) < rows:
         shift += 1
-    return nkb, ngr, 1 << shift
+    return nkb, nkp, ngr, 1 << shift
 
 
-def check_pruned(N, H, D, nwg=256):
-    """Every index formed by key_pack_kernel, bound_live_kernel and
-    pruned_select_kernel (elements of kop / bop / live, LDS offsets) against
-    the sizes the host gives those buffers."""
+def group_layout(sizes):
+    """group_layout_kernel for one head: first positions, first padded slots
+    and the group of every padded key block."""
+    gstart = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    padded = (sizes + 31) // 32 * 32
+    pstart = np.concatenate([[0], np.cumsum(padded)[:-1]])
+    bgroup = np.repeat(np.arange(sizes.size), padded // 32)
+    return gstart, pstart, bgroup
+
+
+def check_pruned(N, H, D, nwg=256, seed=0):
+    """Every index formed by group_layout_kernel, key_pack_kernel,
+    bound_live_kernel and pruned_select_kernel (elements of kop / kid / bop /
+    live and the group tables, LDS offsets) against the sizes the host gives
+    those buffers."""
     NM, NMB = D // 16, D // 8
-    nkb, ngr, live_rows = pruned_sizes(N, H, D)
-    kop_elems, bop_elems = H * nkb * NM * 512, H * ngr * NMB * 512
-    assert ngr <= PR_MAX_WORDS
+    nkb, nkp, ngr, live_rows = pruned_sizes(N, H, D)
+    npiv = order_pivots(N)
+    kop_elems, bop_elems = H * nkp * NM * 512, H * ngr * NMB * 512
+    kid_elems = H * nkp * 32
+    assert ngr <= PR_MAX_WORDS and -(-ngr // 64) * 64 <= PR_MAX_WORDS
+    # group layout: any split of N positions into npiv groups (empty ones
+    # included) fills at most nkp blocks, and every slot maps back inside
+    # its group and the head's order
+    rng = np.random.default_rng(seed)
+    worst = np.full(npiv, N // npiv)
+    worst[: N - worst.sum()] += 1
+    for sizes in (worst, np.bincount(rng.integers(0, npiv, N), minlength=npiv),
+                  np.r_[np.full(npiv - 1, 1), N - npiv + 1]):
+        assert sizes.sum() == N and sizes.size == npiv
+        gstart, pstart, bgroup = group_layout(sizes)
+        nkph = bgroup.size
+        assert nkph <= nkp
+        for b in (0, nkph // 2, nkph - 1):
+            r = bgroup[b]
+            for l in (0, 31):
+                o = b * 32 + l - pstart[r]
+                assert 0 <= o < 32 * -(-sizes[r] // 32)
+                if o < sizes[r]:
+                    assert 0 <= gstart[r] + o < N
     # key_pack_kernel: grid (ceil(32 ngr / 4), H) x 4 wavefronts
     for h in (0, H - 1):
-        for b in (0, nkb - 1, nkb, ngr * 32 - 1):
+        for b in (0, nkb - 1, nkp - 1, nkp, ngr * 32 - 1):
             if b >= ngr * 32:
                 continue
             g, br = b // 32, b % 32
@@ -216,13 +256,14 @@ def check_pruned(N, H, D, nwg=256):
                 for m in range(2 * NM):
                     e = ((h * ngr + g) * 2 * NM + m) * 512 + (br + 32 * lh) * 8
                     assert 0 <= e and e + 8 <= bop_elems
-                if b < nkb:
-                    pos = b * 32 + (lane & 31)
-                    assert h * N + min(pos, N - 1) < H * N
+                if b < nkp:
+                    assert h * nkp + b < H * nkp               # bgroup
+                    assert (h * nkp + b) * 32 + (lane & 31) < kid_elems
+                    assert h * npiv + npiv - 1 < H * npiv      # gstart / gsize / pstart
                     for m in range(NM):
                         node = N - 1
                         assert (node * H + h) * D + 8 * lh + 16 * m + 8 <= N * H * D
-                        e = ((h * nkb + b) * NM + m) * 512 + lane * 8
+                        e = ((h * nkp + b) * NM + m) * 512 + lane * 8
                         assert e + 8 <= kop_elems
     # bound_live_kernel: ranges of live_rows query blocks, sub-tiles of <= 16
     total = H * nkb
@@ -273,21 +314,19 @@ def check_pruned(N, H, D, nwg=256):
         assert r0 + (grid - 1) * PS_WAVES + 3 >= r1 - 1
         PSLOT = NM * 1024 + 256
         assert PS_WAVES * PS_NPF * PSLOT + PS_WAVES * 8 * 64 * 8 <= 160 * 1024
-        for bb in (0, nkb - 1):
+        for bb in (0, nkb - 1, nkp - 1):
             for m in range(NM):
-                e = (H - 1) * nkb * NM * 512 + 63 * 8 + (bb * NM + m) * 512
+                e = (H - 1) * nkp * NM * 512 + 63 * 8 + (bb * NM + m) * 512
                 assert e + 8 <= kop_elems
                 lds = (PS_WAVES - 1) * PS_NPF * PSLOT + (PS_NPF - 1) * PSLOT + m * 1024 + 63 * 16
                 assert lds + 16 <= PS_WAVES * PS_NPF * PSLOT
-            # ids: lane offset (p - 32 bb) * 4 from perm + h N + 32 bb, p < N
+            # ids: lane offset (32 bb + l % 32) * 4 from kid + h nkp 32
             for lane in (0, 31, 63):
-                p = min(bb * 32 + (lane & 31), N - 1)
-                assert 0 <= (p - bb * 32) * 4 <= 124 and (H - 1) * N + p < H * N
+                off = (bb * 32 + (lane & 31)) * 4
+                assert (H - 1) * nkp * 32 + off // 4 < kid_elems and off < (1 << 32)
             lds = (PS_NPF - 1) * PSLOT + NM * 1024 + 63 * 4
             assert lds + 4 <= PS_NPF * PSLOT
     assert covered == total
-    # the last key block holds N - 32 (nkb - 1) keys; live bits past nkb are masked
-    assert 1 <= N - 32 * (nkb - 1) <= 32
     return nkb, ngr, live_rows
 
 
@@ -306,7 +345,7 @@ def test_heavy_parts_and_merge_stay_in_bounds(N, H):
     merge reads entries ((i PARTS 32 + q) 16) + p 32 16 + at, at < topk; the
     parts' words p, p + PARTS, ... cover each word once."""
     PARTS, HMAX = 8, 8192
-    nkb, ngr, live_rows = pruned_sizes(N, H, 32)
+    nkb, nkp, ngr, live_rows = pruned_sizes(N, H, 32)
     heavy_max = min(live_rows, H * nkb, HMAX)
     size = heavy_max * PARTS * 32 * 16
     i, q, p, r = heavy_max - 1, 31, PARTS - 1, 15

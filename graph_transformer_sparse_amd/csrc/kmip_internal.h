@@ -107,8 +107,8 @@ struct ScanArgs {
   //                               empty slot);
   //   kop  [H][nkp][D/16][64][8]  the block's keys in MFMA operand order
   //                               (zero rows in empty slots);
-  //   bop  [H][ngr][D/8][64][8]   per block a bound row [mid | rad], D + D
-  //                               elements, in operand order (see
+  //   bop  [H][ngr][D/16+1][64][8]  per block a bound row [mid | R e0],
+  //                               D + 16 elements, in operand order (see
   //                               key_pack_kernel);
   //   live [wid1 - wid0][ngr]     per query block (wid = h * nkb + block of
   //                               32 positions) a bit per key block whose

@@ -8,7 +8,7 @@
 // are taken in the query order, which groups nodes by their nearest pivot
 // query: for inputs with cluster structure the 32 keys of a block of that
 // order point the same way, and one bound per (query, block)
-//   q . k  <=  q . mid + |q| . rad         (|k_c - mid_c| <= rad_c)
+//   q . k  <=  q . mid + |q| R             (|k - mid| <= R, Euclidean norms)
 // rules most blocks out for a wavefront's 32 queries (which sit next to
 // each other in the same order).  A block never straddles two groups (the
 // last block of a group is padded with empty slots): a block holding the
@@ -20,7 +20,7 @@
 //                      new 32-key block;
 //   key_pack_kernel    keys of each head in query order, per 32-key block in
 //                      MFMA operand order, and the block's bound row
-//                      [mid | rad] (rad widened to cover fp32 rounding);
+//                      [mid | R] (R widened to cover fp32 rounding);
 //   bound_live_kernel  per query block of 32 positions, the bound of every
 //                      key block under the queries' thresholds: a bit per
 //                      key block whose bound reaches one of them;
@@ -35,18 +35,22 @@
 // stay with the streaming selection pass, which then skips all others.
 //
 // Exactness.  The score of (q, k) is one fp32 MFMA result; with M the largest
-// |k_c| of the block, it differs from q . k by at most 2^-19 |q|_1 M
-// (32 products, each exact in fp32, at most 32 roundings of 2^-24).  The
-// bound is a 64-term MFMA result, within 2^-16.4 |q|_1 M of its exact value
-// (|mid_c| <= M, rad_c <= 2M + pad).  rad is widened by pad = 2^-13 M per
-// element, which adds 2^-13 |q|_1 M to the bound: more than both errors, so a
+// |k_c| of the block, it differs from q . k by at most 2^-19 |q|_1 M <=
+// 2^-19 sqrt(d) |q| M (32 products, each exact in fp32, at most 32 roundings
+// of 2^-24).  The bound is a (d + 1)-term MFMA result, within 2^-17.4
+// sqrt(d) |q| M of its exact value (|mid_c| <= M, the norm and R rounded up
+// to bf16, R <= 2 sqrt(d) M + pad).  R is widened by pad = 2^-13 sqrt(d) M,
+// which adds 2^-13 sqrt(d) |q| M to the bound: more than both errors, so a
 // key whose computed score passes a threshold lies in a block whose computed
-// bound passes it too.
+// bound passes it too.  (Against a per-element box bound q . mid + |q| . rad,
+// this ball bound leaves about a third fewer blocks live on the clustered
+// inputs, with d / 16 + 1 operand slices instead of d / 8.)
 #pragma once
 
 constexpr int PR_WAVES = 16;              // bound pass: wavefronts per workgroup
 constexpr int PS_WAVES = 4;               // pruned selection: wavefronts per workgroup
-constexpr float PR_PAD = 0x1p-13f;        // rad widening relative to the block's max |k|
+constexpr float PR_PAD = 0x1p-13f;        // radius widening relative to sqrt(d) max |k|
+template <int D> constexpr float PR_SQRT_D = D == 32 ? 5.6569f : 8.0f;   // >= sqrt(D)
 constexpr int PR_MAX_WORDS = PRUNE_MAX_WORDS;  // live words per query block
 constexpr int PR_LPW = 2;                 // bound pass: operand pieces per wavefront per batch
 constexpr int PR_NBUF = 3;                // bound pass: ring slots
@@ -125,8 +129,9 @@ __global__ __launch_bounds__(GL_THREADS) void group_layout_kernel(ScanArgs a) {
 // exactly the A operand lane l supplies for that slice.
 //   kop[((h nkp + b) NM + m) 512 + 8 l + e]
 //   kid[(h nkp + b) 32 + l]                           for l < 32
-//   bop[((h ngr + g) 2NM + m') 512 + 8 (r + 32 s) + e]   for block 32 g + r:
-//       slices m' < NM hold mid, NM + m' rad, element 16 m' + 8 s + e.
+//   bop[((h ngr + g) (NM + 1) + m') 512 + 8 (r + 32 s) + e]   for block 32 g + r:
+//       slices m' < NM hold mid, element 16 m' + 8 s + e; slice NM holds R
+//       in element 0 and zeros.
 template <int D>
 __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
   constexpr int NM = D / 16;
@@ -140,12 +145,12 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
   const int H = a.H;
   const int64_t g = b / 32;
   const int br = (int)(b % 32);
-  uint16_t* bo = a.bop + (((int64_t)h * a.ngr + g) * (2 * NM)) * 512 + (br + 32 * lhalf) * 8;
+  uint16_t* bo = a.bop + (((int64_t)h * a.ngr + g) * (NM + 1)) * 512 + (br + 32 * lhalf) * 8;
   const int r = b < a.nkp ? a.bgroup[(int64_t)h * a.nkp + b] : -1;
   if (r < 0) {
     if (lrow == 0) {
 #pragma unroll
-      for (int m = 0; m < 2 * NM; ++m) *reinterpret_cast<uint4*>(bo + m * 512) = uint4{0, 0, 0, 0};
+      for (int m = 0; m < NM + 1; ++m) *reinterpret_cast<uint4*>(bo + m * 512) = uint4{0, 0, 0, 0};
     }
     return;
   }
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
 #pragma unroll
   for (int m = 0; m < NM; ++m) *reinterpret_cast<uint4*>(ko + m * 512) = v[m];
 
-  float hi[8 * NM], lo[8 * NM];
+  float hi[8 * NM], lo[8 * NM], xs[8 * NM];
   float amax = 0.f;
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -172,6 +177,7 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+      xs[8 * m + e] = x;
       hi[8 * m + e] = valid ? x : -kInf;
       lo[8 * m + e] = valid ? x : kInf;
       amax = fmaxf(amax, valid ? fabsf(x) : 0.f);
@@ -188,29 +194,34 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  // The centre: the middle of each element's range, truncated to bf16 (any
+  // centre will do; the radius is measured from the rounded one).  The
+  // radius: the largest distance of a row to it, over the rows of the block.
+  float d2 = 0.f;
+  uint32_t mb[8 * NM];
+#pragma unroll
+  for (int c = 0; c < 8 * NM; ++c) {
+    const float mid = __uint_as_float(__float_as_uint(0.5f * hi[c] + 0.5f * lo[c]) & 0xffff0000u);
+    mb[c] = __float_as_uint(mid) >> 16;
+    const float t = valid ? xs[c] - mid : 0.f;
+    d2 = fmaf(t, t, d2);
+  }
+  d2 += __shfl_xor(d2, 32);
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) d2 = fmaxf(d2, __shfl_xor(d2, o));
   if (lrow == 0) {
-    const float pad = PR_PAD * amax;
+    // R >= every row's distance (the fp32 sum and root are within 2^-19 of
+    // it, relative), plus the pad that covers the scores' rounding
+    const float R = sqrtf(d2) * (1.f + 0x1p-16f) + PR_PAD * PR_SQRT_D<D> * amax;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      uint32_t wm[4], wr[4];
+      uint32_t wm[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t mb[2], rb[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int c = 8 * m + 2 * i + t;
-          // any bf16 centre will do; rad is measured from the rounded one
-          const float mid = __uint_as_float(__float_as_uint(0.5f * hi[c] + 0.5f * lo[c]) &
-                                            0xffff0000u);
-          mb[t] = __float_as_uint(mid) >> 16;
-          rb[t] = bf16_bits_up(fmaxf(hi[c] - mid, mid - lo[c]) + pad);
-        }
-        wm[i] = mb[0] | (mb[1] << 16);
-        wr[i] = rb[0] | (rb[1] << 16);
-      }
+      for (int i = 0; i < 4; ++i) wm[i] = mb[8 * m + 2 * i] | (mb[8 * m + 2 * i + 1] << 16);
       *reinterpret_cast<uint4*>(bo + m * 512) = uint4{wm[0], wm[1], wm[2], wm[3]};
-      *reinterpret_cast<uint4*>(bo + (NM + m) * 512) = uint4{wr[0], wr[1], wr[2], wr[3]};
     }
+    *reinterpret_cast<uint4*>(bo + NM * 512) =
+        uint4{lhalf == 0 ? bf16_bits_up(R) : 0u, 0u, 0u, 0u};
   }
 }
 
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
 // w.  The head's bound rows stream through a PR_NBUF-slot LDS ring, GPB
 // groups of 32 key blocks per slot (PR_LPW 1 KB operand pieces per
 // wavefront), two slots ahead.  Each wavefront scores its 32 queries, as
-// [q | |q|], against 32 bound rows per MFMA chain (queries as the A operand,
+// [q | |q| e0], against 32 bound rows per MFMA chain (queries as the A operand,
 // so that a lane's 16 results belong to one key block); a key block is live
 // if its bound exceeds next_down(T) of one of the queries.  The live words
 // gather in LDS and go out after the sub-tile: live[(wid - wid0) ngr + g]
@@ -229,11 +240,11 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
 // in heavy_list / heavy_cnt.
 template <int D>
 __global__ __launch_bounds__(PR_WAVES * 64) void bound_live_kernel(ScanArgs a, int nwg) {
-  constexpr int NM = D / 16, NMB = 2 * NM;
+  constexpr int NM = D / 16, NMB = NM + 1;
   constexpr int PIECES = PR_WAVES * PR_LPW;
-  constexpr int GPB = PIECES / NMB;
+  constexpr int GPB = PIECES / NMB / 2 * 2;            // groups per slot (even)
   constexpr int SLOT = PIECES * 1024;
-  static_assert(GPB * NMB == PIECES, "whole groups per slot");
+  static_assert(GPB >= 2, "two groups per slot at least");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[PR_NBUF * SLOT];
   __shared__ uint32_t wsh[PR_WAVES * PR_MAX_WORDS];
   const unsigned ring_lds =
@@ -253,15 +264,17 @@ __global__ __launch_bounds__(PR_WAVES * 64) void bound_live_kernel(ScanArgs a, i
   uint32_t* ws = wsh + wave * PR_MAX_WORDS;
 
   // Batch ib into ring slot `slot`: piece p = wave + i * PR_WAVES is slice
-  // p % NMB of group GPB ib + p / NMB (past the last group: the last group
-  // again, never read), so every wavefront always issues PR_LPW loads.
+  // p % NMB of group GPB ib + p / NMB (past the last group, or past the
+  // batch's GPB NMB pieces: the last piece again, never read), so every
+  // wavefront always issues PR_LPW loads.
   auto issue = [&](int h, int ib, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PR_LPW; ++i) {
       const int p = wave + i * PR_WAVES;
-      int64_t g = (int64_t)ib * GPB + p / NMB;
+      const int pp = p < GPB * NMB ? p : GPB * NMB - 1;
+      int64_t g = (int64_t)ib * GPB + pp / NMB;
       g = g < ngr ? g : ngr - 1;
-      const uint16_t* base = a.bop + (((int64_t)h * ngr + g) * NMB + p % NMB) * 512;
+      const uint16_t* base = a.bop + (((int64_t)h * ngr + g) * NMB + pp % NMB) * 512;
       asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"((unsigned)lane * 16u), "s"(base),
                    "{m0}"(__builtin_amdgcn_readfirstlane(
                        ring_lds + (unsigned)(slot * SLOT + p * 1024)))
@@ -285,16 +298,27 @@ __global__ __launch_bounds__(PR_WAVES * 64) void bound_live_kernel(ScanArgs a, i
     const bool qvalid = active && pos < N;
     const int64_t qrow = a.perm[(int64_t)h * N + (pos < N ? pos : N - 1)];
     const uint16_t* qp = a.q + (qrow * H + h) * D + 8 * lhalf;
+    // A operand [q | |q| e0]: the row, then its Euclidean norm (rounded up
+    // to bf16, the fp32 sum and root being within 2^-19 of it, relative) as
+    // element 0 of one more slice, against [mid | R e0] of the key blocks.
     bf16x8_t qb[NMB];
+    float qq = 0.f;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      uint4 w = *reinterpret_cast<const uint4*>(qp + 16 * m);
+      const uint4 w = *reinterpret_cast<const uint4*>(qp + 16 * m);
       qb[m] = *reinterpret_cast<const bf16x8_t*>(&w);
-      w.x &= 0x7fff7fffu;
-      w.y &= 0x7fff7fffu;
-      w.z &= 0x7fff7fffu;
-      w.w &= 0x7fff7fffu;
-      qb[NM + m] = *reinterpret_cast<const bf16x8_t*>(&w);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = bf16_lo(ww[i]), x1 = bf16_hi(ww[i]);
+        qq = fmaf(x0, x0, qq);
+        qq = fmaf(x1, x1, qq);
+      }
+    }
+    qq += __shfl_xor(qq, 32);
+    {
+      const uint4 w = {lhalf == 0 ? bf16_bits_up(sqrtf(qq) * (1.f + 0x1p-16f)) : 0u, 0u, 0u, 0u};
+      qb[NM] = *reinterpret_cast<const bf16x8_t*>(&w);
     }
     const float thr = qvalid ? next_down(a.thr[qrow * H + h]) : kInf;
     // The MFMA below puts the queries on the rows: lane l then holds key

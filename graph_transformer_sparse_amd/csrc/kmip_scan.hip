@@ -422,7 +422,7 @@ PruneSizes prune_sizes(int64_t N, int H, int d) {
   z.bgroup = align256((size_t)H * z.nkp * 4);
   z.kid = align256((size_t)H * z.nkp * 32 * 4);
   z.kop = align256((size_t)H * z.nkp * (d / 16) * 1024);
-  z.bop = align256((size_t)H * z.ngr * (d / 8) * 1024);
+  z.bop = align256((size_t)H * z.ngr * (d / 16 + 1) * 1024);
   z.live = align256((size_t)held * z.ngr * 4);
   z.cnt = align256((size_t)rows * 4);
   z.nrange = ceil_div(rows, z.live_rows);

@@ -85,8 +85,8 @@ def test_workspace_sizes_are_linear_in_n():
     # code per row, plus per-head pivot counters (two int32 tables of 16
     # copies per pivot, one pivot per ~96 nodes: under 1.5 bytes per row).
     # The pruned selection adds per padded key slot a copy of its key (2d
-    # bytes), its node id (4 bytes) and a share of its block's bound row (d/8
-    # bytes); every pivot group (one per ~96 nodes) starts a new 32-slot
+    # bytes), its node id (4 bytes) and a share of its block's bound row
+    # (d/16 + 1 bytes); every pivot group (one per ~96 nodes) starts a new 32-slot
     # block, so there are at most N + 32 npiv slots per head.  Plus the live
     # words of one range of query blocks (at most 16 MiB) and the part lists
     # of up to 8192 heavy query blocks (at most 256 MiB).
@@ -152,7 +152,7 @@ def _pruned_bytes(N, H, d):
     nrange = -(-rows // (1 << shift))
     heavy = min(held, 8192)
     return (3 * a(H * npiv * 4) + a(H * 4) + a(H * nkp * 4) + a(H * nkp * 32 * 4)
-            + a(H * nkp * (d // 16) * 1024) + a(H * ngr * (d // 8) * 1024) + a(held * ngr * 4)
+            + a(H * nkp * (d // 16) * 1024) + a(H * ngr * (d // 16 + 1) * 1024) + a(held * ngr * 4)
             + a(rows * 4) + 3 * a(nrange * 4) + a(heavy * 4) + a(heavy * 8 * 32 * 16 * 8))
 
 

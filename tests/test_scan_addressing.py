@@ -220,7 +220,7 @@ def check_pruned(N, H, D, nwg=256, seed=0):
     bound_live_kernel and pruned_select_kernel (elements of kop / kid / bop /
     live and the group tables, LDS offsets) against the sizes the host gives
     those buffers."""
-    NM, NMB = D // 16, D // 8
+    NM, NMB = D // 16, D // 16 + 1
     nkb, nkp, ngr, live_rows = pruned_sizes(N, H, D)
     npiv = order_pivots(N)
     kop_elems, bop_elems = H * nkp * NM * 512, H * ngr * NMB * 512
@@ -253,8 +253,8 @@ def check_pruned(N, H, D, nwg=256, seed=0):
             g, br = b // 32, b % 32
             for lane in (0, 31, 32, 63):
                 lh = lane >> 5
-                for m in range(2 * NM):
-                    e = ((h * ngr + g) * 2 * NM + m) * 512 + (br + 32 * lh) * 8
+                for m in range(NMB):
+                    e = ((h * ngr + g) * NMB + m) * 512 + (br + 32 * lh) * 8
                     assert 0 <= e and e + 8 <= bop_elems
                 if b < nkp:
                     assert h * nkp + b < H * nkp               # bgroup
@@ -268,9 +268,9 @@ def check_pruned(N, H, D, nwg=256, seed=0):
     # bound_live_kernel: ranges of live_rows query blocks, sub-tiles of <= 16
     total = H * nkb
     nrange = -(-total // live_rows)
-    GPB = PR_WAVES * PR_LPW // NMB
-    assert GPB * NMB == PR_WAVES * PR_LPW
-    SLOT = GPB * NMB * 1024
+    GPB = PR_WAVES * PR_LPW // NMB // 2 * 2
+    assert GPB >= 2 and GPB * NMB <= PR_WAVES * PR_LPW
+    SLOT = PR_WAVES * PR_LPW * 1024
     assert PR_NBUF * SLOT + PR_WAVES * PR_MAX_WORDS * 4 <= 160 * 1024
     covered = 0
     for r0 in range(0, total, live_rows):
@@ -299,8 +299,9 @@ def check_pruned(N, H, D, nwg=256, seed=0):
             for w in range(PR_WAVES):
                 for i in range(PR_LPW):
                     p = w + i * PR_WAVES
-                    g = min(ib * GPB + p // NMB, ngr - 1)
-                    e = ((H - 1) * ngr + g) * NMB * 512 + (p % NMB) * 512 + 63 * 8
+                    pp = min(p, GPB * NMB - 1)
+                    g = min(ib * GPB + pp // NMB, ngr - 1)
+                    e = ((H - 1) * ngr + g) * NMB * 512 + (pp % NMB) * 512 + 63 * 8
                     assert e + 8 <= bop_elems
                     lds = (PR_NBUF - 1) * SLOT + p * 1024 + 63 * 16
                     assert lds + 16 <= PR_NBUF * SLOT

@@ -90,8 +90,9 @@ struct ScanArgs {
   // Selection pass: first rank it computes (0, or 16, 32, ... in the passes
   // that recompute rows with overflowing candidate arrays).
   int rank0;
-  // Pruned selection (one graph with a query order, rows of 32 or 64 bf16,
-  // lists of at most 16; kop == nullptr: off).  Keys are taken in the query
+  // Pruned selection (one graph with a query order, rows of 32 or 64 bf16;
+  // lists longer than 16 collect candidates instead of selecting; kop ==
+  // nullptr: off).  Keys are taken in the query
   // order, in 32-key blocks.  Every pivot group of the order starts a new
   // key block (its last block padded with empty slots), so the keys of a
   // block belong to one group and its bound is tight; nkp = nkb + npiv
@@ -122,7 +123,8 @@ struct ScanArgs {
   //                               range with many live key blocks (split over
   //                               several wavefronts), and their number per
   //                               range;
-  //   heavy_parts [heavy_max][parts][32][16]  the parts' lists per query.
+  //   heavy_parts [heavy_max][parts][32][16]  the parts' lists per query
+  //                               (lists of at most 16 only).
   // A range whose query blocks have on average more than PRUNE_STREAM_NUM /
   // PRUNE_STREAM_DEN of the key blocks live (inputs without enough cluster
   // structure) is left to the streaming selection pass; the pruned pass

@@ -413,7 +413,12 @@ __device__ __forceinline__ bool prune_before(uint2 x, uint2 y) {
 // live words, whose own waits are stricter).  Leaves each lane's half-list
 // (top KP under (score descending, id ascending), +inf sentinels in slots
 // [0, KP - topk)) in ls / lj.
-template <int D, int KP, int NPF>
+//
+// COL (lists longer than 16): no lists; every key above the seed goes to the
+// row's candidate array, cand[(lhalf cap + n) N H + row] for n < cap, and the
+// lane's count (past cap when the array overflowed) to cand_cnt[2 row +
+// lhalf], as the streaming collecting pass does.
+template <int D, int KP, int NPF, bool COL = false>
 __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int start, int stride,
                                            unsigned char* wring, uint2* wcb, float (&ls)[KP],
                                            int (&lj)[KP], int64_t& qrow_out, bool& qvalid_out) {
@@ -432,6 +437,11 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
   const int64_t qrow = a.perm[(int64_t)h * N + (qvalid ? pos : N - 1)];
   qrow_out = qrow;
   qvalid_out = qvalid;
+  const int64_t NH = N * H;
+  const int64_t crow = qrow * H + h;
+  int ccnt = 0;
+  (void)NH;
+  (void)crow;
   bf16x8_t qb[NM];
   {
     const uint16_t* qp = a.q + (qrow * H + h) * D + 8 * lhalf;
@@ -597,6 +607,26 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
     bool gq[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) gq[qq] = quarter_hit(s, qq, thr);
+    if constexpr (COL) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        if (gq[qq]) {
+          const int4 id4 = *reinterpret_cast<const int4*>(ids + 8 * qq + 4 * lhalf);
+          const int idv[4] = {id4.x, id4.y, id4.z, id4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sv = s[4 * qq + r];
+            if (sv > thr && idv[r] >= 0) {
+              if (ccnt < a.cap)
+                a.cand[(int64_t)(lhalf * a.cap + ccnt) * NH + crow] =
+                    make_uint2(__float_as_uint(sv), (unsigned)idv[r]);
+              ++ccnt;
+            }
+          }
+        }
+      }
+      return;
+    }
     static_assert(SCAN_CAP >= 8, "a half block appends up to 8 scores");
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -636,7 +666,11 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
   }
   // the ring loads still in flight land in this wavefront's own slots
   __builtin_amdgcn_s_waitcnt(0x0f70);
-  drain();
+  if constexpr (COL) {
+    if (qvalid) a.cand_cnt[2 * crow + lhalf] = ccnt;
+  } else {
+    drain();
+  }
 }
 
 // One wavefront per query block wid in [wid0, wid1) of a range left to this
@@ -645,10 +679,10 @@ __device__ __forceinline__ void prune_wave(const ScanArgs& a, int64_t wid, int s
 // wavefronts; logical ids grouped per XCD (gridDim.x is a multiple of 8),
 // so each XCD's L2 serves neighbouring query blocks, which share most live
 // key blocks.
-template <int D, int KP>
+template <int D, int KP, bool COL = false>
 __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3))) void pruned_select_kernel(ScanArgs a) {
   static_assert(KP <= 16, "register lists");
-  constexpr int CBW = SCAN_CAP * 64;
+  constexpr int CBW = COL ? 1 : SCAN_CAP * 64;
   constexpr int SLOT = (D / 16) * 1024 + 256;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[PS_WAVES * PS_NPF * SLOT];
   __shared__ __attribute__((aligned(16))) uint2 cbuf[PS_WAVES * CBW];
@@ -660,7 +694,9 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
   const int64_t wid = a.wid0 + L * PS_WAVES + wave;
   if (wid >= a.wid1) return;
   if (prune_range_stream(a, wid)) return;              // left to the streaming pass
-  if (a.qb_cnt[wid] > PR_HEAVY) return;                // left to the parts (below)
+  // (lists longer than 16 take every query block here: their candidate
+  // counts are per lane)
+  if (!COL && a.qb_cnt[wid] > PR_HEAVY) return;        // left to the parts (below)
   const int H = a.H, topk = a.topk;
   const int h = (int)(wid / a.nkb);
   float ls[KP];
@@ -668,8 +704,9 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
   int64_t qrow;
   bool qvalid;
   uint2* wl = cbuf + wave * CBW;
-  prune_wave<D, KP, PS_NPF>(a, wid, 0, 1, ring + wave * (PS_NPF * SLOT), wl, ls, lj, qrow,
-                            qvalid);
+  prune_wave<D, KP, PS_NPF, COL>(a, wid, 0, 1, ring + wave * (PS_NPF * SLOT), wl, ls, lj, qrow,
+                                 qvalid);
+  if constexpr (COL) return;
 
   // Two-pointer merge of the half-lists of each query (lanes l, l ^ 32)
   // under (score descending, id ascending), as in the streaming pass.
@@ -850,11 +887,12 @@ __global__ void prune_decide_kernel(ScanArgs a) {
   a.range_stream[r] = (int64_t)a.range_cnt[r] * PRUNE_STREAM_DEN >= rows * a.nkb * PRUNE_STREAM_NUM;
 }
 
-// Group layout, key copy and bound rows, then per range of query blocks the bound pass and
-// the pruned selection: light query blocks, the parts of heavy ones, their
-// merge.  range_cnt / heavy_cnt then tell the streaming pass which ranges are
+// Group layout, key copy and bound rows, then per range of query blocks the
+// bound pass and the pruned selection: light query blocks, the parts of heavy
+// ones, their merge (COL: every query block collects its candidates in one
+// wavefront).  range_stream then tells the streaming pass which ranges are
 // its own.
-template <int D, int KP>
+template <int D, int KP, bool COL = false>
 hipError_t launch_prune(const ScanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(group_layout_kernel, dim3((unsigned)a.H), dim3(GL_THREADS), 0, s, a);
   hipLaunchKernelGGL(key_pack_kernel<D>, dim3((unsigned)ceil_div(a.ngr * 32, 4), (unsigned)a.H),
@@ -877,10 +915,11 @@ hipError_t launch_prune(const ScanArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t wgs = ceil_div(b.wid1 - b.wid0, PS_WAVES);
-    hipLaunchKernelGGL((pruned_select_kernel<D, KP>), dim3((unsigned)(8 * ceil_div(wgs, 8))),
+    hipLaunchKernelGGL((pruned_select_kernel<D, KP, COL>), dim3((unsigned)(8 * ceil_div(wgs, 8))),
                        dim3(PS_WAVES * 64), 0, s, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (COL) continue;
     hipLaunchKernelGGL(pk, dim3((unsigned)ceil_div((int64_t)a.heavy_max * PH_PARTS, PS_WAVES)),
                        dim3(PS_WAVES * 64), 0, s, b);
     e = hipGetLastError();

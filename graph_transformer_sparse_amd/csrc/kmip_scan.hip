@@ -441,7 +441,7 @@ bool prune_applies(int64_t N, int H, int d, int topk) {
   // cost per wavefront).  Up to 2^19: block and word indices are 32-bit
   // shifts of the query block index, and a query block's live words fit the
   // bound pass's LDS.
-  if (!((d == 32 || d == 64) && scan_list_len(topk) <= 16 && N >= ((int64_t)1 << 16) &&
+  if (!((d == 32 || d == 64) && scan_list_len(topk) > 0 && N >= ((int64_t)1 << 16) &&
         N <= ((int64_t)1 << 19)))
     return false;
   return prune_sizes(N, H, d).ngr <= PRUNE_MAX_WORDS;
@@ -450,8 +450,9 @@ bool prune_applies(int64_t N, int H, int d, int topk) {
 size_t prune_ws(int64_t N, int H, int d, int topk) {
   if (!prune_applies(N, H, d, topk)) return 0;
   const PruneSizes z = prune_sizes(N, H, d);
+  // lists longer than 16 collect their candidates (no heavy parts)
   return z.groups + z.bgroup + z.kid + z.kop + z.bop + z.live + z.cnt + z.rcnt + z.heavy +
-         z.parts;
+         (scan_list_len(topk) <= 16 ? z.parts : 0);
 }
 
 void prune_setup(ScanArgs& a, int d, char* w) {
@@ -485,7 +486,7 @@ void prune_setup(ScanArgs& a, int d, char* w) {
   w += align256((size_t)z.heavy_max * 4);
   a.heavy_cnt = reinterpret_cast<int32_t*>(w);
   w += align256((size_t)z.nrange * 4);
-  a.heavy_parts = reinterpret_cast<uint2*>(w);
+  a.heavy_parts = scan_list_len(a.topk) <= 16 ? reinterpret_cast<uint2*>(w) : nullptr;
   a.heavy_max = (int)z.heavy_max;
   a.nkb = z.nkb;
   a.nkp = z.nkp;

@@ -261,6 +261,9 @@ struct Scanner {
     // tight bound, and this sample only guards inputs without cluster
     // structure: 8 times sparser (N = 10^5: 3.10 -> 3.02 ms for the whole
     // selection; dropping it entirely gained no more).
+    // (Long lists keep every second chunk on the pruned path too: at N =
+    // 10^5, k = 45 every fourth or sixteenth left so many rows' candidate
+    // arrays overflowing that the rank passes cost more than was saved.)
     const int sparse = perm != nullptr ? 8 : 1;
     const int sample = !(PRE && KP <= 16)       ? SAMPLE
                        : nkeys >= (int64_t)1 << 16 ? 4 * SAMPLE * sparse
@@ -300,7 +303,7 @@ struct Scanner {
       const int64_t r = qrow[0] * H + t.h;
       keep[0] = qvalid[0] && (a.cand_cnt[2 * r] > a.cap || a.cand_cnt[2 * r + 1] > a.cap);
       wave_rows = __ballot(keep[0]) != 0ull;
-    } else if constexpr (MODE == M_SELECT && (D == 32 || D == 64)) {
+    } else if constexpr ((MODE == M_SELECT || MODE == M_COLLECT) && (D == 32 || D == 64)) {
       static_assert(QB == 1, "one query block per wavefront");
       if (a.range_stream != nullptr) {
         filtered = true;
@@ -777,15 +780,25 @@ __global__ __launch_bounds__(256) void collect_topk_kernel(ScanArgs a) {
     ls[i] = i < nsent ? kInf : -kInf;
     lj[i] = -1;
   }
+  // Candidates are read eight at a time, so that eight loads are in flight
+  // before the first insertion waits for its entry.
+  constexpr int PF = 8;
   for (int hf = 0; hf < 2; ++hf) {
     const int n = hf ? c1 : c0;
     const uint2* src = a.cand + (int64_t)hf * a.cap * NH + r;
-    for (int u = 0; u < n; ++u) {
-      const uint2 e = src[(int64_t)u * NH];
-      const float sv = __uint_as_float(e.x);
-      const int j = (int)e.y;
-      if (sv > ls[KP - 1] || (sv == ls[KP - 1] && (unsigned)j < (unsigned)lj[KP - 1]))
-        ordered_insert<KP>(ls, lj, sv, j);
+    for (int u0 = 0; u0 < n; u0 += PF) {
+      uint2 e[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i)
+        e[i] = u0 + i < n ? src[(int64_t)(u0 + i) * NH] : make_uint2(__float_as_uint(-kInf), ~0u);
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        const float sv = __uint_as_float(e[i].x);
+        const int j = (int)e[i].y;
+        if (u0 + i < n &&
+            (sv > ls[KP - 1] || (sv == ls[KP - 1] && (unsigned)j < (unsigned)lj[KP - 1])))
+          ordered_insert<KP>(ls, lj, sv, j);
+      }
     }
   }
   int32_t* oi = a.idx + r * a.topk;
@@ -908,10 +921,20 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if constexpr (KP > 16) {
-    // Long lists: collect candidates, select from them, then recompute the
-    // rows whose candidate arrays overflowed (that pass usually only checks
-    // the counts).
-    e = launch_pass<D, KP, M_COLLECT>(a, s);
+    // Long lists: collect candidates (the pruned pass for the ranges it
+    // keeps, the streaming pass for the rest), select from them, then
+    // recompute the rows whose candidate arrays overflowed (that pass
+    // usually only checks the counts).
+    ScanArgs c = a;
+    c.range_stream = nullptr;
+    if constexpr (D == 32 || D == 64) {
+      if (a.kop != nullptr) {
+        e = launch_prune<D, 16, true>(a, s);
+        if (e != hipSuccess) return e;
+        c.range_stream = a.range_stream;
+      }
+    }
+    e = launch_pass<D, KP, M_COLLECT>(c, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(collect_topk_kernel<KP>, dim3((unsigned)ceil_div(a.N * a.H, 256)),
                        dim3(256), 0, s, a);

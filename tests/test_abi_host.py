@@ -100,8 +100,10 @@ def test_workspace_sizes_are_linear_in_n():
     for (N, H, d) in [(100000, 4, 32), (200000, 4, 32), (500000, 4, 32), (8192, 4, 64)]:
         without = f(N, H, d, 15, 0) - _pruned_bytes(N, H, d)
         assert 10 * N * H <= without <= 12 * N * H + (1 << 20)
-    # without the pruned pass (lists longer than 16): the first three terms only
-    assert rows * 10 <= f(100000, 4, 32, 45, 0) - 2 * 128 * rows * 8 - rows * 8 <= rows * 10 + (4 << 20)
+    # lists longer than 16: the pruned buffers without the heavy parts, and
+    # the candidate arrays (2 x 128 entries of 8 bytes per row) with counts
+    assert rows * 10 <= (f(100000, 4, 32, 45, 0) - _pruned_bytes(100000, 4, 32, parts=False)
+                         - 2 * 128 * rows * 8 - rows * 8) <= rows * 10 + (4 << 20)
     assert f(100000, 4, 32, 15, 64) > rows * 4                # thresholds plus the tile plan
     b1, b2 = b(100000, 4, 32, 15), b(200000, 4, 32, 15)
     assert 1.9 < b2 / b1 < 2.1                              # O(N * H * k)
@@ -133,9 +135,10 @@ def test_backward_f32_rejects():
     assert L.kmip_backward_f32(*args, FAKE, 1 << 40, None) == INVALID
 
 
-def _pruned_bytes(N, H, d):
+def _pruned_bytes(N, H, d, parts=True):
     """Buffers of the pruned selection (one graph with a query order, bf16
-    rows of 32 or 64, lists of at most 16, 2^16 <= N <= 2^19)."""
+    rows of 32 or 64, 2^16 <= N <= 2^19); lists longer than 16 have no
+    heavy parts' lists."""
     if not (1 << 16) <= N <= (1 << 19):
         return 0
     a = lambda x: (x + 255) // 256 * 256
@@ -153,7 +156,8 @@ def _pruned_bytes(N, H, d):
     heavy = min(held, 8192)
     return (3 * a(H * npiv * 4) + a(H * 4) + a(H * nkp * 4) + a(H * nkp * 32 * 4)
             + a(H * nkp * (d // 16) * 1024) + a(H * ngr * (d // 16 + 1) * 1024) + a(held * ngr * 4)
-            + a(rows * 4) + 3 * a(nrange * 4) + a(heavy * 4) + a(heavy * 8 * 32 * 16 * 8))
+            + a(rows * 4) + 3 * a(nrange * 4) + a(heavy * 4)
+            + (a(heavy * 8 * 32 * 16 * 8) if parts else 0))
 
 
 def test_f32_workspace_adds_split_rows():

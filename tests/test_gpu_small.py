@@ -226,11 +226,13 @@ def test_deterministic_repeat_query_order(topk):
     _repeat(small_case(12288, 4, 32, topk, law="clustered", clusters=24, seed=55 + topk))
 
 
-def test_deterministic_repeat_pruned():
+@pytest.mark.parametrize("topk", [15, 45])
+def test_deterministic_repeat_pruned(topk):
     """2^16 nodes: the pruned selection, whose heavy query blocks are listed
     through an atomic counter (their order, and where their parts' lists
-    go, change between calls); results must not."""
-    _repeat(small_case(65536, 2, 32, 15, law="clustered", clusters=64, seed=57))
+    go, change between calls); k = 45 collects candidates from the pruned
+    key blocks.  Results must not change."""
+    _repeat(small_case(65536, 2, 32, topk, law="clustered", clusters=64, seed=57))
 
 
 def test_deterministic_repeat_batched():
@@ -256,15 +258,18 @@ def _sample(n, m, seed):
     return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=m, replace=False)]))
 
 
-def test_exact_ties_on_the_pruned_path():
+@pytest.mark.parametrize("topk", [15, 45])
+def test_exact_ties_on_the_pruned_path(topk):
     """One graph of 2^16 nodes (the pruned selection: keys scored in the
     query order, out of node order): 97 distinct key rows, each repeated
     ~676 times, give bitwise-equal scores, and the smaller node id must still
-    win every tie, in the oracle's order, on 4096 sampled rows."""
+    win every tie, in the oracle's order, on 4096 sampled rows.  At k = 45
+    the tied candidates overflow the rows' arrays, and the rank passes
+    recompute those rows."""
     from tests.gpu_util import np_, run_forward
     from tests.parity import oracle_forward
     n = 65536
-    w = small_case(n, 1, 32, 15, law="clustered", clusters=48, seed=131, backward=False)
+    w = small_case(n, 1, 32, topk, law="clustered", clusters=48, seed=131, backward=False)
     w.k = w.k[np.arange(n) % 97]
     print(f"[case] ties n={w.n} H={w.heads} d={w.d} k={w.topk}", flush=True)
     t, out, idx, score = run_forward(w)
@@ -274,8 +279,8 @@ def test_exact_ties_on_the_pruned_path():
     assert np.array_equal(np_(idx)[rows], ref["idx"].astype(np.int32))
 
 
-@pytest.mark.parametrize("d", [32, 64])
-def test_pruned_and_streaming_query_blocks_mixed(d):
+@pytest.mark.parametrize("d,topk", [(32, 8), (64, 8), (32, 45)])
+def test_pruned_and_streaming_query_blocks_mixed(d, topk):
     """One graph of 2^16 nodes, half of them in tight clusters, half i.i.d.:
     the clustered query blocks' key blocks are mostly ruled out by their
     bounds, the i.i.d. ones (whose bounds leave most key blocks live) become
@@ -283,7 +288,7 @@ def test_pruned_and_streaming_query_blocks_mixed(d):
     oracle, forward and backward."""
     from workloads import f32_to_bf16_bits
     n, heads = 65536, 1
-    w = small_case(n, heads, d, 8, law="clustered", clusters=32, seed=171 + d)
+    w = small_case(n, heads, d, topk, law="clustered", clusters=32, seed=171 + d)
     rng = np.random.default_rng(5 + d)
     half = n // 2
     for name in ("q", "k"):
@@ -301,10 +306,11 @@ def test_pruned_and_streaming_query_blocks_mixed(d):
     assert_rows_close(np_(dq)[rows], rq, "dq")
 
 
-def test_pruned_path_streams_inputs_without_cluster_structure():
+@pytest.mark.parametrize("topk", [15, 45])
+def test_pruned_path_streams_inputs_without_cluster_structure(topk):
     """One graph of 2^16 i.i.d. nodes: nearly every key block stays live, so
     the range goes to the streaming pass; 2048 sampled rows against the
     oracle."""
-    w = small_case(65536, 1, 32, 15, law="iid", seed=191, backward=False)
+    w = small_case(65536, 1, 32, topk, law="iid", seed=191, backward=False)
     rows = _sample(65536, 2048, 9)
     _forward_check(w, rows=rows)

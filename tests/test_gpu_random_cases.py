@@ -59,3 +59,43 @@ def test_random_case(case):
     assert_rows_close(np_(dq), rq, "dq")
     assert_rows_close(np_(dk), rk, "dk")
     assert_rows_close(np_(dv), rv, "dv")
+
+
+def _draw_pruned(case):
+    """One graph of 2^16 .. 2 * 10^5 nodes (the pruned selection's range):
+    clustered inputs of random tightness and cluster count (some ranges
+    stream, some query blocks split), or i.i.d. inputs (everything streams),
+    with short and long lists."""
+    rng = np.random.default_rng(930_000 + case)
+    d = int(rng.choice([32, 64]))
+    heads = int(rng.choice([1, 2, 4]))
+    topk = int(rng.choice([1, 5, 8, 15, 16, 17, 32, 45, 64]))
+    law = str(rng.choice(["clustered", "clustered", "clustered", "iid"]))
+    clusters = int(rng.choice([16, 64, 256, 1024]))
+    sigma = float(rng.choice([0.05, 0.3, 1.0]))
+    n = int(rng.integers(1 << 16, 200_000))
+    return make_workload(f"random_pruned_{case}", n=n, heads=heads, d=d, topk=topk, law=law,
+                         clusters=clusters if law == "clustered" else 0, sigma=sigma,
+                         backward=True, seed=int(rng.integers(1 << 30)))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_case_pruned(case):
+    """The pruned path on random shapes: selection and output on 2048 seeded
+    nodes x all heads, and dq on those rows, against the oracle."""
+    from tests.gpu_util import np_, run_backward, run_forward
+    w = _draw_pruned(case)
+    print(f"[case] random pruned {case}: n={w.n} H={w.heads} d={w.d} k={w.topk} "
+          f"{w.meta['law']} C={w.meta['clusters']} sigma={w.meta['sigma']}", flush=True)
+    t, out, idx, score = run_forward(w)
+    q, k, v = decode(w)
+    idx_n = np_(idx)
+    rows = np.unique(np.concatenate(
+        [[0, w.n - 1], np.random.default_rng(case).choice(w.n, 2048, replace=False)]))
+    check_selection(idx_n, np_(score), q, k, w.offsets, w.topk, rows)
+    ref = orc.attend_on_sets(q, k, v, idx_n[rows].astype(np.int64), rows=rows)
+    assert_rows_close(np_(out)[rows], ref["out"], "out")
+    dq, _, _ = run_backward(w, t, idx, score)
+    rq, _, _ = orc.kmip_backward_on_sets(q, k, v, idx_n[rows].astype(np.int64),
+                                         w.dout.astype(np.float64), rows=rows)
+    assert_rows_close(np_(dq)[rows], rq, "dq")

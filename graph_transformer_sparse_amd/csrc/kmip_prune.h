@@ -50,11 +50,21 @@
 constexpr int PR_WAVES = 16;              // bound pass: wavefronts per workgroup
 constexpr int PS_WAVES = 4;               // pruned selection: wavefronts per workgroup
 constexpr float PR_PAD = 0x1p-13f;        // radius widening relative to sqrt(d) max |k|
-template <int D> constexpr float PR_SQRT_D = D == 32 ? 5.6569f : 8.0f;   // >= sqrt(D)
+template <int D> constexpr float PR_SQRT_D = D == 32 ? 5.6569f : D == 64 ? 8.0f : 9.7980f;  // >= sqrt(D)
 constexpr int PR_MAX_WORDS = PRUNE_MAX_WORDS;  // live words per query block
 constexpr int PR_LPW = 2;                 // bound pass: operand pieces per wavefront per batch
 constexpr int PR_NBUF = 3;                // bound pass: ring slots
 constexpr int PS_NPF = 4;                 // pruned selection: key blocks in flight per wavefront
+// (split-precision rows of 96: two, so that two workgroups share a CU's LDS)
+template <int D> constexpr int ps_npf = D > 64 ? 2 : PS_NPF;
+// Split-precision rows (D = 96: q3 = [q_hi | q_hi | q_lo], k3 = [k_hi | k_lo |
+// k_hi] of d = 32 elements each) are bounded through their high parts:
+//   q3 . k3 = q_hi . k_hi + q_hi . k_lo + q_lo . k_hi
+//          <= q_hi . mid + |q_hi| (R + L) + |q_lo| G
+// with mid, R the centre and radius of the block's k_hi, L and G the largest
+// |k_lo| and |k_hi|.  Bound dimensions and bound-row slices per row width:
+template <int D> constexpr int PR_DB = D == 96 ? 32 : D;
+template <int D> constexpr int PR_NB = PR_DB<D> / 16 + 1;
 constexpr int PR_HEAVY = 512;             // live key blocks above which a query block is heavy
 constexpr int PH_PARTS = PRUNE_HEAVY_PARTS;  // wavefronts sharing a heavy query block
 
@@ -145,12 +155,13 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
   const int H = a.H;
   const int64_t g = b / 32;
   const int br = (int)(b % 32);
-  uint16_t* bo = a.bop + (((int64_t)h * a.ngr + g) * (NM + 1)) * 512 + (br + 32 * lhalf) * 8;
+  constexpr int NMD = PR_DB<D> / 16;                  // slices of bounded dimensions
+  uint16_t* bo = a.bop + (((int64_t)h * a.ngr + g) * PR_NB<D>) * 512 + (br + 32 * lhalf) * 8;
   const int r = b < a.nkp ? a.bgroup[(int64_t)h * a.nkp + b] : -1;
   if (r < 0) {
     if (lrow == 0) {
 #pragma unroll
-      for (int m = 0; m < NM + 1; ++m) *reinterpret_cast<uint4*>(bo + m * 512) = uint4{0, 0, 0, 0};
+      for (int m = 0; m < PR_NB<D>; ++m) *reinterpret_cast<uint4*>(bo + m * 512) = uint4{0, 0, 0, 0};
     }
     return;
   }
@@ -169,25 +180,32 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
 #pragma unroll
   for (int m = 0; m < NM; ++m) *reinterpret_cast<uint4*>(ko + m * 512) = v[m];
 
-  float hi[8 * NM], lo[8 * NM], xs[8 * NM];
-  float amax = 0.f;
+  // Bounded elements: the whole row, or for split rows the high part
+  // (slices 0 .. NMD - 1); M (amax) over those elements.
+  float hi[8 * NMD], lo[8 * NMD], xs[8 * NMD];
+  float amax = 0.f, lo2 = 0.f, hi2 = 0.f;
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const uint32_t w[4] = {v[m].x, v[m].y, v[m].z, v[m].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-      xs[8 * m + e] = x;
-      hi[8 * m + e] = valid ? x : -kInf;
-      lo[8 * m + e] = valid ? x : kInf;
-      amax = fmaxf(amax, valid ? fabsf(x) : 0.f);
+      if (m < NMD) {
+        xs[8 * m + e] = x;
+        hi[8 * m + e] = valid ? x : -kInf;
+        lo[8 * m + e] = valid ? x : kInf;
+        amax = fmaxf(amax, valid ? fabsf(x) : 0.f);
+        hi2 = fmaf(x, x, hi2);
+      } else if (m < 2 * NMD) {
+        lo2 = fmaf(x, x, lo2);                 // split rows: k_lo
+      }
     }
   }
   // over the 32 rows of this lane's half, then M over the whole block
 #pragma unroll
   for (int o = 1; o < 32; o <<= 1) {
 #pragma unroll
-    for (int c = 0; c < 8 * NM; ++c) {
+    for (int c = 0; c < 8 * NMD; ++c) {
       hi[c] = fmaxf(hi[c], __shfl_xor(hi[c], o));
       lo[c] = fminf(lo[c], __shfl_xor(lo[c], o));
     }
@@ -198,30 +216,43 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
   // centre will do; the radius is measured from the rounded one).  The
   // radius: the largest distance of a row to it, over the rows of the block.
   float d2 = 0.f;
-  uint32_t mb[8 * NM];
+  uint32_t mb[8 * NMD];
 #pragma unroll
-  for (int c = 0; c < 8 * NM; ++c) {
+  for (int c = 0; c < 8 * NMD; ++c) {
     const float mid = __uint_as_float(__float_as_uint(0.5f * hi[c] + 0.5f * lo[c]) & 0xffff0000u);
     mb[c] = __float_as_uint(mid) >> 16;
     const float t = valid ? xs[c] - mid : 0.f;
     d2 = fmaf(t, t, d2);
   }
   d2 += __shfl_xor(d2, 32);
+  lo2 += __shfl_xor(lo2, 32);                  // (empty slots hold zero rows)
+  hi2 += __shfl_xor(hi2, 32);
 #pragma unroll
-  for (int o = 1; o < 32; o <<= 1) d2 = fmaxf(d2, __shfl_xor(d2, o));
+  for (int o = 1; o < 32; o <<= 1) {
+    d2 = fmaxf(d2, __shfl_xor(d2, o));
+    lo2 = fmaxf(lo2, __shfl_xor(lo2, o));
+    hi2 = fmaxf(hi2, __shfl_xor(hi2, o));
+  }
   if (lrow == 0) {
     // R >= every row's distance (the fp32 sum and root are within 2^-19 of
-    // it, relative), plus the pad that covers the scores' rounding
-    const float R = sqrtf(d2) * (1.f + 0x1p-16f) + PR_PAD * PR_SQRT_D<D> * amax;
+    // it, relative), plus the pad that covers the scores' rounding; split
+    // rows add L = max |k_lo| to it and G = max |k_hi| (both rounded up).
+    const float up = 1.f + 0x1p-16f;
+    float R = sqrtf(d2) * up + PR_PAD * PR_SQRT_D<PR_DB<D>> * amax;
+    uint32_t gbits = 0u;
+    if constexpr (D == 96) {
+      R += sqrtf(lo2) * up;
+      gbits = bf16_bits_up(sqrtf(hi2) * up);
+    }
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
+    for (int m = 0; m < NMD; ++m) {
       uint32_t wm[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) wm[i] = mb[8 * m + 2 * i] | (mb[8 * m + 2 * i + 1] << 16);
       *reinterpret_cast<uint4*>(bo + m * 512) = uint4{wm[0], wm[1], wm[2], wm[3]};
     }
-    *reinterpret_cast<uint4*>(bo + NM * 512) =
-        uint4{lhalf == 0 ? bf16_bits_up(R) : 0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint4*>(bo + NMD * 512) =
+        uint4{lhalf == 0 ? (bf16_bits_up(R) | (gbits << 16)) : 0u, 0u, 0u, 0u};
   }
 }
 
@@ -240,7 +271,7 @@ __global__ __launch_bounds__(256) void key_pack_kernel(ScanArgs a) {
 // in heavy_list / heavy_cnt.
 template <int D>
 __global__ __launch_bounds__(PR_WAVES * 64) void bound_live_kernel(ScanArgs a, int nwg) {
-  constexpr int NM = D / 16, NMB = NM + 1;
+  constexpr int NMD = PR_DB<D> / 16, NMB = PR_NB<D>;
   constexpr int PIECES = PR_WAVES * PR_LPW;
   constexpr int GPB = PIECES / NMB / 2 * 2;            // groups per slot (even)
   constexpr int SLOT = PIECES * 1024;
@@ -301,24 +332,33 @@ __global__ __launch_bounds__(PR_WAVES * 64) void bound_live_kernel(ScanArgs a, i
     // A operand [q | |q| e0]: the row, then its Euclidean norm (rounded up
     // to bf16, the fp32 sum and root being within 2^-19 of it, relative) as
     // element 0 of one more slice, against [mid | R e0] of the key blocks.
+    // Split rows: [q_hi | |q_hi| e0 + |q_lo| e1] against [mid | R e0 + G e1].
     bf16x8_t qb[NMB];
-    float qq = 0.f;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const uint4 w = *reinterpret_cast<const uint4*>(qp + 16 * m);
-      qb[m] = *reinterpret_cast<const bf16x8_t*>(&w);
+    float qq = 0.f, ql = 0.f;
+    auto sq = [&](const uint4& w, float& acc) __attribute__((always_inline)) {
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x0 = bf16_lo(ww[i]), x1 = bf16_hi(ww[i]);
-        qq = fmaf(x0, x0, qq);
-        qq = fmaf(x1, x1, qq);
+        acc = fmaf(x0, x0, acc);
+        acc = fmaf(x1, x1, acc);
       }
+    };
+#pragma unroll
+    for (int m = 0; m < NMD; ++m) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qp + 16 * m);
+      qb[m] = *reinterpret_cast<const bf16x8_t*>(&w);
+      sq(w, qq);
+      if constexpr (D == 96) sq(*reinterpret_cast<const uint4*>(qp + 16 * (2 * NMD + m)), ql);
     }
     qq += __shfl_xor(qq, 32);
+    ql += __shfl_xor(ql, 32);
     {
-      const uint4 w = {lhalf == 0 ? bf16_bits_up(sqrtf(qq) * (1.f + 0x1p-16f)) : 0u, 0u, 0u, 0u};
-      qb[NM] = *reinterpret_cast<const bf16x8_t*>(&w);
+      const float up = 1.f + 0x1p-16f;
+      const uint32_t e01 = bf16_bits_up(sqrtf(qq) * up) |
+                           (D == 96 ? bf16_bits_up(sqrtf(ql) * up) << 16 : 0u);
+      const uint4 w = {lhalf == 0 ? e01 : 0u, 0u, 0u, 0u};
+      qb[NMD] = *reinterpret_cast<const bf16x8_t*>(&w);
     }
     const float thr = qvalid ? next_down(a.thr[qrow * H + h]) : kInf;
     // The MFMA below puts the queries on the rows: lane l then holds key
@@ -684,7 +724,7 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
   static_assert(KP <= 16, "register lists");
   constexpr int CBW = COL ? 1 : SCAN_CAP * 64;
   constexpr int SLOT = (D / 16) * 1024 + 256;
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[PS_WAVES * PS_NPF * SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[PS_WAVES * ps_npf<D> * SLOT];
   __shared__ __attribute__((aligned(16))) uint2 cbuf[PS_WAVES * CBW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -704,7 +744,7 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
   int64_t qrow;
   bool qvalid;
   uint2* wl = cbuf + wave * CBW;
-  prune_wave<D, KP, PS_NPF, COL>(a, wid, 0, 1, ring + wave * (PS_NPF * SLOT), wl, ls, lj, qrow,
+  prune_wave<D, KP, ps_npf<D>, COL>(a, wid, 0, 1, ring + wave * (ps_npf<D> * SLOT), wl, ls, lj, qrow,
                                  qvalid);
   if constexpr (COL) return;
 
@@ -766,7 +806,7 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
   static_assert(KP <= 16, "register lists");
   constexpr int CBW = SCAN_CAP * 64;
   constexpr int SLOT = (D / 16) * 1024 + 256;
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[PS_WAVES * PS_NPF * SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[PS_WAVES * ps_npf<D> * SLOT];
   __shared__ __attribute__((aligned(16))) uint2 cbuf[PS_WAVES * CBW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -786,7 +826,7 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
     int lj[KP];
     int64_t qrow;
     bool qvalid;
-    prune_wave<D, KP, PS_NPF>(a, wid, part, PH_PARTS, ring + wave * (PS_NPF * SLOT), wl, ls, lj,
+    prune_wave<D, KP, ps_npf<D>>(a, wid, part, PH_PARTS, ring + wave * (ps_npf<D> * SLOT), wl, ls, lj,
                               qrow, qvalid);
     (void)qrow;
     (void)qvalid;

@@ -422,7 +422,7 @@ PruneSizes prune_sizes(int64_t N, int H, int d) {
   z.bgroup = align256((size_t)H * z.nkp * 4);
   z.kid = align256((size_t)H * z.nkp * 32 * 4);
   z.kop = align256((size_t)H * z.nkp * (d / 16) * 1024);
-  z.bop = align256((size_t)H * z.ngr * (d / 16 + 1) * 1024);
+  z.bop = align256((size_t)H * z.ngr * ((d == 96 ? 32 : d) / 16 + 1) * 1024);
   z.live = align256((size_t)held * z.ngr * 4);
   z.cnt = align256((size_t)rows * 4);
   z.nrange = ceil_div(rows, z.live_rows);
@@ -440,8 +440,11 @@ bool prune_applies(int64_t N, int H, int d, int topk) {
   // 0.48 against 0.68 ms; the pruned pass pays a bound pass and a fixed
   // cost per wavefront).  Up to 2^19: block and word indices are 32-bit
   // shifts of the query block index, and a query block's live words fit the
-  // bound pass's LDS.
-  if (!((d == 32 || d == 64) && scan_list_len(topk) > 0 && N >= ((int64_t)1 << 16) &&
+  // bound pass's LDS.  Rows of 32 or 64 bf16, or the split-precision rows of
+  // 96 of the fp32 entry points at d = 32 (the bound holds for any inner
+  // product the scan computes; 192-wide rows would leave one workgroup per
+  // CU).
+  if (!((d == 32 || d == 64 || d == 96) && scan_list_len(topk) > 0 && N >= ((int64_t)1 << 16) &&
         N <= ((int64_t)1 << 19)))
     return false;
   return prune_sizes(N, H, d).ngr <= PRUNE_MAX_WORDS;

@@ -303,7 +303,7 @@ struct Scanner {
       const int64_t r = qrow[0] * H + t.h;
       keep[0] = qvalid[0] && (a.cand_cnt[2 * r] > a.cap || a.cand_cnt[2 * r + 1] > a.cap);
       wave_rows = __ballot(keep[0]) != 0ull;
-    } else if constexpr ((MODE == M_SELECT || MODE == M_COLLECT) && (D == 32 || D == 64)) {
+    } else if constexpr ((MODE == M_SELECT || MODE == M_COLLECT) && (D == 32 || D == 64 || D == 96)) {
       static_assert(QB == 1, "one query block per wavefront");
       if (a.range_stream != nullptr) {
         filtered = true;
@@ -927,7 +927,7 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     // usually only checks the counts).
     ScanArgs c = a;
     c.range_stream = nullptr;
-    if constexpr (D == 32 || D == 64) {
+    if constexpr (D == 32 || D == 64 || D == 96) {
       if (a.kop != nullptr) {
         e = launch_prune<D, 16, true>(a, s);
         if (e != hipSuccess) return e;
@@ -954,7 +954,7 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     ScanArgs b = a;
     b.cand_cnt = nullptr;
     b.range_stream = nullptr;                  // SELECT writes every row...
-    if constexpr (D == 32 || D == 64) {
+    if constexpr (D == 32 || D == 64 || D == 96) {
       if (a.kop != nullptr) {                  // ...but those of the pruned pass
         // short lists run the pruned pass with 8-entry lists (sentinels fill
         // the rest): 5-entry instantiations compile to far more registers

@@ -137,8 +137,8 @@ def test_backward_f32_rejects():
 
 def _pruned_bytes(N, H, d, parts=True):
     """Buffers of the pruned selection (one graph with a query order, bf16
-    rows of 32 or 64, 2^16 <= N <= 2^19); lists longer than 16 have no
-    heavy parts' lists."""
+    rows of 32 or 64, or split-precision rows of 96, 2^16 <= N <= 2^19);
+    lists longer than 16 have no heavy parts' lists."""
     if not (1 << 16) <= N <= (1 << 19):
         return 0
     a = lambda x: (x + 255) // 256 * 256
@@ -155,20 +155,20 @@ def _pruned_bytes(N, H, d, parts=True):
     nrange = -(-rows // (1 << shift))
     heavy = min(held, 8192)
     return (3 * a(H * npiv * 4) + a(H * 4) + a(H * nkp * 4) + a(H * nkp * 32 * 4)
-            + a(H * nkp * (d // 16) * 1024) + a(H * ngr * (d // 16 + 1) * 1024) + a(held * ngr * 4)
+            + a(H * nkp * (d // 16) * 1024) + a(H * ngr * ((32 if d == 96 else d) // 16 + 1) * 1024) + a(held * ngr * 4)
             + a(rows * 4) + 3 * a(nrange * 4) + a(heavy * 4)
             + (a(heavy * 8 * 32 * 16 * 8) if parts else 0))
 
 
 def test_f32_workspace_adds_split_rows():
     # The fp32 forward also holds q and k as bf16 rows of 3d elements; its
-    # rows are 3d wide, so it has no pruned selection.
-    for (N, H, d, k, B, pruned) in [(1000, 2, 32, 15, 0, False), (100000, 4, 32, 15, 0, True),
-                                    (5000, 4, 64, 45, 7, False)]:
+    # pruned selection (d = 32 only) works on those 96-wide rows.
+    for (N, H, d, k, B) in [(1000, 2, 32, 15, 0), (100000, 4, 32, 15, 0), (100000, 4, 64, 15, 0),
+                            (5000, 4, 64, 45, 7)]:
         extra = kmip.forward_f32_workspace_bytes(N, H, d, k, B) - kmip.forward_workspace_bytes(
             N, H, d, k, B)
-        if pruned:
-            extra += _pruned_bytes(N, H, d)
+        if B == 0:
+            extra += _pruned_bytes(N, H, d) - (_pruned_bytes(N, H, 3 * d) if d == 32 else 0)
         assert 12 * N * H * d <= extra <= 12 * N * H * d + 512
     assert kmip.forward_f32_workspace_bytes(10, 4, 48, 15, 0) == 0
 

@@ -74,25 +74,30 @@ def _draw_pruned(case):
     clusters = int(rng.choice([16, 64, 256, 1024]))
     sigma = float(rng.choice([0.05, 0.3, 1.0]))
     n = int(rng.integers(1 << 16, 200_000))
+    seed = int(rng.integers(1 << 30))
+    # fp32 inputs at d = 32 prune on their 96-wide split rows
+    dtype = "f32" if d == 32 and rng.random() < 0.3 else "bf16"
     return make_workload(f"random_pruned_{case}", n=n, heads=heads, d=d, topk=topk, law=law,
                          clusters=clusters if law == "clustered" else 0, sigma=sigma,
-                         backward=True, seed=int(rng.integers(1 << 30)))
+                         backward=True, seed=seed, dtype=dtype)
 
 
 @pytest.mark.parametrize("case", range(24))
 def test_random_case_pruned(case):
-    """The pruned path on random shapes: selection and output on 2048 seeded
-    nodes x all heads, and dq on those rows, against the oracle."""
+    """The pruned path on random shapes (bf16 rows, and fp32 inputs on their
+    split rows): selection and output on 2048 seeded nodes x all heads, and
+    dq on those rows, against the oracle."""
     from tests.gpu_util import np_, run_backward, run_forward
     w = _draw_pruned(case)
     print(f"[case] random pruned {case}: n={w.n} H={w.heads} d={w.d} k={w.topk} "
-          f"{w.meta['law']} C={w.meta['clusters']} sigma={w.meta['sigma']}", flush=True)
+          f"{w.meta['law']} C={w.meta['clusters']} sigma={w.meta['sigma']} {w.dtype}", flush=True)
     t, out, idx, score = run_forward(w)
     q, k, v = decode(w)
     idx_n = np_(idx)
     rows = np.unique(np.concatenate(
         [[0, w.n - 1], np.random.default_rng(case).choice(w.n, 2048, replace=False)]))
-    check_selection(idx_n, np_(score), q, k, w.offsets, w.topk, rows)
+    split = dict(band_rel=0.0, split=True) if w.dtype == "f32" else {}
+    check_selection(idx_n, np_(score), q, k, w.offsets, w.topk, rows, **split)
     ref = orc.attend_on_sets(q, k, v, idx_n[rows].astype(np.int64), rows=rows)
     assert_rows_close(np_(out)[rows], ref["out"], "out")
     dq, _, _ = run_backward(w, t, idx, score)

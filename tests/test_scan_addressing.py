@@ -220,7 +220,8 @@ def check_pruned(N, H, D, nwg=256, seed=0):
     bound_live_kernel and pruned_select_kernel (elements of kop / kid / bop /
     live and the group tables, LDS offsets) against the sizes the host gives
     those buffers."""
-    NM, NMB = D // 16, D // 16 + 1
+    NM, NMB = D // 16, (32 if D == 96 else D) // 16 + 1   # split rows: bounds on the high part
+    NPF = 2 if D > 64 else PS_NPF
     nkb, nkp, ngr, live_rows = pruned_sizes(N, H, D)
     npiv = order_pivots(N)
     kop_elems, bop_elems = H * nkp * NM * 512, H * ngr * NMB * 512
@@ -314,24 +315,26 @@ def check_pruned(N, H, D, nwg=256, seed=0):
         # the largest wid it scores and the block reads
         assert r0 + (grid - 1) * PS_WAVES + 3 >= r1 - 1
         PSLOT = NM * 1024 + 256
-        assert PS_WAVES * PS_NPF * PSLOT + PS_WAVES * 8 * 64 * 8 <= 160 * 1024
+        assert PS_WAVES * NPF * PSLOT + PS_WAVES * 8 * 64 * 8 <= 160 * 1024
+        if D == 96:                                   # two workgroups per CU
+            assert PS_WAVES * NPF * PSLOT + PS_WAVES * 8 * 64 * 8 <= 80 * 1024
         for bb in (0, nkb - 1, nkp - 1):
             for m in range(NM):
                 e = (H - 1) * nkp * NM * 512 + 63 * 8 + (bb * NM + m) * 512
                 assert e + 8 <= kop_elems
-                lds = (PS_WAVES - 1) * PS_NPF * PSLOT + (PS_NPF - 1) * PSLOT + m * 1024 + 63 * 16
-                assert lds + 16 <= PS_WAVES * PS_NPF * PSLOT
+                lds = (PS_WAVES - 1) * NPF * PSLOT + (NPF - 1) * PSLOT + m * 1024 + 63 * 16
+                assert lds + 16 <= PS_WAVES * NPF * PSLOT
             # ids: lane offset (32 bb + l % 32) * 4 from kid + h nkp 32
             for lane in (0, 31, 63):
                 off = (bb * 32 + (lane & 31)) * 4
                 assert (H - 1) * nkp * 32 + off // 4 < kid_elems and off < (1 << 32)
-            lds = (PS_NPF - 1) * PSLOT + NM * 1024 + 63 * 4
-            assert lds + 4 <= PS_NPF * PSLOT
+            lds = (NPF - 1) * PSLOT + NM * 1024 + 63 * 4
+            assert lds + 4 <= NPF * PSLOT
     assert covered == total
     return nkb, ngr, live_rows
 
 
-@pytest.mark.parametrize("N,H,D", [(100000, 4, 32), (31623, 4, 32), (8192, 4, 32), (16384, 2, 64),
+@pytest.mark.parametrize("N,H,D", [(100000, 4, 32), (100000, 4, 96), (31623, 4, 32), (8192, 4, 32), (16384, 2, 64),
                                    (500000, 4, 32), (524288, 4, 64), (9000, 4, 32)])
 def test_pruned_selection_indices_stay_in_bounds(N, H, D):
     nkb, ngr, live_rows = check_pruned(N, H, D)

@@ -44,7 +44,12 @@
 // key whose computed score passes a threshold lies in a block whose computed
 // bound passes it too.  (Against a per-element box bound q . mid + |q| . rad,
 // this ball bound leaves about a third fewer blocks live on the clustered
-// inputs, with d / 16 + 1 operand slices instead of d / 8.)
+// inputs, with d / 16 + 1 operand slices instead of d / 8.)  Split rows: the
+// low parts are within 2^-8 of the high parts elementwise, so the 96 exact
+// products of a score sum to at most (1 + 2^-7) |q_hi|_1 M and the score is
+// within 2^-17.4 sqrt(d) |q_hi| M of q3 . k3; the bound's d + 2 terms (R, L,
+// G and both norms rounded up) are within 2^-17 sqrt(d) |q_hi| M; the same
+// pad on R, times |q_hi|, covers both.
 #pragma once
 
 constexpr int PR_WAVES = 16;              // bound pass: wavefronts per workgroup

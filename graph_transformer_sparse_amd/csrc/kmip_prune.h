@@ -59,9 +59,11 @@ template <int D> constexpr float PR_SQRT_D = D == 32 ? 5.6569f : D == 64 ? 8.0f 
 constexpr int PR_MAX_WORDS = PRUNE_MAX_WORDS;  // live words per query block
 constexpr int PR_LPW = 2;                 // bound pass: operand pieces per wavefront per batch
 constexpr int PR_NBUF = 3;                // bound pass: ring slots
-constexpr int PS_NPF = 4;                 // pruned selection: key blocks in flight per wavefront
-// (split-precision rows of 96: two, so that two workgroups share a CU's LDS)
-template <int D> constexpr int ps_npf = D > 64 ? 2 : PS_NPF;
+// Pruned selection: key blocks in flight per wavefront.  Two, so that four
+// workgroups (16 wavefronts) share a CU's LDS at rows of 32: at the bench
+// workload 1.63 ms for kmip_score_topk against 1.75 ms with four blocks in
+// flight (three workgroups per CU) and 1.73 ms with three.
+constexpr int PS_NPF = 2;
 // Split-precision rows (D = 96: q3 = [q_hi | q_hi | q_lo], k3 = [k_hi | k_lo |
 // k_hi] of d = 32 elements each) are bounded through their high parts:
 //   q3 . k3 = q_hi . k_hi + q_hi . k_lo + q_lo . k_hi
@@ -729,7 +731,7 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
   static_assert(KP <= 16, "register lists");
   constexpr int CBW = COL ? 1 : SCAN_CAP * 64;
   constexpr int SLOT = (D / 16) * 1024 + 256;
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[PS_WAVES * ps_npf<D> * SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[PS_WAVES * PS_NPF * SLOT];
   __shared__ __attribute__((aligned(16))) uint2 cbuf[PS_WAVES * CBW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -749,7 +751,7 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
   int64_t qrow;
   bool qvalid;
   uint2* wl = cbuf + wave * CBW;
-  prune_wave<D, KP, ps_npf<D>, COL>(a, wid, 0, 1, ring + wave * (ps_npf<D> * SLOT), wl, ls, lj, qrow,
+  prune_wave<D, KP, PS_NPF, COL>(a, wid, 0, 1, ring + wave * (PS_NPF * SLOT), wl, ls, lj, qrow,
                                  qvalid);
   if constexpr (COL) return;
 
@@ -811,7 +813,7 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
   static_assert(KP <= 16, "register lists");
   constexpr int CBW = SCAN_CAP * 64;
   constexpr int SLOT = (D / 16) * 1024 + 256;
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[PS_WAVES * ps_npf<D> * SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[PS_WAVES * PS_NPF * SLOT];
   __shared__ __attribute__((aligned(16))) uint2 cbuf[PS_WAVES * CBW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -831,7 +833,7 @@ __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3
     int lj[KP];
     int64_t qrow;
     bool qvalid;
-    prune_wave<D, KP, ps_npf<D>>(a, wid, part, PH_PARTS, ring + wave * (ps_npf<D> * SLOT), wl, ls, lj,
+    prune_wave<D, KP, PS_NPF>(a, wid, part, PH_PARTS, ring + wave * (PS_NPF * SLOT), wl, ls, lj,
                               qrow, qvalid);
     (void)qrow;
     (void)qvalid;

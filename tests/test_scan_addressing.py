@@ -183,7 +183,7 @@ def test_partition_is_contiguous_per_workgroup():
 
 
 # ---------------------------------------------------------------- pruned selection
-PR_WAVES, PS_WAVES, PR_MAX_WORDS, PR_LPW, PR_NBUF, PS_NPF = 16, 4, 704, 2, 3, 4
+PR_WAVES, PS_WAVES, PR_MAX_WORDS, PR_LPW, PR_NBUF, PS_NPF = 16, 4, 704, 2, 3, 2
 
 
 def order_pivots(N):
@@ -221,7 +221,7 @@ def check_pruned(N, H, D, nwg=256, seed=0):
     live and the group tables, LDS offsets) against the sizes the host gives
     those buffers."""
     NM, NMB = D // 16, (32 if D == 96 else D) // 16 + 1   # split rows: bounds on the high part
-    NPF = 2 if D > 64 else PS_NPF
+    NPF = PS_NPF
     nkb, nkp, ngr, live_rows = pruned_sizes(N, H, D)
     npiv = order_pivots(N)
     kop_elems, bop_elems = H * nkp * NM * 512, H * ngr * NMB * 512
@@ -316,6 +316,8 @@ def check_pruned(N, H, D, nwg=256, seed=0):
         assert r0 + (grid - 1) * PS_WAVES + 3 >= r1 - 1
         PSLOT = NM * 1024 + 256
         assert PS_WAVES * NPF * PSLOT + PS_WAVES * 8 * 64 * 8 <= 160 * 1024
+        if D == 32:                                   # four workgroups per CU
+            assert PS_WAVES * NPF * PSLOT + PS_WAVES * 8 * 64 * 8 <= 40 * 1024
         if D == 96:                                   # two workgroups per CU
             assert PS_WAVES * NPF * PSLOT + PS_WAVES * 8 * 64 * 8 <= 80 * 1024
         for bb in (0, nkb - 1, nkp - 1):

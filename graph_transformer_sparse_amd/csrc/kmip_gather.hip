@@ -214,7 +214,7 @@ __device__ __forceinline__ void store_span(float* p, const float* x) {
 // l keeps the sums of step l >> 2, which are those of slot l.  Pass 2 gives
 // each lane d/16 columns of dq = sum_t ds_t k_t; the ds_t and the first
 // chunk's K rows reach it through LDS (later chunks' K rows are read again).
-template <int D, typename T>
+template <int D, typename T, int KMAX>
 __global__ __launch_bounds__(256) void bwd_query_kernel(
     const T* __restrict__ Q, const T* __restrict__ Kt, const T* __restrict__ V, int64_t NH,
     int H, int topk, const int32_t* __restrict__ idx, const float* __restrict__ dout,
@@ -225,8 +225,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   // groups of a wave start on different banks), ds and key of every slot.
   constexpr int KROW = 16 * D + 64 / (int)sizeof(T);
   __shared__ T klds[ROWS_PER_BLOCK * KROW];
-  __shared__ double dsl[ROWS_PER_BLOCK][MAXK];
-  __shared__ int32_t jl[ROWS_PER_BLOCK][MAXK];
+  __shared__ double dsl[ROWS_PER_BLOCK][KMAX];
+  __shared__ int32_t jl[ROWS_PER_BLOCK][KMAX];
   const int l16 = threadIdx.x & 15, grp = threadIdx.x >> 4;
   const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + grp;
   if (row >= NH) return;                // whole 16-lane groups; no block barriers below
@@ -256,11 +256,11 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   // cancellation that loses the small terms of sum_u p_u dp_u when the
   // softmax is nearly one-hot.  Unused slots read the query's own row and
   // count zero.
-  double wv[MAXK / 16], dpv[MAXK / 16];
+  double wv[KMAX / 16], dpv[KMAX / 16];
   double zl = 0.0, dl = 0.0;    // this lane's share of Z and sum w (dp - dp_0)
   double dp0 = 0.0, m = 0.0;    // entry 0's dp and score (the forward's best)
 #pragma unroll
-  for (int c = 0; c < MAXK / 16; ++c) {
+  for (int c = 0; c < KMAX / 16; ++c) {
     wv[c] = 0.0;
     dpv[c] = 0.0;
     if (c * 16 < topk) {
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
 
   // Pass 2: ds_t, then dq = sum ds_t k_t over this lane's columns.
 #pragma unroll
-  for (int c = 0; c < MAXK / 16; ++c) {
+  for (int c = 0; c < KMAX / 16; ++c) {
     if (c * 16 < topk) {
       const int t = c * 16 + l16;
       const double p = wv[c] * inv;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
 #pragma unroll
-  for (int c = 0; c < MAXK / 16; ++c) {
+  for (int c = 0; c < KMAX / 16; ++c) {
     if (c * 16 < topk) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -361,9 +361,15 @@ template <int D, typename T>
 void launch_bwd_query_t(const T* q, const T* k, const T* v, int64_t NH, int H, int topk,
                         const int32_t* idx, const float* dout, float* dq, float2* pairs,
                         hipStream_t s) {
+  // Per-row LDS sized by the list length: 20 KB per workgroup at k <= 16
+  // (seven share a CU) instead of 30 KB (five).
   const unsigned blocks = (unsigned)ceil_div(NH, ROWS_PER_BLOCK);
-  hipLaunchKernelGGL((bwd_query_kernel<D, T>), dim3(blocks), dim3(256), 0, s, q, k, v, NH, H,
-                     topk, idx, dout, dq, pairs);
+  if (topk <= 16)
+    hipLaunchKernelGGL((bwd_query_kernel<D, T, 16>), dim3(blocks), dim3(256), 0, s, q, k, v, NH,
+                       H, topk, idx, dout, dq, pairs);
+  else
+    hipLaunchKernelGGL((bwd_query_kernel<D, T, MAXK>), dim3(blocks), dim3(256), 0, s, q, k, v,
+                       NH, H, topk, idx, dout, dq, pairs);
 }
 
 }  // namespace

@@ -21,7 +21,7 @@ constexpr int SCAN_QPW = 32;
 constexpr int SCAN_QT_MIN = SCAN_WAVES_LONG * SCAN_QPW;   // smallest planned tile
 constexpr int SCAN_CAP = 8;                       // per-lane candidate buffer entries
 constexpr int SCAN_CHUNKS = 32;                   // threshold pass: key ranges per lane half
-constexpr int COLLECT_CAP = 128;                  // candidates per row and lane half
+constexpr int COLLECT_CAP = 256;                  // candidates per row and lane half
 
 // Key-side backward: consecutive sorted (key, pair) positions per slice.
 constexpr int SEG_SLICE = 128;

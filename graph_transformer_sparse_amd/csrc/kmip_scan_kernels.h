@@ -261,11 +261,15 @@ struct Scanner {
     // tight bound, and this sample only guards inputs without cluster
     // structure: 8 times sparser (N = 10^5: 3.10 -> 3.02 ms for the whole
     // selection; dropping it entirely gained no more).
-    // (Long lists keep every second chunk on the pruned path too: at N =
-    // 10^5, k = 45 every fourth or sixteenth left so many rows' candidate
-    // arrays overflowing that the rank passes cost more than was saved.)
+    // Long lists on the pruned path (whose ranges with cluster structure also
+    // get the window bound) sample every fourth chunk: at N = 10^5, k = 45
+    // the threshold pass 1.79 -> 1.05 ms, with candidate arrays of 256 per
+    // lane half, which then almost never overflow (every sixteenth chunk, or
+    // every fourth with 128 entries, left so many rows overflowing that the
+    // rank passes cost more than was saved).
     const int sparse = perm != nullptr ? 8 : 1;
-    const int sample = !(PRE && KP <= 16)       ? SAMPLE
+    const int sample = PRE && KP > 16 && a.kop != nullptr ? 2 * SAMPLE
+                       : !(PRE && KP <= 16)       ? SAMPLE
                        : nkeys >= (int64_t)1 << 16 ? 4 * SAMPLE * sparse
                        : nkeys >= (int64_t)1 << 14 ? SAMPLE * sparse
                                                    : 1;
@@ -781,7 +785,10 @@ __global__ __launch_bounds__(256) void collect_topk_kernel(ScanArgs a) {
     lj[i] = -1;
   }
   // Candidates are read eight at a time, so that eight loads are in flight
-  // before the first insertion waits for its entry.
+  // before the first insertion waits for its entry.  (A first pass finding
+  // the k-th score with value lists, so that only the kept candidates and
+  // their ties are inserted, was slower: 1.36 against 1.16 ms at N = 10^5,
+  // k = 45, the candidates being read twice.)
   constexpr int PF = 8;
   for (int hf = 0; hf < 2; ++hf) {
     const int n = hf ? c1 : c0;

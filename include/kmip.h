@@ -169,7 +169,7 @@ kmip_status_t kmip_backward(const void* q, const void* k, const void* v, int64_t
  *  - Limit: sizes whose kmip_forward_workspace_bytes(...) exceeds
  *    KMIP_NO_WORKSPACE_BYTES return KMIP_ERR_WORKSPACE before anything is
  *    enqueued (about 3 * 10^6 (node, head) rows for topk <= 16; lists longer
- *    than 16 need 2 KB per row, so about 16000 rows).
+ *    than 16 need 4 KB per row, so about 8000 rows).
  *  - Races: every call on one GPU uses the same scratch array, so calls whose
  *    work may overlap on that GPU (different streams, other threads) race;
  *    serialise them.  Calls on one stream are ordered and safe.

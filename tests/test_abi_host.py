@@ -101,9 +101,9 @@ def test_workspace_sizes_are_linear_in_n():
         without = f(N, H, d, 15, 0) - _pruned_bytes(N, H, d)
         assert 10 * N * H <= without <= 12 * N * H + (1 << 20)
     # lists longer than 16: the pruned buffers without the heavy parts, and
-    # the candidate arrays (2 x 128 entries of 8 bytes per row) with counts
+    # the candidate arrays (2 x 256 entries of 8 bytes per row) with counts
     assert rows * 10 <= (f(100000, 4, 32, 45, 0) - _pruned_bytes(100000, 4, 32, parts=False)
-                         - 2 * 128 * rows * 8 - rows * 8) <= rows * 10 + (4 << 20)
+                         - 2 * 256 * rows * 8 - rows * 8) <= rows * 10 + (4 << 20)
     assert f(100000, 4, 32, 15, 64) > rows * 4                # thresholds plus the tile plan
     b1, b2 = b(100000, 4, 32, 15), b(200000, 4, 32, 15)
     assert 1.9 < b2 / b1 < 2.1                              # O(N * H * k)
@@ -177,7 +177,7 @@ def test_no_workspace_forward_rejects_before_any_gpu_call():
     """Sizes beyond the static scratch and invalid arguments are refused on
     the host, before the scratch array's address is looked up."""
     L = kmip.lib()
-    # lists longer than 16 need 2 KB of candidate arrays per row: 4e5 rows
+    # lists longer than 16 need 4 KB of candidate arrays per row: 4e5 rows
     st = L.kmip_forward_no_workspace(FAKE, FAKE, FAKE, 100000, 4, 32, 45, None, 0, FAKE, FAKE,
                                      FAKE, None)
     assert st == 3                                     # KMIP_ERR_WORKSPACE

@@ -785,10 +785,12 @@ __global__ __launch_bounds__(256) void collect_topk_kernel(ScanArgs a) {
     lj[i] = -1;
   }
   // Candidates are read eight at a time, so that eight loads are in flight
-  // before the first insertion waits for its entry.  (A first pass finding
-  // the k-th score with value lists, so that only the kept candidates and
-  // their ties are inserted, was slower: 1.36 against 1.16 ms at N = 10^5,
-  // k = 45, the candidates being read twice.)
+  // before the first insertion waits for its entry.  (Slower, at N = 10^5,
+  // k = 45: a first pass finding the k-th score with value lists, so that
+  // only the kept candidates and their ties are inserted, 1.36 against
+  // 1.16 ms, the candidates being read twice; two lanes per row, one per
+  // lane half's array, merged through LDS, 1.35 ms, each half list
+  // inserting more of its candidates.)
   constexpr int PF = 8;
   for (int hf = 0; hf < 2; ++hf) {
     const int n = hf ? c1 : c0;

@@ -29,7 +29,7 @@ import pytest
 
 SCAN_QPW = 32
 SCAN_CAP = 8
-COLLECT_CAP = 128
+COLLECT_CAP = 256
 M_THRESH, M_SELECT, M_COLLECT = 0, 1, 2
 QB = 1
 

@@ -122,3 +122,28 @@ def test_f32_resolves_what_bf16_rounding_cannot():
     print(f"rows with the oracle's set: fp32 path {same32:.4f}, bf16-rounded {samebf:.4f}")
     assert same32 >= 0.995
     assert samebf < same32
+
+
+@pytest.mark.parametrize("topk", [15, 45])
+def test_f32_deterministic_repeat_pruned(topk):
+    """2^16 nodes in fp32: the pruned selection over split rows (ball bounds
+    through the high parts), whose heavy query blocks are listed through an
+    atomic counter; k = 45 collects candidates from the pruned key blocks.
+    Two calls give identical outputs and gradients, and the selection of a
+    sample of rows matches the oracle."""
+    from tests.gpu_util import np_, run_backward, run_forward, to_device
+    w = small_case(65536, 2, 32, topk, law="clustered", clusters=64, seed=58, dtype="f32")
+    print(f"[case f32] repeat {w.name} n={w.n} H={w.heads} k={w.topk}", flush=True)
+    t = to_device(w)
+    a = run_forward(w, t)
+    b = run_forward(w, t)
+    for x, y in zip(a[1:], b[1:]):
+        assert np.array_equal(np_(x), np_(y))
+    ga = run_backward(w, t, a[2], a[3])
+    gb = run_backward(w, t, a[2], a[3])
+    for x, y in zip(ga, gb):
+        assert np.array_equal(np_(x), np_(y))
+    q, k, v = decode(w)
+    rows = np.sort(np.random.default_rng(58).choice(w.n, 512, replace=False))
+    check_selection(np_(a[2]), np_(a[3]), q, k, w.offsets, w.topk, rows, band_rel=0.0,
+                    split=True)
